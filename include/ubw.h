@@ -1,0 +1,202 @@
+/*
+ * ubw.h — C ABI of libubw.so: matrix-vector products against decoupled row-column binary
+ * bases, evaluated by table lookup on AMD MI355X (gfx950).
+ *
+ * Method: "FluxBin: Flexible LUT-based Ultra-low-bit LLM Inference by Algorithm-Kernel
+ * Synergy" (gist.science/ko/paper/2608.15602), technical summary.
+ *   - "1. Algorithm innovation": each base is W_hat^(k) = (alpha_r^(k) alpha_c^(k)^T) (.) B^(k)
+ *     with B^(k) in {-1,+1}^{N x K}; the weight is the sum of the global bases plus a
+ *     salient-refinement branch on selected columns.
+ *   - "2. Kernel innovation": LUT-BSF folds alpha_c into the partial-sum tables when they are
+ *     built; VCM maps the sparse salient columns onto a dense virtual matrix by gathering
+ *     activations and scales; the kernel streams packed uint32 words, extracts pattern
+ *     indices with bit operations, fetches partial sums and applies alpha_r in the reduction.
+ * So y[b][r] = sum_k alpha_r^(k)[r] * sum_j B^(k)[r][j] * alpha_c^(k)[j] * x[b][j]
+ *            + the same over the salient columns with the refinement bases.
+ *
+ * Conventions shared by every call
+ *   - Sign bits: bit 1 means +1, bit 0 means -1.
+ *   - Canonical bit format (input of ubw_pack_bases): uint32 words [nb][N][ceil(K/32)], column
+ *     j of a row at word j/32, bit j%32 (least significant first). Bits at columns >= K are
+ *     ignored.
+ *   - Packed format (output of ubw_pack_bases, input of the GEMV calls): an opaque GPU tile
+ *     layout of ubw_packed_words() uint32 words. Tiles of 256 rows x 256 columns per base;
+ *     padding rows and columns are zero. Only this library reads it.
+ *   - Group width g: the number of columns one pattern index covers (tables of 2^g entries).
+ *     ubw_lut_gemv and ubw_vcm_gather_refine take g = 8. ubw_build_lut and
+ *     ubw_extract_patterns take g = 4 or 8.
+ *   - Scalars: alpha_r [nb][N] and alpha_c [nb][K] fp32, row-major; y [batch][N] fp32.
+ *   - Activations x [batch][K], fp16 (UBW_F16) or fp32 (UBW_F32), row-major.
+ *   - Pointers are device pointers unless a comment says otherwise. The caller allocates
+ *     and owns every buffer; the library allocates nothing and keeps no global state.
+ *   - stream is a hipStream_t (NULL = the default stream). Every call only enqueues work on
+ *     it and returns; results are ready when the stream is synchronized.
+ *   - Return value: UBW_OK (0) or a negative ubw_status. Arguments are validated on the host
+ *     before anything is enqueued, so a failing call leaves every buffer untouched. Faults
+ *     inside kernels surface at the next stream synchronization.
+ *   - Outputs must not alias inputs.
+ */
+#ifndef UBW_H
+#define UBW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    UBW_OK = 0,
+    UBW_EINVAL = -1,        /* null pointer, non-positive size, batch out of range */
+    UBW_EUNSUPPORTED = -2,  /* g or dtype or source format not supported */
+    UBW_EALIGN = -3,        /* packed / x / workspace pointer not 16-byte aligned */
+    UBW_ERANGE = -4,        /* a size or index out of its allowed range */
+    UBW_EHIP = -5,          /* the HIP runtime rejected a launch */
+    UBW_ESIZE = -6          /* a caller buffer is smaller than required */
+} ubw_status;
+
+enum { UBW_F32 = 0, UBW_F16 = 1 };                       /* activation dtypes */
+enum { UBW_SRC_CANON_BITS = 0, UBW_SRC_INT8_SIGNS = 1 };  /* ubw_pack_bases sources */
+
+/* Largest batch one GEMV call accepts. */
+#define UBW_MAX_BATCH 16
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* ubw_status_str(int status);
+
+/* Library ABI version (increments when a signature or the packed layout changes). */
+int ubw_version(void);
+
+/*
+ * Size in uint32 words of the packed layout of nb bases of an N x K matrix (padding
+ * included). Host-only, enqueues nothing. *out_words is a host pointer.
+ */
+int ubw_packed_words(int nb, int64_t N, int64_t K, int g, int64_t* out_words);
+
+/*
+ * Pack sign bases into the GPU tile layout (load time; not on the per-token path).
+ * Section "2. Kernel innovation", execution flow: the kernel streams compressed uint32
+ * weights. The layout puts each 256-row x 256-column tile of a base in one contiguous
+ * block whose 16-byte vectors are read by consecutive lanes, so the GEMV's weight stream
+ * is a sequence of fully coalesced 1 KiB wave reads.
+ *   src      UBW_SRC_CANON_BITS: uint32 [nb][N][ceil(K/32)] canonical words;
+ *            UBW_SRC_INT8_SIGNS: int8 [nb][N][K], value > 0 means +1, otherwise -1.
+ *   dst      uint32 [ubw_packed_words(nb, N, K, g)], fully overwritten.
+ * Errors: UBW_EINVAL (null, nb < 1, N < 1, K < 1), UBW_EUNSUPPORTED (src_fmt, g),
+ *         UBW_EALIGN (dst not 16-byte aligned), UBW_EHIP.
+ */
+int ubw_pack_bases(const void* src, int src_fmt, int nb, int64_t N, int64_t K, int g,
+                   uint32_t* dst, void* stream);
+
+/*
+ * Encode ternary weights w in {-1, 0, +1} as two binary bases at half scale:
+ * w = (B1 + B2) / 2, with B1 = B2 = sign(w) where w != 0 and (B1, B2) = (+1, -1) where
+ * w == 0; both bases get alpha_r = scale / 2 and alpha_c = 1. (FlashLM v6 page: 81% of the
+ * model's parameters are ternary; the two-base encoding lets the binary-basis GEMV run them.)
+ *   w        int8 [N][K] (values outside {-1,0,1} are read by sign)
+ *   scale    fp32 [N] per-row scale of the ternary layer
+ *   packed   uint32 [ubw_packed_words(2, N, K, g)] output
+ *   alpha_r  fp32 [2][N] output;  alpha_c  fp32 [2][K] output
+ * Errors: UBW_EINVAL, UBW_EUNSUPPORTED (g), UBW_EALIGN (packed), UBW_EHIP.
+ */
+int ubw_ternary_encode(const int8_t* w, const float* scale, int64_t N, int64_t K, int g,
+                       uint32_t* packed, float* alpha_r, float* alpha_c, void* stream);
+
+/*
+ * LUT-BSF tables written to memory (the GEMV builds the same tables in LDS with the same
+ * device code; this call exists so the tables can be checked).
+ * Section "2. Kernel innovation", LUT-BSF: v = alpha_c^(k) (.) x_b rounded to fp32; for the
+ * group of columns gi*g .. gi*g+g-1 (v = 0 past column K),
+ * lut[b][k][gi][p] = sum_{i<g} (2*bit_i(p) - 1) * v[gi*g + i],  p in [0, 2^g).
+ *   x        [batch][K] fp16 or fp32;  alpha_c fp32 [nb][K]
+ *   lut      fp32 [batch][nb][ceil(K/g)][2^g] output
+ * Errors: UBW_EINVAL (null, sizes, batch < 1), UBW_EUNSUPPORTED (g, dtype), UBW_EHIP.
+ */
+int ubw_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, int nb,
+                  int64_t K, int g, float* lut, void* stream);
+
+/*
+ * Workspace bytes ubw_lut_gemv / ubw_vcm_gather_refine need for this shape. The current
+ * kernels need none (0); the argument pair is kept so a caller's allocation code does not
+ * change when a kernel starts using one. *out is a host pointer.
+ */
+int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out);
+
+/*
+ * Main GEMV: y (= or +=) sum_k alpha_r^(k) (.) (B^(k) (alpha_c^(k) (.) x)), for every
+ * activation row. Tables are built per 256-column slice in LDS (LUT-BSF), pattern indices
+ * are read from the packed words with byte-permute operations, and alpha_r is applied to
+ * each row's partial sum; slices of one row are combined with fp32 atomics, so the
+ * summation order (not the result beyond rounding) varies between runs.
+ *   packed       from ubw_pack_bases(nb, N, K, g=8)
+ *   accumulate   0: y = result; 1: y += result
+ *   workspace    may be NULL when ws_bytes == 0
+ * Errors: UBW_EINVAL (null, nb < 1, N < 1, K < 1, batch not in [1, UBW_MAX_BATCH]),
+ *         UBW_EUNSUPPORTED (g != 8, dtype), UBW_EALIGN (packed), UBW_ESIZE (ws_bytes),
+ *         UBW_EHIP.
+ */
+int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb,
+                 int64_t N, int64_t K, int g, const void* x, int x_dtype, int batch,
+                 float* y, int accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Salient refinement by virtual columnar mapping, accumulated into y.
+ * Section "2. Kernel innovation", VCM: the s salient columns idx[0..s) are mapped onto a
+ * dense virtual N x s matrix; its activations x[b][idx[q]] and scales alpha_c_s[k][q] are
+ * gathered while the tables are built, and the same LUT-GEMV runs over it:
+ * y[b][r] += sum_{k<ns} alpha_r_s[k][r] * sum_{q<s} B_s^(k)[r][q] * alpha_c_s[k][q] * x[b][idx[q]].
+ *   idx          int32 [s], each in [0, K) (order free; ascending is the convention)
+ *   packed_s     from ubw_pack_bases(ns, N, s, g=8) of the refinement bases [ns][N][s]
+ *   alpha_r_s    fp32 [ns][N];  alpha_c_s fp32 [ns][s]
+ *   K            columns of x (the activation row length)
+ * Indices are not range-checked on the device (the page's VCM carries no metadata checks);
+ * ubw_check_indices validates them when the caller wants that.
+ * Errors: as ubw_lut_gemv; s < 1 is UBW_EINVAL.
+ */
+int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_s,
+                          const float* alpha_r_s, const float* alpha_c_s, int ns, int64_t N,
+                          int64_t K, int g, const void* x, int x_dtype, int batch, float* y,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Host-side check of a salient index list: every idx[q] in [0, K) and strictly ascending.
+ * idx is a HOST pointer. Returns UBW_OK or UBW_ERANGE (UBW_EINVAL for null / s < 1).
+ */
+int ubw_check_indices(const int32_t* idx_host, int64_t s, int64_t K);
+
+/*
+ * Test export: pattern indices as the GEMV's bit extraction sees them, written in canonical
+ * order out[k][r][gi] (uint16), gi < ceil(K/g); columns >= K read as 0.
+ * Errors: UBW_EINVAL, UBW_EUNSUPPORTED (g not 4 or 8), UBW_EALIGN (packed), UBW_EHIP.
+ */
+int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, int g,
+                         uint16_t* out, void* stream);
+
+/*
+ * Test and tuning export: ubw_lut_gemv (vcm = 0) or ubw_vcm_gather_refine (vcm = 1) with an
+ * explicit launch geometry. rows_per_group in {1, 2, 4} row tiles of 256 rows per
+ * workgroup; slices_per_group >= 1 column slices of 256 columns per workgroup. Results
+ * equal the default geometry's up to fp32 summation order. For vcm = 0, idx is ignored and
+ * Kv = K; for vcm = 1, Kv = s, and accumulate must be 1.
+ */
+int ubw_lut_gemv_geometry(const uint32_t* packed, const float* alpha_r, const float* alpha_c,
+                          int nb, int64_t N, int64_t Kv, const int32_t* idx, int64_t K,
+                          const void* x, int x_dtype, int batch, float* y, int accumulate,
+                          int vcm, int rows_per_group, int slices_per_group, void* stream);
+
+/*
+ * Measurement helper (no part of the product computation): reads `bytes` bytes of `buf` with
+ * the GEMV's access shape (16-byte loads, consecutive lanes on consecutive vectors, one
+ * workgroup per 8 KiB, every load issued before any is consumed) and writes one word per
+ * workgroup to out[ceil(bytes / 8192)] that depends on the data. Benchmarks time it at the
+ * size of a GEMV's weight stream to show the ceiling of a single read of that size.
+ * Errors: UBW_EINVAL (null, bytes < 16 or not a multiple of 16), UBW_EALIGN, UBW_EHIP.
+ */
+int ubw_bench_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UBW_H */

@@ -1,0 +1,126 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol include/ubw.h
+declares, and rejects bad arguments on the host before anything is enqueued (no GPU needed:
+none of these calls reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import ultra_bit_weight_uint32_amd as ubw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ubw.h")
+
+EINVAL, EUNSUP, EALIGN, ERANGE = -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced on these paths
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(ubw_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(ubw.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ubw.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert ubw.lib().ubw_version() >= 1
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert ubw.status_str(st).startswith("UBW_") or st == 0
+    assert "unknown" in ubw.status_str(-99)
+
+
+def test_packed_words_sizes():
+    # tiles of 256 rows x 256 columns per base: 2048 words each
+    assert ubw.packed_words(2, 4096, 4096) == 2 * 16 * 16 * 2048
+    assert ubw.packed_words(1, 1, 1) == 2048
+    assert ubw.packed_words(3, 257, 257) == 3 * 2 * 2 * 2048
+    assert ubw.packed_words(1, 256, 4096, g=4) == 16 * 2048
+    out = ctypes.c_int64()
+    L = ubw.lib()
+    assert L.ubw_packed_words(0, 10, 10, 8, ctypes.byref(out)) == EINVAL
+    assert L.ubw_packed_words(1, 0, 10, 8, ctypes.byref(out)) == EINVAL
+    assert L.ubw_packed_words(1, 10, 0, 8, ctypes.byref(out)) == EINVAL
+    assert L.ubw_packed_words(1, 10, 10, 6, ctypes.byref(out)) == EUNSUP
+    assert L.ubw_packed_words(1, 10, 10, 8, None) == EINVAL
+
+
+def test_workspace_bytes():
+    assert ubw.workspace_bytes(2, 4096, 4096, 8, 1) == 0
+    sz = ctypes.c_size_t()
+    assert ubw.lib().ubw_workspace_bytes(2, 4096, 4096, 8, 17, ctypes.byref(sz)) == EINVAL
+    assert ubw.lib().ubw_workspace_bytes(2, 4096, 4096, 4, 1, ctypes.byref(sz)) == EUNSUP
+
+
+def gemv_args(**kw):
+    a = dict(packed=FAKE, alpha_r=FAKE, alpha_c=FAKE, nb=2, N=64, K=64, g=8, x=FAKE, x_dtype=1, batch=1,
+             y=FAKE, accumulate=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return ubw.lib().ubw_lut_gemv(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(packed=None), EINVAL), (dict(alpha_r=None), EINVAL), (dict(alpha_c=None), EINVAL),
+    (dict(x=None), EINVAL), (dict(y=None), EINVAL), (dict(nb=0), EINVAL), (dict(N=0), EINVAL),
+    (dict(K=0), EINVAL), (dict(N=-5), EINVAL), (dict(batch=0), EINVAL), (dict(batch=17), EINVAL),
+    (dict(x_dtype=7), EUNSUP), (dict(g=4), EUNSUP), (dict(g=5), EUNSUP), (dict(packed=MISALIGNED), EALIGN),
+])
+def test_lut_gemv_rejects(kw, status):
+    assert gemv_args(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(idx=None), EINVAL), (dict(s=0), EINVAL), (dict(packed_s=None), EINVAL), (dict(ns=0), EINVAL),
+    (dict(K=0), EINVAL), (dict(g=4), EUNSUP), (dict(batch=0), EINVAL), (dict(packed_s=MISALIGNED), EALIGN),
+])
+def test_vcm_rejects(kw, status):
+    a = dict(idx=FAKE, s=10, packed_s=FAKE, alpha_r_s=FAKE, alpha_c_s=FAKE, ns=2, N=64, K=64, g=8, x=FAKE,
+             x_dtype=1, batch=1, y=FAKE, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    assert ubw.lib().ubw_vcm_gather_refine(*a.values()) == status
+
+
+def test_geometry_rejects():
+    L = ubw.lib()
+    base = [FAKE, FAKE, FAKE, 2, 64, 64, None, 64, FAKE, 1, 1, FAKE, 0, 0]
+    assert L.ubw_lut_gemv_geometry(*base, 3, 1, None) == ERANGE      # rows_per_group not in {1,2,4}
+    assert L.ubw_lut_gemv_geometry(*base, 1, 0, None) == ERANGE      # slices_per_group < 1
+    b4 = list(base)
+    b4[10] = 4                                                       # batch 4 allows only 1 row tile
+    assert L.ubw_lut_gemv_geometry(*b4, 2, 1, None) == ERANGE
+    vcm = list(base)
+    vcm[13] = 1                                                      # vcm without idx
+    assert L.ubw_lut_gemv_geometry(*vcm, 1, 1, None) == EINVAL
+
+
+def test_other_entry_points_reject():
+    L = ubw.lib()
+    assert L.ubw_pack_bases(None, 0, 1, 8, 8, 8, FAKE, None) == EINVAL
+    assert L.ubw_pack_bases(FAKE, 5, 1, 8, 8, 8, FAKE, None) == EUNSUP
+    assert L.ubw_pack_bases(FAKE, 0, 1, 8, 8, 3, FAKE, None) == EUNSUP
+    assert L.ubw_pack_bases(FAKE, 0, 1, 8, 8, 8, MISALIGNED, None) == EALIGN
+    assert L.ubw_ternary_encode(None, FAKE, 8, 8, 8, FAKE, FAKE, FAKE, None) == EINVAL
+    assert L.ubw_ternary_encode(FAKE, FAKE, 8, 8, 8, MISALIGNED, FAKE, FAKE, None) == EALIGN
+    assert L.ubw_build_lut(FAKE, 1, 0, FAKE, 1, 8, 8, FAKE, None) == EINVAL
+    assert L.ubw_build_lut(FAKE, 3, 1, FAKE, 1, 8, 8, FAKE, None) == EUNSUP
+    assert L.ubw_build_lut(FAKE, 1, 1, FAKE, 1, 8, 2, FAKE, None) == EUNSUP
+    assert L.ubw_extract_patterns(FAKE, 1, 8, 8, 7, FAKE, None) == EUNSUP
+    assert L.ubw_extract_patterns(MISALIGNED, 1, 8, 8, 8, FAKE, None) == EALIGN
+
+
+def test_check_indices_host():
+    ubw.check_indices(np.array([0, 3, 9], np.int32), 10)
+    for bad in ([3, 3], [4, 2], [-1, 2], [0, 10]):
+        with pytest.raises(ubw.UbwError) as e:
+            ubw.check_indices(np.array(bad, np.int32), 10)
+        assert e.value.status == ERANGE

@@ -1,0 +1,368 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle, element by element.
+
+Bars: bit-exact for pattern indices, packing and every integer-valued case (unit scales,
+integer activations: all partial sums are integers below 2**24, so any fp32 summation order is
+exact); for floating-point inputs the elementwise error
+    e = max |y - r| / max(|r|, 1e-3 * max_row |r|)
+must stay at or below 1e-3 (fp32 accumulation, fp16 activations).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import ultra_bit_weight_uint32_amd as ubw
+from workloads import (config1, config2, config3, config4, config5, draw_bits, make_gemv, make_integer_gemv,
+                       words_per_row)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+DEV = "cuda:0"
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    elif a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def max_rel_err(y, r):
+    y = np.asarray(y, np.float64)
+    r = np.asarray(r, np.float64)
+    floor = 1e-3 * np.max(np.abs(r), axis=-1, keepdims=True)
+    den = np.maximum(np.abs(r), floor)
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max(np.abs(y - r) / den))
+
+
+def pack(bits, k):
+    nb, n, _ = bits.shape
+    return ubw.pack_bases(dev(bits), nb, n, k)
+
+
+def gpu_gemv(g, packed=None, refine=True, y=None, accumulate=False):
+    """Main GEMV (+ refinement) of a workloads.Gemv on the GPU; returns float64 [batch, n]."""
+    packed = pack(g.bits, g.k) if packed is None else packed
+    x = dev(g.x)
+    y = ubw.lut_gemv(packed, dev(g.alpha_r), dev(g.alpha_c), x, g.n, g.k, y=y, accumulate=accumulate)
+    if refine and g.s:
+        ps = pack(g.bits_s, g.s)
+        ubw.vcm_gather_refine(dev(g.idx), ps, dev(g.alpha_r_s), dev(g.alpha_c_s), x, g.n, g.k, y)
+    return host(y).astype(np.float64)
+
+
+def oracle_gemv(g, refine=True):
+    kw = g.refine_kwargs() if refine else {}
+    return oracle.gemv(g.bits, g.alpha_r, g.alpha_c, g.x, **kw)
+
+
+# ------------------------------------------------------------------------------------------
+# packing and pattern extraction (bit-exact)
+
+SHAPES = [(1, 1), (7, 33), (256, 256), (300, 700), (513, 1000)]
+
+
+@pytest.mark.parametrize("g_width", [8, 4])
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_patterns_bit_exact(g_width, n, k):
+    rng = np.random.default_rng(n * 1000 + k)
+    bits = draw_bits(rng, 2, n, k)   # garbage past column K on purpose
+    p = ubw.extract_patterns(pack(bits, k), 2, n, k, g=g_width)
+    assert np.array_equal(host(p).view(np.uint16), oracle.patterns(bits, k, g=g_width))
+
+
+def test_patterns_every_value_in_every_position():
+    n, k = 512, 512
+    ng = k // 8
+    bits = np.zeros((1, n, words_per_row(k)), np.uint32)
+    for r in range(n):
+        big = 0
+        for gi in range(ng):
+            big |= ((7 * r + gi) % 256) << (8 * gi)
+        for w in range(bits.shape[2]):
+            bits[0, r, w] = (big >> (32 * w)) & 0xFFFFFFFF
+    p = host(ubw.extract_patterns(pack(bits, k), 1, n, k)).view(np.uint16)
+    want = (7 * np.arange(n)[:, None] + np.arange(ng)[None, :]) % 256
+    assert np.array_equal(p[0], want)
+
+
+@pytest.mark.parametrize("n,k", [(5, 40), (300, 700)])
+def test_pack_from_int8_signs_matches_canonical(n, k):
+    rng = np.random.default_rng(3)
+    bits = draw_bits(rng, 3, n, k)
+    by = bits.view(np.uint8).reshape(3, n, -1)
+    signs = (np.unpackbits(by, axis=2, bitorder="little")[:, :, :k].astype(np.int8) * 2 - 1)
+    a = host(pack(bits, k))
+    b = host(ubw.pack_bases(dev(signs), 3, n, k))
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------------------------------
+# LUT-BSF tables
+
+@pytest.mark.parametrize("g_width", [8, 4])
+def test_build_lut_integer_exact(g_width):
+    rng = np.random.default_rng(4)
+    k = 300
+    x = rng.integers(-8, 9, (3, k)).astype(np.float16)
+    ac = np.ones((2, k), np.float32)
+    T = host(ubw.build_lut(dev(x), dev(ac), g=g_width))
+    assert np.array_equal(T.astype(np.float64), oracle.lut_tables(x, ac, g=g_width))
+
+
+@pytest.mark.parametrize("g_width", [8, 4])
+@pytest.mark.parametrize("xdt", [np.float16, np.float32])
+def test_build_lut_float(g_width, xdt):
+    rng = np.random.default_rng(5)
+    k = 777
+    x = rng.standard_normal((2, k)).astype(xdt)
+    ac = rng.uniform(0.05, 0.5, (3, k)).astype(np.float32)
+    T = host(ubw.build_lut(dev(x), dev(ac), g=g_width)).astype(np.float64)
+    R = oracle.lut_tables(x, ac, g=g_width)
+    ng = R.shape[2]
+    v = np.abs(ac[None].astype(np.float64) * x[:, None].astype(np.float64))
+    v = np.concatenate([v, np.zeros((2, 3, ng * g_width - k))], axis=2).reshape(2, 3, ng, g_width)
+    bound = 16 * 2.0 ** -24 * v.sum(-1, keepdims=True)   # fp32 rounding of v and of the sums
+    assert np.all(np.abs(T - R) <= bound)
+
+
+# ------------------------------------------------------------------------------------------
+# main GEMV
+
+INT_SHAPES = [(1, 1, 1), (5, 33, 2), (256, 256, 1), (300, 700, 3), (1000, 2050, 2), (4096, 4096, 2)]
+
+
+@pytest.mark.parametrize("n,k,nb", INT_SHAPES)
+@pytest.mark.parametrize("batch", [1, 3, 16])
+def test_gemv_integer_exact(n, k, nb, batch):
+    rng = np.random.default_rng(n + 7 * k + nb + 100 * batch)
+    g = make_integer_gemv(rng, n, k, nb, batch=batch)
+    assert np.array_equal(gpu_gemv(g), oracle_gemv(g))
+
+
+@pytest.mark.parametrize("rpg", [1, 2, 4])
+@pytest.mark.parametrize("spg", [1, 2, 3, 7])
+def test_gemv_geometries_integer_exact(rpg, spg):
+    """Every workgroup shape gives the same exact result (5 row tiles x 7 column slices, both
+    ragged at the edge)."""
+    rng = np.random.default_rng(rpg * 10 + spg)
+    n, k = 4 * 256 + 100, 6 * 256 + 77
+    g = make_integer_gemv(rng, n, k, 2, batch=1)
+    y = torch.full((1, n), 123.0, device=DEV)
+    ubw.lut_gemv_geometry(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y,
+                          rows_per_group=rpg, slices_per_group=spg)
+    assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g))
+
+
+@pytest.mark.parametrize("batch", [2, 4, 8, 16])
+def test_gemv_geometries_batched(batch):
+    rng = np.random.default_rng(batch)
+    n, k = 3 * 256 + 5, 3 * 256 + 1
+    g = make_integer_gemv(rng, n, k, 3, batch=batch)
+    for rpg in (1, 2):
+        if rpg > 1 and batch > 2:
+            continue
+        y = torch.zeros((batch, n), device=DEV)
+        ubw.lut_gemv_geometry(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y,
+                              rows_per_group=rpg, slices_per_group=2)
+        assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g))
+
+
+def test_gemv_accumulate():
+    rng = np.random.default_rng(11)
+    g = make_integer_gemv(rng, 700, 1500, 2, batch=2)
+    y0 = rng.integers(-100, 100, (2, 700)).astype(np.float32)
+    y = dev(y0)
+    out = gpu_gemv(g, y=y, accumulate=True)
+    assert np.array_equal(out, oracle_gemv(g) + y0)
+
+
+def test_one_hot_reads_signs():
+    """alpha = 1, x = e_j: y is column j of B as +-1 (sign convention end to end)."""
+    rng = np.random.default_rng(12)
+    n, k = 256, 512
+    bits = draw_bits(rng, 1, n, k)
+    packed = pack(bits, k)
+    by = bits.view(np.uint8).reshape(1, n, -1)
+    signs = np.unpackbits(by, axis=2, bitorder="little")[0, :, :k].astype(np.float64) * 2 - 1
+    xs = np.eye(k, dtype=np.float16)
+    ar, ac = dev(np.ones((1, n), np.float32)), dev(np.ones((1, k), np.float32))
+    for j0 in range(0, k, 16):   # 16 one-hot vectors per call as a batch
+        y = ubw.lut_gemv(packed, ar, ac, dev(xs[j0:j0 + 16]), n, k)
+        assert np.array_equal(host(y).astype(np.float64), signs[:, j0:j0 + 16].T)
+
+
+@pytest.mark.parametrize("n,k,nb,xdt", [(256, 512, 1, np.float32), (300, 700, 2, np.float16),
+                                        (1024, 4096, 3, np.float16), (777, 333, 2, np.float32)])
+@pytest.mark.parametrize("batch", [1, 5])
+def test_gemv_float_tolerance(n, k, nb, xdt, batch):
+    rng = np.random.default_rng(n + k + batch)
+    g = make_gemv(rng, "f", n, k, nb, batch=batch, x_dtype=xdt)
+    assert max_rel_err(gpu_gemv(g), oracle_gemv(g)) <= TOL
+
+
+# ------------------------------------------------------------------------------------------
+# salient refinement (VCM)
+
+@pytest.mark.parametrize("k,s", [(64, 1), (700, 37), (4096, 205), (1000, 300), (2000, 1434)])
+@pytest.mark.parametrize("batch", [1, 4])
+def test_vcm_integer_exact(k, s, batch):
+    rng = np.random.default_rng(k + s + batch)
+    g = make_integer_gemv(rng, 300, k, 2, s=s, ns=2, batch=batch)
+    assert np.array_equal(gpu_gemv(g), oracle_gemv(g))
+
+
+def test_vcm_geometries_integer_exact():
+    rng = np.random.default_rng(21)
+    n, k, s = 600, 3000, 700
+    g = make_integer_gemv(rng, n, k, 1, s=s, ns=2, batch=2)
+    ps = pack(g.bits_s, s)
+    want = oracle_gemv(g) - oracle_gemv(g, refine=False)
+    for rpg, spg in ((1, 1), (2, 2), (1, 3)):
+        y = torch.zeros((2, n), device=DEV)
+        ubw.lut_gemv_geometry(ps, dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), n, s, y, idx=dev(g.idx), k=k,
+                              accumulate=True, rows_per_group=rpg, slices_per_group=spg)
+        assert np.array_equal(host(y).astype(np.float64), want)
+
+
+def test_vcm_every_column_salient_doubles():
+    rng = np.random.default_rng(22)
+    n, k = 300, 500
+    g = make_integer_gemv(rng, n, k, 2, batch=2)
+    x = dev(g.x)
+    packed = pack(g.bits, k)
+    y = ubw.lut_gemv(packed, dev(g.alpha_r), dev(g.alpha_c), x, n, k)
+    y1 = host(y).copy()
+    ubw.vcm_gather_refine(dev(np.arange(k, dtype=np.int32)), packed, dev(g.alpha_r), dev(g.alpha_c), x, n, k, y)
+    assert np.array_equal(host(y), 2 * y1)
+
+
+def test_vcm_permutation_invariant():
+    rng = np.random.default_rng(23)
+    n, k, s = 260, 900, 90
+    g = make_integer_gemv(rng, n, k, 1, s=s, ns=2, batch=1)
+    base = gpu_gemv(g)
+    perm = rng.permutation(s)
+    by = g.bits_s.view(np.uint8).reshape(2, n, -1)
+    b01 = np.unpackbits(by, axis=2, bitorder="little")[:, :, :s][:, :, perm]
+    b01 = np.concatenate([b01, np.zeros((2, n, (-s) % 32), np.uint8)], axis=2)
+    g.bits_s = np.packbits(b01, axis=2, bitorder="little").view(np.uint32).reshape(2, n, -1)
+    g.idx = g.idx[perm].copy()
+    g.alpha_c_s = g.alpha_c_s[:, perm].copy()
+    assert np.array_equal(gpu_gemv(g), base)
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_vcm_float_tolerance(batch):
+    rng = np.random.default_rng(24 + batch)
+    g = make_gemv(rng, "v", 1000, 3000, 2, s=150, ns=2, batch=batch)
+    assert max_rel_err(gpu_gemv(g), oracle_gemv(g)) <= TOL
+
+
+# ------------------------------------------------------------------------------------------
+# ternary weights as two half-scale bases
+
+def test_ternary_encode_patterns_match_oracle_encoding():
+    rng = np.random.default_rng(30)
+    n, k = 300, 520
+    w = rng.integers(-1, 2, (n, k)).astype(np.int8)
+    packed, ar, ac = ubw.ternary_encode(dev(w), dev(np.ones(n, np.float32)))
+    want = oracle.patterns(oracle.ternary_encode(w, zero_first_plus=True), k)
+    assert np.array_equal(host(ubw.extract_patterns(packed, 2, n, k)).view(np.uint16), want)
+    assert np.array_equal(host(ar), np.full((2, n), 0.5, np.float32))
+    assert np.array_equal(host(ac), np.ones((2, k), np.float32))
+
+
+def test_ternary_gemv_integer_exact():
+    rng = np.random.default_rng(31)
+    n, k = 768, 256
+    w = rng.integers(-1, 2, (n, k)).astype(np.int8)
+    x = rng.integers(-8, 9, (4, k)).astype(np.float16)
+    packed, ar, ac = ubw.ternary_encode(dev(w), dev(np.full(n, 2.0, np.float32)))
+    y = ubw.lut_gemv(packed, ar, ac, dev(x), n, k)
+    assert np.array_equal(host(y).astype(np.float64), oracle.ternary_gemv(w, np.full(n, 2.0, np.float32), x))
+
+
+def test_config2_ternary_stack():
+    """4 x (256 -> 768 -> 256) ternary layers over 64 tokens, fp16 activations between layers.
+    Every layer is checked on the GPU's own fp16 input (teacher forcing) at the elementwise 1e-3
+    bar. The end-to-end output is compared with the oracle's own chain norm-wise: the two chains
+    re-round slightly different fp32 results to fp16 after each of the 8 layers, so outputs
+    near zero can differ by more than 1e-3 of themselves while the row stays within ~1e-4 of
+    its largest entry."""
+    wl = config2()
+    enc = [ubw.ternary_encode(dev(L.w), dev(L.scale)) for L in wl.ternary]
+    xt = dev(wl.tokens)
+    worst = 0.0
+    for t in range(wl.tokens.shape[0]):
+        a = xt[t:t + 1]
+        for L, (packed, ar, ac) in zip(wl.ternary, enc):
+            n, k = L.w.shape
+            y = ubw.lut_gemv(packed, ar, ac, a, n, k)
+            r = oracle.ternary_gemv(L.w, L.scale, host(a))
+            worst = max(worst, max_rel_err(host(y), r))
+            a = y.to(torch.float16)
+    assert worst <= TOL
+    # end to end, 16 tokens per call (the batch limit of one call)
+    for t0 in range(0, wl.tokens.shape[0], ubw.MAX_BATCH):
+        a_gpu = xt[t0:t0 + ubw.MAX_BATCH]
+        a_ref = wl.tokens[t0:t0 + ubw.MAX_BATCH].astype(np.float64)
+        for L, (packed, ar, ac) in zip(wl.ternary, enc):
+            n, k = L.w.shape
+            a_gpu = ubw.lut_gemv(packed, ar, ac, a_gpu, n, k).to(torch.float16)
+            a_ref = oracle.ternary_gemv(L.w, L.scale, a_ref).astype(np.float16).astype(np.float64)
+        d = np.abs(host(a_gpu).astype(np.float64) - a_ref).max(axis=1) / np.abs(a_ref).max(axis=1)
+        assert d.max() <= 1e-2
+
+
+# ------------------------------------------------------------------------------------------
+# the workloads at full size, in the launch configuration the benchmark uses
+
+def test_config1_full():
+    g = config1().gemvs[0]
+    assert max_rel_err(gpu_gemv(g), oracle_gemv(g)) <= TOL
+
+
+def test_config3_full():
+    g = config3().gemvs[0]
+    assert max_rel_err(gpu_gemv(g), oracle_gemv(g)) <= TOL
+    assert max_rel_err(gpu_gemv(g, refine=False), oracle_gemv(g, refine=False)) <= TOL
+
+
+def test_config4_full():
+    wl = config4()
+    for g in wl.gemvs:
+        for b in wl.batches:
+            gb = g.with_batch(b)
+            assert max_rel_err(gpu_gemv(gb), oracle_gemv(gb)) <= TOL, (g.name, b)
+
+
+def sampled_rows(g, rows):
+    """The same problem restricted to a subset of rows (the oracle then computes exactly
+    those outputs)."""
+    from workloads import Gemv
+    s = Gemv(g.name, len(rows), g.k, g.bits[:, rows], g.alpha_r[:, rows], g.alpha_c, g.x)
+    if g.s:
+        s.idx, s.bits_s, s.alpha_r_s, s.alpha_c_s = g.idx, g.bits_s[:, rows], g.alpha_r_s[:, rows], g.alpha_c_s
+    return s
+
+
+def test_config5_full_sampled():
+    wl = config5()
+    rng = np.random.default_rng(55)
+    for g in wl.gemvs:
+        rows = np.sort(rng.choice(g.n, size=min(g.n, 384), replace=False))
+        for b in wl.batches:
+            gb = g.with_batch(b)
+            y = gpu_gemv(gb)[:, rows]
+            r = oracle_gemv(sampled_rows(gb, rows))
+            assert max_rel_err(y, r) <= TOL, (g.name, b)

@@ -1,0 +1,285 @@
+"""Table-lookup GEMV over decoupled row-column binary bases for AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libubw.so`` (C ABI declared in ``include/ubw.h``). Every step of the
+computation runs in the library's HIP kernels; this module only checks tensor devices, dtypes
+and shapes, allocates outputs with PyTorch, and passes device pointers and the current HIP
+stream. There is no CPU fallback: if the library is missing or the tensors are not on a GPU,
+calls raise.
+
+Method: FluxBin (gist.science/ko/paper/2608.15602), technical summary — "1. Algorithm
+innovation" (W_hat^(k) = (alpha_r^(k) alpha_c^(k)^T) (.) B^(k), global + salient-refinement
+bases) and "2. Kernel innovation" (LUT-BSF tables, virtual columnar mapping, uint32 weight
+stream with bit-extracted pattern indices and alpha_r applied in the reduction).
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBPATH = os.path.join(_HERE, "libubw.so")
+
+UBW_OK = 0
+UBW_F32, UBW_F16 = 0, 1
+UBW_SRC_CANON_BITS, UBW_SRC_INT8_SIGNS = 0, 1
+MAX_BATCH = 16
+
+# every symbol include/ubw.h declares
+EXPORTS = (
+    "ubw_status_str", "ubw_version", "ubw_packed_words", "ubw_pack_bases", "ubw_ternary_encode",
+    "ubw_build_lut", "ubw_workspace_bytes", "ubw_lut_gemv", "ubw_vcm_gather_refine",
+    "ubw_check_indices", "ubw_extract_patterns", "ubw_lut_gemv_geometry", "ubw_bench_stream_read",
+)
+
+
+class UbwError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libubw.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBPATH):
+        raise ImportError(f"{LIBPATH} is missing: build it with `python -m ultra_bit_weight_uint32_amd.build`")
+    L = ctypes.CDLL(LIBPATH)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "ubw_status_str": ([I], ctypes.c_char_p),
+        "ubw_version": ([], I),
+        "ubw_packed_words": ([I, I64, I64, I, ctypes.POINTER(I64)], I),
+        "ubw_pack_bases": ([P, I, I, I64, I64, I, P, P], I),
+        "ubw_ternary_encode": ([P, P, I64, I64, I, P, P, P, P], I),
+        "ubw_build_lut": ([P, I, I, P, I, I64, I, P, P], I),
+        "ubw_workspace_bytes": ([I, I64, I64, I, I, ctypes.POINTER(SZ)], I),
+        "ubw_lut_gemv": ([P, P, P, I, I64, I64, I, P, I, I, P, I, P, SZ, P], I),
+        "ubw_vcm_gather_refine": ([P, I64, P, P, P, I, I64, I64, I, P, I, I, P, P, SZ, P], I),
+        "ubw_check_indices": ([P, I64, I64], I),
+        "ubw_extract_patterns": ([P, I, I64, I64, I, P, P], I),
+        "ubw_lut_gemv_geometry": ([P, P, P, I, I64, I64, P, I64, P, I, I, P, I, I, I, I, P], I),
+        "ubw_bench_stream_read": ([P, I64, P, P], I),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().ubw_status_str(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != UBW_OK:
+        raise UbwError(fn, status)
+
+
+# ---------------------------------------------------------------------------------------------
+# torch marshalling helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtypes):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (no CPU path exists)")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _xdtype(x):
+    torch = _torch()
+    if x.dtype == torch.float16:
+        return UBW_F16
+    if x.dtype == torch.float32:
+        return UBW_F32
+    raise TypeError(f"x must be float16 or float32, got {x.dtype}")
+
+
+def _as_2d(x):
+    return x if x.dim() == 2 else x.reshape(1, -1)
+
+
+def _words_dtypes():
+    torch = _torch()
+    return (torch.int32, torch.uint32)
+
+
+# ---------------------------------------------------------------------------------------------
+# the calls (same names as the C ABI without the ubw_ prefix)
+
+def packed_words(nb: int, n: int, k: int, g: int = 8) -> int:
+    out = ctypes.c_int64(0)
+    _check("ubw_packed_words", lib().ubw_packed_words(nb, n, k, g, ctypes.byref(out)))
+    return out.value
+
+
+def workspace_bytes(nb: int, n: int, k: int, g: int = 8, batch: int = 1) -> int:
+    out = ctypes.c_size_t(0)
+    _check("ubw_workspace_bytes", lib().ubw_workspace_bytes(nb, n, k, g, batch, ctypes.byref(out)))
+    return out.value
+
+
+def pack_bases(src, nb: int, n: int, k: int, g: int = 8, out=None):
+    """Pack canonical uint32 words [nb, n, ceil(k/32)] (int32/uint32 tensor) or int8 signs
+    [nb, n, k] into the GPU tile layout; returns an int32 tensor of packed_words() words."""
+    torch = _torch()
+    if src.dtype == torch.int8:
+        fmt = UBW_SRC_INT8_SIGNS
+        if tuple(src.shape) != (nb, n, k):
+            raise ValueError(f"int8 signs must have shape {(nb, n, k)}, got {tuple(src.shape)}")
+    else:
+        fmt = UBW_SRC_CANON_BITS
+        if tuple(src.shape) != (nb, n, (k + 31) // 32):
+            raise ValueError(f"canonical words must have shape {(nb, n, (k + 31) // 32)}, got {tuple(src.shape)}")
+    sp = _dev(src, "src", (torch.int8,) + _words_dtypes())
+    words = packed_words(nb, n, k, g)
+    if out is None:
+        out = torch.empty(words, dtype=torch.int32, device=src.device)
+    elif out.numel() < words:
+        raise ValueError("out is too small")
+    _check("ubw_pack_bases", lib().ubw_pack_bases(sp, fmt, nb, n, k, g, _dev(out, "out", _words_dtypes()), _stream()))
+    return out
+
+
+def ternary_encode(w, scale, g: int = 8):
+    """Ternary int8 weights [n, k] and per-row scale [n] -> (packed, alpha_r [2, n], alpha_c [2, k])."""
+    torch = _torch()
+    n, k = w.shape
+    wp = _dev(w, "w", (torch.int8,))
+    sp = _dev(scale, "scale", (torch.float32,))
+    packed = torch.empty(packed_words(2, n, k, g), dtype=torch.int32, device=w.device)
+    ar = torch.empty((2, n), dtype=torch.float32, device=w.device)
+    ac = torch.empty((2, k), dtype=torch.float32, device=w.device)
+    _check("ubw_ternary_encode", lib().ubw_ternary_encode(wp, sp, n, k, g, _dev(packed, "packed", None),
+                                                          _dev(ar, "alpha_r", None), _dev(ac, "alpha_c", None),
+                                                          _stream()))
+    return packed, ar, ac
+
+
+def build_lut(x, alpha_c, g: int = 8):
+    """LUT-BSF tables [batch, nb, ceil(K/g), 2**g] fp32 with alpha_c folded in."""
+    torch = _torch()
+    x = _as_2d(x)
+    batch, k = x.shape
+    nb = alpha_c.shape[0]
+    if alpha_c.shape[1] != k:
+        raise ValueError("alpha_c must be [nb, K]")
+    ng = (k + g - 1) // g
+    lut = torch.empty((batch, nb, ng, 1 << g), dtype=torch.float32, device=x.device)
+    _check("ubw_build_lut", lib().ubw_build_lut(_dev(x, "x", None), _xdtype(x), batch,
+                                                _dev(alpha_c, "alpha_c", (torch.float32,)), nb, k, g,
+                                                _dev(lut, "lut", None), _stream()))
+    return lut
+
+
+def lut_gemv(packed, alpha_r, alpha_c, x, n: int, k: int, g: int = 8, y=None, accumulate: bool = False,
+             workspace=None):
+    """y (= or +=) sum_k alpha_r^(k) (.) (B^(k) (alpha_c^(k) (.) x)); x [batch, K] fp16/fp32,
+    y [batch, N] fp32. Returns y."""
+    torch = _torch()
+    x = _as_2d(x)
+    batch = x.shape[0]
+    nb = alpha_r.shape[0]
+    if x.shape[1] != k or tuple(alpha_r.shape) != (nb, n) or tuple(alpha_c.shape) != (nb, k):
+        raise ValueError("shape mismatch between x, alpha_r, alpha_c and (n, k)")
+    if packed.numel() < packed_words(nb, n, k, g):
+        raise ValueError("packed buffer smaller than packed_words()")
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs y")
+        y = torch.empty((batch, n), dtype=torch.float32, device=x.device)
+    if tuple(y.shape) != (batch, n):
+        raise ValueError(f"y must be [{batch}, {n}]")
+    ws, wsb = (None, 0) if workspace is None else (_dev(workspace, "workspace", None), workspace.numel() * workspace.element_size())
+    _check("ubw_lut_gemv", lib().ubw_lut_gemv(_dev(packed, "packed", _words_dtypes()),
+                                              _dev(alpha_r, "alpha_r", (torch.float32,)),
+                                              _dev(alpha_c, "alpha_c", (torch.float32,)), nb, n, k, g,
+                                              _dev(x, "x", None), _xdtype(x), batch,
+                                              _dev(y, "y", (torch.float32,)), 1 if accumulate else 0,
+                                              ws, wsb, _stream()))
+    return y
+
+
+def vcm_gather_refine(idx, packed_s, alpha_r_s, alpha_c_s, x, n: int, k: int, y, g: int = 8, workspace=None):
+    """y += salient refinement over the columns idx (int32 [s]); returns y."""
+    torch = _torch()
+    x = _as_2d(x)
+    batch = x.shape[0]
+    s = idx.shape[0]
+    ns = alpha_r_s.shape[0]
+    if x.shape[1] != k or tuple(alpha_r_s.shape) != (ns, n) or tuple(alpha_c_s.shape) != (ns, s):
+        raise ValueError("shape mismatch between x, idx, alpha_r_s, alpha_c_s and (n, k)")
+    if packed_s.numel() < packed_words(ns, n, s, g):
+        raise ValueError("packed_s buffer smaller than packed_words()")
+    if tuple(y.shape) != (batch, n):
+        raise ValueError(f"y must be [{batch}, {n}]")
+    ws, wsb = (None, 0) if workspace is None else (_dev(workspace, "workspace", None), workspace.numel() * workspace.element_size())
+    _check("ubw_vcm_gather_refine",
+           lib().ubw_vcm_gather_refine(_dev(idx, "idx", (torch.int32,)), s, _dev(packed_s, "packed_s", _words_dtypes()),
+                                       _dev(alpha_r_s, "alpha_r_s", (torch.float32,)),
+                                       _dev(alpha_c_s, "alpha_c_s", (torch.float32,)), ns, n, k, g,
+                                       _dev(x, "x", None), _xdtype(x), batch, _dev(y, "y", (torch.float32,)),
+                                       ws, wsb, _stream()))
+    return y
+
+
+def check_indices(idx_host, k: int) -> None:
+    """Host check: indices ascending, distinct, inside [0, k). idx_host: numpy int32 array."""
+    import numpy as np
+    a = np.ascontiguousarray(idx_host, dtype=np.int32)
+    _check("ubw_check_indices", lib().ubw_check_indices(a.ctypes.data_as(ctypes.c_void_p), a.shape[0], k))
+
+
+def extract_patterns(packed, nb: int, n: int, k: int, g: int = 8):
+    """Pattern indices [nb, n, ceil(k/g)] (int16 storage of uint16 values)."""
+    torch = _torch()
+    ng = (k + g - 1) // g
+    out = torch.empty((nb, n, ng), dtype=torch.int16, device=packed.device)
+    _check("ubw_extract_patterns", lib().ubw_extract_patterns(_dev(packed, "packed", _words_dtypes()), nb, n, k, g,
+                                                              _dev(out, "out", None), _stream()))
+    return out
+
+
+def lut_gemv_geometry(packed, alpha_r, alpha_c, x, n: int, kv: int, y, *, idx=None, k=None, accumulate=False,
+                      rows_per_group=1, slices_per_group=1):
+    """Main (idx None) or refinement (idx given, k = x's row length) GEMV with an explicit
+    launch geometry; for tests and tuning."""
+    torch = _torch()
+    x = _as_2d(x)
+    batch = x.shape[0]
+    nb = alpha_r.shape[0]
+    vcm = idx is not None
+    _check("ubw_lut_gemv_geometry",
+           lib().ubw_lut_gemv_geometry(_dev(packed, "packed", _words_dtypes()), _dev(alpha_r, "alpha_r", (torch.float32,)),
+                                       _dev(alpha_c, "alpha_c", (torch.float32,)), nb, n, kv,
+                                       _dev(idx, "idx", (torch.int32,)) if vcm else None, k if vcm else kv,
+                                       _dev(x, "x", None), _xdtype(x), batch, _dev(y, "y", (torch.float32,)),
+                                       1 if accumulate else 0, 1 if vcm else 0, rows_per_group, slices_per_group,
+                                       _stream()))
+    return y
+
+
+def bench_stream_read(buf, nbytes: int, out):
+    """Measurement helper: one streaming read of nbytes of buf (see include/ubw.h)."""
+    _check("ubw_bench_stream_read", lib().ubw_bench_stream_read(_dev(buf, "buf", None), int(nbytes),
+                                                                _dev(out, "out", None), _stream()))

@@ -1,0 +1,235 @@
+// C ABI of libubw.so: argument validation, launch-geometry choice and dispatch.
+// Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "../../include/ubw.h"
+#include "ubw_internal.h"
+
+using namespace ubw;
+
+namespace {
+
+constexpr int kVersion = 1;
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool fits_int(int64_t v) { return v >= 1 && v <= INT_MAX / 2; }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? UBW_OK : UBW_EHIP; }
+
+int64_t packed_words_of(int nb, int64_t N, int64_t K) {
+    return (int64_t)nb * ceil_div(N, kTileRows) * ceil_div(K, kSliceCols) * kTileWords;
+}
+
+// Launch geometry: row tiles and column slices per workgroup. A workgroup needs 64 KiB of
+// tables plus its activation buffer, so two fit on a CU. Prefer at least 512 workgroups
+// (two per CU on 256 CUs) when the matrix is large enough; beyond that, give each workgroup
+// more row tiles (tables are built once per slice and activation row, so more rows per
+// workgroup means fewer table entries per lookup), then more slices (fewer partial sums
+// combined by atomics).
+void choose_geometry(int64_t NT, int64_t KT, int batch, int* rpl, int* spg) {
+    const int64_t target = 512;
+    *rpl = 1;
+    *spg = 1;
+    if (NT * KT <= target) return;
+    for (int r : {4, 2}) {
+        if (r <= max_rows_per_group(batch) && ceil_div(NT, r) * KT >= target) {
+            *rpl = r;
+            break;
+        }
+    }
+    for (int64_t s2 = 2; s2 <= KT; ++s2) {
+        if (ceil_div(NT, *rpl) * ceil_div(KT, s2) >= target) *spg = (int)s2;
+        else break;
+    }
+}
+
+int validate_gemv_common(const void* packed, const float* ar, const float* ac, int nb, int64_t N, int64_t Kv,
+                         const void* x, int x_dtype, int batch, const float* y) {
+    if (!packed || !ar || !ac || !x || !y) return UBW_EINVAL;
+    if (nb < 1 || nb > 64 || !fits_int(N) || !fits_int(Kv)) return UBW_EINVAL;
+    if (batch < 1 || batch > UBW_MAX_BATCH) return UBW_EINVAL;
+    if (x_dtype != UBW_F16 && x_dtype != UBW_F32) return UBW_EUNSUPPORTED;
+    if (!aligned16(packed)) return UBW_EALIGN;
+    return UBW_OK;
+}
+
+int run_gemv(GemvArgs a, bool zero_first, hipStream_t s) {
+    const int64_t NT = ceil_div(a.N, kTileRows), KT = ceil_div(a.Kv, kSliceCols);
+    const int64_t n_kgroups = ceil_div(KT, a.slices_per_group);
+    if (zero_first && n_kgroups > 1) {
+        hipError_t e = launch_fill_zero(a.y, (int64_t)a.batch * a.N, s);
+        if (e != hipSuccess) return UBW_EHIP;
+    }
+    (void)NT;
+    return hip_status(launch_gemv8(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ubw_status_str(int status) {
+    switch (status) {
+        case UBW_OK: return "UBW_OK";
+        case UBW_EINVAL: return "UBW_EINVAL: invalid argument (null pointer or size out of range)";
+        case UBW_EUNSUPPORTED: return "UBW_EUNSUPPORTED: unsupported group width, dtype or format";
+        case UBW_EALIGN: return "UBW_EALIGN: pointer not 16-byte aligned";
+        case UBW_ERANGE: return "UBW_ERANGE: index out of range or not ascending";
+        case UBW_EHIP: return "UBW_EHIP: HIP runtime error";
+        case UBW_ESIZE: return "UBW_ESIZE: buffer too small";
+        default: return "unknown ubw status";
+    }
+}
+
+int ubw_version(void) { return kVersion; }
+
+int ubw_packed_words(int nb, int64_t N, int64_t K, int g, int64_t* out_words) {
+    if (!out_words || nb < 1 || nb > 64 || !fits_int(N) || !fits_int(K)) return UBW_EINVAL;
+    if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
+    *out_words = packed_words_of(nb, N, K);
+    return UBW_OK;
+}
+
+int ubw_pack_bases(const void* src, int src_fmt, int nb, int64_t N, int64_t K, int g, uint32_t* dst,
+                   void* stream) {
+    if (!src || !dst || nb < 1 || nb > 64 || !fits_int(N) || !fits_int(K)) return UBW_EINVAL;
+    if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
+    if (src_fmt != UBW_SRC_CANON_BITS && src_fmt != UBW_SRC_INT8_SIGNS) return UBW_EUNSUPPORTED;
+    if (!aligned16(dst)) return UBW_EALIGN;
+    if (packed_words_of(nb, N, K) > (int64_t)INT_MAX * 256) return UBW_ERANGE;
+    return hip_status(launch_pack(src, src_fmt, nb, (int)N, (int)K, dst, as_stream(stream)));
+}
+
+int ubw_ternary_encode(const int8_t* w, const float* scale, int64_t N, int64_t K, int g, uint32_t* packed,
+                       float* alpha_r, float* alpha_c, void* stream) {
+    if (!w || !scale || !packed || !alpha_r || !alpha_c || !fits_int(N) || !fits_int(K)) return UBW_EINVAL;
+    if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
+    if (!aligned16(packed)) return UBW_EALIGN;
+    return hip_status(launch_ternary(w, scale, (int)N, (int)K, packed, alpha_r, alpha_c, as_stream(stream)));
+}
+
+int ubw_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, int nb, int64_t K, int g,
+                  float* lut, void* stream) {
+    if (!x || !alpha_c || !lut || nb < 1 || nb > 64 || !fits_int(K)) return UBW_EINVAL;
+    if (batch < 1 || batch > UBW_MAX_BATCH) return UBW_EINVAL;
+    if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
+    if (x_dtype != UBW_F16 && x_dtype != UBW_F32) return UBW_EUNSUPPORTED;
+    return hip_status(launch_build_lut(x, x_dtype, batch, alpha_c, nb, (int)K, g, lut, as_stream(stream)));
+}
+
+int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out) {
+    if (!out || nb < 1 || !fits_int(N) || !fits_int(K) || batch < 1 || batch > UBW_MAX_BATCH) return UBW_EINVAL;
+    if (g != 8) return UBW_EUNSUPPORTED;
+    *out = 0;
+    return UBW_OK;
+}
+
+int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb, int64_t N,
+                 int64_t K, int g, const void* x, int x_dtype, int batch, float* y, int accumulate,
+                 void* workspace, size_t ws_bytes, void* stream) {
+    (void)workspace;
+    (void)ws_bytes;
+    int st = validate_gemv_common(packed, alpha_r, alpha_c, nb, N, K, x, x_dtype, batch, y);
+    if (st != UBW_OK) return st;
+    if (g != 8) return UBW_EUNSUPPORTED;
+    GemvArgs a{};
+    a.packed = packed;
+    a.alpha_r = alpha_r;
+    a.alpha_c = alpha_c;
+    a.nb = nb;
+    a.N = (int)N;
+    a.Kv = (int)K;
+    a.x = x;
+    a.x_dtype = x_dtype;
+    a.ldx = K;
+    a.idx = nullptr;
+    a.batch = batch;
+    a.y = y;
+    a.accumulate = accumulate ? 1 : 0;
+    choose_geometry(ceil_div(N, kTileRows), ceil_div(K, kSliceCols), batch, &a.rows_per_group, &a.slices_per_group);
+    return run_gemv(a, !accumulate, as_stream(stream));
+}
+
+int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_s, const float* alpha_r_s,
+                          const float* alpha_c_s, int ns, int64_t N, int64_t K, int g, const void* x,
+                          int x_dtype, int batch, float* y, void* workspace, size_t ws_bytes, void* stream) {
+    (void)workspace;
+    (void)ws_bytes;
+    if (!idx) return UBW_EINVAL;
+    int st = validate_gemv_common(packed_s, alpha_r_s, alpha_c_s, ns, N, s, x, x_dtype, batch, y);
+    if (st != UBW_OK) return st;
+    if (!fits_int(K)) return UBW_EINVAL;
+    if (g != 8) return UBW_EUNSUPPORTED;
+    GemvArgs a{};
+    a.packed = packed_s;
+    a.alpha_r = alpha_r_s;
+    a.alpha_c = alpha_c_s;
+    a.nb = ns;
+    a.N = (int)N;
+    a.Kv = (int)s;
+    a.x = x;
+    a.x_dtype = x_dtype;
+    a.ldx = K;
+    a.idx = idx;
+    a.batch = batch;
+    a.y = y;
+    a.accumulate = 1;
+    choose_geometry(ceil_div(N, kTileRows), ceil_div(s, kSliceCols), batch, &a.rows_per_group, &a.slices_per_group);
+    return run_gemv(a, false, as_stream(stream));
+}
+
+int ubw_check_indices(const int32_t* idx_host, int64_t s, int64_t K) {
+    if (!idx_host || s < 1 || K < 1) return UBW_EINVAL;
+    for (int64_t q = 0; q < s; ++q) {
+        if (idx_host[q] < 0 || idx_host[q] >= K) return UBW_ERANGE;
+        if (q > 0 && idx_host[q] <= idx_host[q - 1]) return UBW_ERANGE;
+    }
+    return UBW_OK;
+}
+
+int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, int g, uint16_t* out,
+                         void* stream) {
+    if (!packed || !out || nb < 1 || nb > 64 || !fits_int(N) || !fits_int(K)) return UBW_EINVAL;
+    if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
+    if (!aligned16(packed)) return UBW_EALIGN;
+    return hip_status(launch_extract(packed, nb, (int)N, (int)K, g, out, as_stream(stream)));
+}
+
+int ubw_lut_gemv_geometry(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb, int64_t N,
+                          int64_t Kv, const int32_t* idx, int64_t K, const void* x, int x_dtype, int batch,
+                          float* y, int accumulate, int vcm, int rows_per_group, int slices_per_group,
+                          void* stream) {
+    int st = validate_gemv_common(packed, alpha_r, alpha_c, nb, N, Kv, x, x_dtype, batch, y);
+    if (st != UBW_OK) return st;
+    if (rows_per_group != 1 && rows_per_group != 2 && rows_per_group != 4) return UBW_ERANGE;
+    if (rows_per_group > max_rows_per_group(batch)) return UBW_ERANGE;
+    if (slices_per_group < 1) return UBW_ERANGE;
+    if (vcm && (!idx || !accumulate || !fits_int(K))) return UBW_EINVAL;
+    GemvArgs a{};
+    a.packed = packed;
+    a.alpha_r = alpha_r;
+    a.alpha_c = alpha_c;
+    a.nb = nb;
+    a.N = (int)N;
+    a.Kv = (int)Kv;
+    a.x = x;
+    a.x_dtype = x_dtype;
+    a.ldx = vcm ? K : Kv;
+    a.idx = vcm ? idx : nullptr;
+    a.batch = batch;
+    a.y = y;
+    a.accumulate = accumulate ? 1 : 0;
+    a.rows_per_group = rows_per_group;
+    a.slices_per_group = slices_per_group;
+    return run_gemv(a, !accumulate, as_stream(stream));
+}
+
+int ubw_bench_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
+    if (!buf || !out || bytes < 16 || (bytes & 15) != 0) return UBW_EINVAL;
+    if (!aligned16(buf)) return UBW_EALIGN;
+    return hip_status(launch_stream_read(buf, bytes, out, as_stream(stream)));
+}
+
+}  // extern "C"
