@@ -117,9 +117,17 @@ int ubw_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, i
                   int64_t K, int g, float* lut, void* stream);
 
 /*
- * Workspace bytes ubw_lut_gemv / ubw_vcm_gather_refine need for this shape. The current
- * kernels need none (0); the argument pair is kept so a caller's allocation code does not
- * change when a kernel starts using one. *out is a host pointer.
+ * Workspace bytes the GEMV calls use for this shape (64 + 256 * ceil(N / 256)). *out is a
+ * host pointer.
+ * A workspace lets a call that overwrites y (accumulate = 0) run as ONE launch when the whole
+ * grid fits on the device at once: the column slices of a row are combined with fp32 atomics,
+ * the workgroup of each 256-row group's first column slices zeroes those rows and raises a
+ * flag in the workspace, and the group's other workgroups read the flag before adding.
+ * Without a workspace (NULL, 0 bytes), or for grids larger than the device holds at once, the
+ * library zero-fills y with a separate launch first. Rules: zero-fill the workspace once after allocating it (the kernels leave it
+ * consistent after every call, whatever the shape); a workspace serves calls on one stream at a
+ * time (calls that may run concurrently need separate workspaces); word 0 becomes nonzero only
+ * if a wait gave up (an internal error that should never occur).
  */
 int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out);
 
@@ -131,10 +139,10 @@ int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* 
  * summation order (not the result beyond rounding) varies between runs.
  *   packed       from ubw_pack_bases(nb, N, K, g=8)
  *   accumulate   0: y = result; 1: y += result
- *   workspace    may be NULL when ws_bytes == 0
- * Errors: UBW_EINVAL (null, nb < 1, N < 1, K < 1, batch not in [1, UBW_MAX_BATCH]),
- *         UBW_EUNSUPPORTED (g != 8, dtype), UBW_EALIGN (packed), UBW_ESIZE (ws_bytes),
- *         UBW_EHIP.
+ *   workspace    ubw_workspace_bytes() bytes, or NULL with ws_bytes == 0 (see there)
+ * Errors: UBW_EINVAL (null, nb < 1, N < 1, K < 1, batch not in [1, UBW_MAX_BATCH], workspace
+ *         NULL with ws_bytes != 0), UBW_EUNSUPPORTED (g != 8, dtype), UBW_EALIGN (packed or
+ *         workspace), UBW_ESIZE (ws_bytes too small), UBW_EHIP.
  */
 int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb,
                  int64_t N, int64_t K, int g, const void* x, int x_dtype, int batch,
@@ -160,6 +168,19 @@ int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * The whole step in ONE launch: main bases plus salient refinement (ubw_lut_gemv followed by
+ * ubw_vcm_gather_refine on the same x and y, with the same results up to fp32 summation
+ * order). Section "2. Kernel innovation", VCM: the mapping exists so that the refinement runs
+ * in the same unified kernel as the global bases; here the refinement's workgroups are part
+ * of the main grid. Arguments as the two calls; accumulate and workspace as ubw_lut_gemv.
+ */
+int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb,
+                         const int32_t* idx, int64_t s, const uint32_t* packed_s,
+                         const float* alpha_r_s, const float* alpha_c_s, int ns, int64_t N,
+                         int64_t K, int g, const void* x, int x_dtype, int batch, float* y,
+                         int accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Host-side check of a salient index list: every idx[q] in [0, K) and strictly ascending.
  * idx is a HOST pointer. Returns UBW_OK or UBW_ERANGE (UBW_EINVAL for null / s < 1).
  */
@@ -175,15 +196,17 @@ int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, i
 
 /*
  * Test and tuning export: ubw_lut_gemv (vcm = 0) or ubw_vcm_gather_refine (vcm = 1) with an
- * explicit launch geometry. rows_per_group in {1, 2, 4} row tiles of 256 rows per
- * workgroup; slices_per_group >= 1 column slices of 256 columns per workgroup. Results
+ * explicit launch geometry. rows_per_group in {1, 2} row tiles of 256 rows per workgroup;
+ * slices_per_group >= 1 column slices of 256 columns per workgroup. Results
  * equal the default geometry's up to fp32 summation order. For vcm = 0, idx is ignored and
- * Kv = K; for vcm = 1, Kv = s, and accumulate must be 1.
+ * Kv = K; for vcm = 1, Kv = s. rows_per_group must be 1 for batch above 2 (UBW_ERANGE
+ * otherwise). workspace as ubw_lut_gemv.
  */
 int ubw_lut_gemv_geometry(const uint32_t* packed, const float* alpha_r, const float* alpha_c,
                           int nb, int64_t N, int64_t Kv, const int32_t* idx, int64_t K,
                           const void* x, int x_dtype, int batch, float* y, int accumulate,
-                          int vcm, int rows_per_group, int slices_per_group, void* stream);
+                          int vcm, int rows_per_group, int slices_per_group, void* workspace,
+                          size_t ws_bytes, void* stream);
 
 /*
  * Measurement helper (no part of the product computation): reads `bytes` bytes of `buf` with

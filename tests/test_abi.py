@@ -13,7 +13,7 @@ import ultra_bit_weight_uint32_amd as ubw
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ubw.h")
 
-EINVAL, EUNSUP, EALIGN, ERANGE = -1, -2, -3, -4
+EINVAL, EUNSUP, EALIGN, ERANGE, ESIZE = -1, -2, -3, -4, -6
 FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced on these paths
 MISALIGNED = ctypes.c_void_p(0x10004)
 
@@ -56,7 +56,9 @@ def test_packed_words_sizes():
 
 
 def test_workspace_bytes():
-    assert ubw.workspace_bytes(2, 4096, 4096, 8, 1) == 0
+    # 16 header words + 64 words per 256-row group
+    assert ubw.workspace_bytes(2, 4096, 4096, 8, 1) == 4 * (16 + 64 * 16)
+    assert ubw.workspace_bytes(1, 1, 1, 8, 1) == 4 * (16 + 64)
     sz = ctypes.c_size_t()
     assert ubw.lib().ubw_workspace_bytes(2, 4096, 4096, 8, 17, ctypes.byref(sz)) == EINVAL
     assert ubw.lib().ubw_workspace_bytes(2, 4096, 4096, 4, 1, ctypes.byref(sz)) == EUNSUP
@@ -74,6 +76,7 @@ def gemv_args(**kw):
     (dict(x=None), EINVAL), (dict(y=None), EINVAL), (dict(nb=0), EINVAL), (dict(N=0), EINVAL),
     (dict(K=0), EINVAL), (dict(N=-5), EINVAL), (dict(batch=0), EINVAL), (dict(batch=17), EINVAL),
     (dict(x_dtype=7), EUNSUP), (dict(g=4), EUNSUP), (dict(g=5), EUNSUP), (dict(packed=MISALIGNED), EALIGN),
+    (dict(ws=None, wsb=8), EINVAL), (dict(ws=MISALIGNED, wsb=4096), EALIGN), (dict(ws=FAKE, wsb=8), ESIZE),
 ])
 def test_lut_gemv_rejects(kw, status):
     assert gemv_args(**kw) == status
@@ -93,14 +96,29 @@ def test_vcm_rejects(kw, status):
 def test_geometry_rejects():
     L = ubw.lib()
     base = [FAKE, FAKE, FAKE, 2, 64, 64, None, 64, FAKE, 1, 1, FAKE, 0, 0]
-    assert L.ubw_lut_gemv_geometry(*base, 3, 1, None) == ERANGE      # rows_per_group not in {1,2,4}
-    assert L.ubw_lut_gemv_geometry(*base, 1, 0, None) == ERANGE      # slices_per_group < 1
+    tail = [None, 0, None]
+    assert L.ubw_lut_gemv_geometry(*base, 3, 1, *tail) == ERANGE      # rows_per_group not in {1,2}
+    assert L.ubw_lut_gemv_geometry(*base, 4, 1, *tail) == ERANGE
+    assert L.ubw_lut_gemv_geometry(*base, 1, 0, *tail) == ERANGE      # slices_per_group < 1
     b4 = list(base)
-    b4[10] = 4                                                       # batch 4 allows only 1 row tile
-    assert L.ubw_lut_gemv_geometry(*b4, 2, 1, None) == ERANGE
+    b4[10] = 4                                                        # batch 4 allows only 1 row tile
+    assert L.ubw_lut_gemv_geometry(*b4, 2, 1, *tail) == ERANGE
     vcm = list(base)
-    vcm[13] = 1                                                      # vcm without idx
-    assert L.ubw_lut_gemv_geometry(*vcm, 1, 1, None) == EINVAL
+    vcm[13] = 1                                                       # vcm without idx
+    assert L.ubw_lut_gemv_geometry(*vcm, 1, 1, *tail) == EINVAL
+    assert L.ubw_lut_gemv_geometry(*base, 1, 1, FAKE, 4, None) == ESIZE
+
+
+def test_refined_rejects():
+    L = ubw.lib()
+    args = dict(packed=FAKE, ar=FAKE, ac=FAKE, nb=2, idx=FAKE, s=10, packed_s=FAKE, ar_s=FAKE, ac_s=FAKE, ns=2,
+                N=64, K=64, g=8, x=FAKE, x_dtype=1, batch=1, y=FAKE, acc=0, ws=None, wsb=0, stream=None)
+    for kw, status in [(dict(idx=None), EINVAL), (dict(s=0), EINVAL), (dict(ns=0), EINVAL), (dict(nb=0), EINVAL),
+                       (dict(packed_s=MISALIGNED), EALIGN), (dict(g=4), EUNSUP), (dict(ws=FAKE, wsb=4), ESIZE),
+                       (dict(batch=17), EINVAL)]:
+        a = dict(args)
+        a.update(kw)
+        assert L.ubw_lut_gemv_refined(*a.values()) == status, kw
 
 
 def test_other_entry_points_reject():

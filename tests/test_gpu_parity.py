@@ -49,15 +49,33 @@ def pack(bits, k):
     return ubw.pack_bases(dev(bits), nb, n, k)
 
 
-def gpu_gemv(g, packed=None, refine=True, y=None, accumulate=False):
-    """Main GEMV (+ refinement) of a workloads.Gemv on the GPU; returns float64 [batch, n]."""
+MODES = ("two_calls", "two_calls_ws", "fused", "fused_ws")
+
+
+def gpu_gemv(g, packed=None, refine=True, y=None, accumulate=False, mode="fused_ws", ws=None):
+    """Main GEMV (+ refinement) of a workloads.Gemv on the GPU; returns float64 [batch, n].
+    mode: two calls (lut_gemv then vcm_gather_refine) or the single fused launch, each with a
+    workspace (single launch also for y = result) or without one (zero-fill launch first)."""
     packed = pack(g.bits, g.k) if packed is None else packed
     x = dev(g.x)
-    y = ubw.lut_gemv(packed, dev(g.alpha_r), dev(g.alpha_c), x, g.n, g.k, y=y, accumulate=accumulate)
-    if refine and g.s:
-        ps = pack(g.bits_s, g.s)
-        ubw.vcm_gather_refine(dev(g.idx), ps, dev(g.alpha_r_s), dev(g.alpha_c_s), x, g.n, g.k, y)
-    return host(y).astype(np.float64)
+    if mode.endswith("_ws") and ws is None:
+        ws = ubw.workspace(g.n, DEV)
+    elif not mode.endswith("_ws"):
+        ws = None
+    if mode.startswith("fused") and refine and g.s:
+        y = ubw.lut_gemv_refined(packed, dev(g.alpha_r), dev(g.alpha_c), dev(g.idx), pack(g.bits_s, g.s),
+                                 dev(g.alpha_r_s), dev(g.alpha_c_s), x, g.n, g.k, y=y, accumulate=accumulate,
+                                 workspace=ws)
+    else:
+        y = ubw.lut_gemv(packed, dev(g.alpha_r), dev(g.alpha_c), x, g.n, g.k, y=y, accumulate=accumulate,
+                         workspace=ws)
+        if refine and g.s:
+            ps = pack(g.bits_s, g.s)
+            ubw.vcm_gather_refine(dev(g.idx), ps, dev(g.alpha_r_s), dev(g.alpha_c_s), x, g.n, g.k, y, workspace=ws)
+    out = host(y).astype(np.float64)
+    if ws is not None:
+        assert host(ws)[0] == 0, "a workgroup gave up waiting for its row group's flag"
+    return out
 
 
 def oracle_gemv(g, refine=True):
@@ -146,10 +164,11 @@ INT_SHAPES = [(1, 1, 1), (5, 33, 2), (256, 256, 1), (300, 700, 3), (1000, 2050, 
 def test_gemv_integer_exact(n, k, nb, batch):
     rng = np.random.default_rng(n + 7 * k + nb + 100 * batch)
     g = make_integer_gemv(rng, n, k, nb, batch=batch)
-    assert np.array_equal(gpu_gemv(g), oracle_gemv(g))
+    for mode in ("two_calls", "two_calls_ws"):
+        assert np.array_equal(gpu_gemv(g, mode=mode), oracle_gemv(g)), mode
 
 
-@pytest.mark.parametrize("rpg", [1, 2, 4])
+@pytest.mark.parametrize("rpg", [1, 2])
 @pytest.mark.parametrize("spg", [1, 2, 3, 7])
 def test_gemv_geometries_integer_exact(rpg, spg):
     """Every workgroup shape gives the same exact result (5 row tiles x 7 column slices, both
@@ -157,10 +176,11 @@ def test_gemv_geometries_integer_exact(rpg, spg):
     rng = np.random.default_rng(rpg * 10 + spg)
     n, k = 4 * 256 + 100, 6 * 256 + 77
     g = make_integer_gemv(rng, n, k, 2, batch=1)
-    y = torch.full((1, n), 123.0, device=DEV)
-    ubw.lut_gemv_geometry(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y,
-                          rows_per_group=rpg, slices_per_group=spg)
-    assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g))
+    for ws in (None, ubw.workspace(n, DEV)):
+        y = torch.full((1, n), float("nan"), device=DEV)
+        ubw.lut_gemv_geometry(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y,
+                              rows_per_group=rpg, slices_per_group=spg, workspace=ws)
+        assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g))
 
 
 @pytest.mark.parametrize("batch", [2, 4, 8, 16])
@@ -177,13 +197,36 @@ def test_gemv_geometries_batched(batch):
         assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g))
 
 
-def test_gemv_accumulate():
+@pytest.mark.parametrize("mode", MODES)
+def test_gemv_accumulate(mode):
     rng = np.random.default_rng(11)
-    g = make_integer_gemv(rng, 700, 1500, 2, batch=2)
+    g = make_integer_gemv(rng, 700, 1500, 2, s=70, ns=1, batch=2)
     y0 = rng.integers(-100, 100, (2, 700)).astype(np.float32)
-    y = dev(y0)
-    out = gpu_gemv(g, y=y, accumulate=True)
+    out = gpu_gemv(g, y=dev(y0), accumulate=True, mode=mode)
     assert np.array_equal(out, oracle_gemv(g) + y0)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_overwrite_ignores_previous_contents(mode):
+    """y = result must not depend on what y held (NaN garbage here)."""
+    rng = np.random.default_rng(13)
+    g = make_integer_gemv(rng, 900, 3000, 2, s=100, ns=2, batch=3)
+    y = torch.full((3, 900), float("nan"), device=DEV)
+    assert np.array_equal(gpu_gemv(g, y=y, mode=mode), oracle_gemv(g))
+
+
+def test_workspace_reused_across_shapes_and_calls():
+    """One workspace, many calls of different shapes back to back on one stream: the row-group
+    counters stay consistent (every result exact, error word zero)."""
+    rng = np.random.default_rng(14)
+    ws = ubw.workspace(5000, DEV)
+    cases = [make_integer_gemv(rng, n, k, nb, s=s, ns=ns, batch=b)
+             for n, k, nb, s, ns, b in ((5000, 2000, 2, 90, 2, 1), (300, 700, 1, 0, 0, 2), (4096, 4096, 2, 205, 2, 1),
+                                        (1000, 2600, 3, 33, 1, 4), (5000, 600, 2, 300, 2, 16))]
+    for rep in range(3):
+        for g in cases:
+            mode = "fused_ws" if g.s else "two_calls_ws"
+            assert np.array_equal(gpu_gemv(g, mode=mode, ws=ws), oracle_gemv(g)), (rep, g.n, g.k)
 
 
 def test_one_hot_reads_signs():
@@ -215,10 +258,12 @@ def test_gemv_float_tolerance(n, k, nb, xdt, batch):
 
 @pytest.mark.parametrize("k,s", [(64, 1), (700, 37), (4096, 205), (1000, 300), (2000, 1434)])
 @pytest.mark.parametrize("batch", [1, 4])
-def test_vcm_integer_exact(k, s, batch):
-    rng = np.random.default_rng(k + s + batch)
-    g = make_integer_gemv(rng, 300, k, 2, s=s, ns=2, batch=batch)
-    assert np.array_equal(gpu_gemv(g), oracle_gemv(g))
+@pytest.mark.parametrize("ns", [1, 2, 3])
+def test_vcm_integer_exact(k, s, batch, ns):
+    rng = np.random.default_rng(k + s + batch + 10 * ns)
+    g = make_integer_gemv(rng, 300, k, 2, s=s, ns=ns, batch=batch)
+    for mode in MODES:
+        assert np.array_equal(gpu_gemv(g, mode=mode), oracle_gemv(g)), mode
 
 
 def test_vcm_geometries_integer_exact():
@@ -231,6 +276,11 @@ def test_vcm_geometries_integer_exact():
         y = torch.zeros((2, n), device=DEV)
         ubw.lut_gemv_geometry(ps, dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), n, s, y, idx=dev(g.idx), k=k,
                               accumulate=True, rows_per_group=rpg, slices_per_group=spg)
+        assert np.array_equal(host(y).astype(np.float64), want)
+        y = torch.full((2, n), float("nan"), device=DEV)
+        ubw.lut_gemv_geometry(ps, dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), n, s, y, idx=dev(g.idx), k=k,
+                              accumulate=False, rows_per_group=rpg, slices_per_group=spg,
+                              workspace=ubw.workspace(n, DEV))
         assert np.array_equal(host(y).astype(np.float64), want)
 
 
@@ -332,10 +382,11 @@ def test_config1_full():
     assert max_rel_err(gpu_gemv(g), oracle_gemv(g)) <= TOL
 
 
-def test_config3_full():
+@pytest.mark.parametrize("mode", MODES)
+def test_config3_full(mode):
     g = config3().gemvs[0]
-    assert max_rel_err(gpu_gemv(g), oracle_gemv(g)) <= TOL
-    assert max_rel_err(gpu_gemv(g, refine=False), oracle_gemv(g, refine=False)) <= TOL
+    assert max_rel_err(gpu_gemv(g, mode=mode), oracle_gemv(g)) <= TOL
+    assert max_rel_err(gpu_gemv(g, refine=False, mode=mode), oracle_gemv(g, refine=False)) <= TOL
 
 
 def test_config4_full():

@@ -25,7 +25,7 @@ MAX_BATCH = 16
 # every symbol include/ubw.h declares
 EXPORTS = (
     "ubw_status_str", "ubw_version", "ubw_packed_words", "ubw_pack_bases", "ubw_ternary_encode",
-    "ubw_build_lut", "ubw_workspace_bytes", "ubw_lut_gemv", "ubw_vcm_gather_refine",
+    "ubw_build_lut", "ubw_workspace_bytes", "ubw_lut_gemv", "ubw_vcm_gather_refine", "ubw_lut_gemv_refined",
     "ubw_check_indices", "ubw_extract_patterns", "ubw_lut_gemv_geometry", "ubw_bench_stream_read",
 )
 
@@ -60,7 +60,8 @@ def lib():
         "ubw_vcm_gather_refine": ([P, I64, P, P, P, I, I64, I64, I, P, I, I, P, P, SZ, P], I),
         "ubw_check_indices": ([P, I64, I64], I),
         "ubw_extract_patterns": ([P, I, I64, I64, I, P, P], I),
-        "ubw_lut_gemv_geometry": ([P, P, P, I, I64, I64, P, I64, P, I, I, P, I, I, I, I, P], I),
+        "ubw_lut_gemv_refined": ([P, P, P, I, P, I64, P, P, P, I, I64, I64, I, P, I, I, P, I, P, SZ, P], I),
+        "ubw_lut_gemv_geometry": ([P, P, P, I, I64, I64, P, I64, P, I, I, P, I, I, I, I, P, SZ, P], I),
         "ubw_bench_stream_read": ([P, I64, P, P], I),
     }
     for name, (args, res) in sig.items():
@@ -139,6 +140,18 @@ def workspace_bytes(nb: int, n: int, k: int, g: int = 8, batch: int = 1) -> int:
     return out.value
 
 
+def workspace(n: int, device="cuda"):
+    """A zero-filled workspace for GEMV calls with n output rows (reusable on one stream)."""
+    torch = _torch()
+    return torch.zeros(workspace_bytes(1, n, 1) // 4, dtype=torch.int32, device=device)
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _dev(workspace, "workspace", None), workspace.numel() * workspace.element_size()
+
+
 def pack_bases(src, nb: int, n: int, k: int, g: int = 8, out=None):
     """Pack canonical uint32 words [nb, n, ceil(k/32)] (int32/uint32 tensor) or int8 signs
     [nb, n, k] into the GPU tile layout; returns an int32 tensor of packed_words() words."""
@@ -210,7 +223,7 @@ def lut_gemv(packed, alpha_r, alpha_c, x, n: int, k: int, g: int = 8, y=None, ac
         y = torch.empty((batch, n), dtype=torch.float32, device=x.device)
     if tuple(y.shape) != (batch, n):
         raise ValueError(f"y must be [{batch}, {n}]")
-    ws, wsb = (None, 0) if workspace is None else (_dev(workspace, "workspace", None), workspace.numel() * workspace.element_size())
+    ws, wsb = _ws(workspace)
     _check("ubw_lut_gemv", lib().ubw_lut_gemv(_dev(packed, "packed", _words_dtypes()),
                                               _dev(alpha_r, "alpha_r", (torch.float32,)),
                                               _dev(alpha_c, "alpha_c", (torch.float32,)), nb, n, k, g,
@@ -233,13 +246,44 @@ def vcm_gather_refine(idx, packed_s, alpha_r_s, alpha_c_s, x, n: int, k: int, y,
         raise ValueError("packed_s buffer smaller than packed_words()")
     if tuple(y.shape) != (batch, n):
         raise ValueError(f"y must be [{batch}, {n}]")
-    ws, wsb = (None, 0) if workspace is None else (_dev(workspace, "workspace", None), workspace.numel() * workspace.element_size())
+    ws, wsb = _ws(workspace)
     _check("ubw_vcm_gather_refine",
            lib().ubw_vcm_gather_refine(_dev(idx, "idx", (torch.int32,)), s, _dev(packed_s, "packed_s", _words_dtypes()),
                                        _dev(alpha_r_s, "alpha_r_s", (torch.float32,)),
                                        _dev(alpha_c_s, "alpha_c_s", (torch.float32,)), ns, n, k, g,
                                        _dev(x, "x", None), _xdtype(x), batch, _dev(y, "y", (torch.float32,)),
                                        ws, wsb, _stream()))
+    return y
+
+
+def lut_gemv_refined(packed, alpha_r, alpha_c, idx, packed_s, alpha_r_s, alpha_c_s, x, n: int, k: int, g: int = 8,
+                     y=None, accumulate: bool = False, workspace=None):
+    """Main bases plus salient refinement in one launch; returns y [batch, N]."""
+    torch = _torch()
+    x = _as_2d(x)
+    batch = x.shape[0]
+    nb, ns, s = alpha_r.shape[0], alpha_r_s.shape[0], idx.shape[0]
+    if x.shape[1] != k or tuple(alpha_r.shape) != (nb, n) or tuple(alpha_c.shape) != (nb, k):
+        raise ValueError("shape mismatch between x, alpha_r, alpha_c and (n, k)")
+    if tuple(alpha_r_s.shape) != (ns, n) or tuple(alpha_c_s.shape) != (ns, s):
+        raise ValueError("shape mismatch between idx, alpha_r_s, alpha_c_s and n")
+    if packed.numel() < packed_words(nb, n, k, g) or packed_s.numel() < packed_words(ns, n, s, g):
+        raise ValueError("packed buffer smaller than packed_words()")
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs y")
+        y = torch.empty((batch, n), dtype=torch.float32, device=x.device)
+    if tuple(y.shape) != (batch, n):
+        raise ValueError(f"y must be [{batch}, {n}]")
+    ws, wsb = _ws(workspace)
+    F32 = (torch.float32,)
+    _check("ubw_lut_gemv_refined",
+           lib().ubw_lut_gemv_refined(_dev(packed, "packed", _words_dtypes()), _dev(alpha_r, "alpha_r", F32),
+                                      _dev(alpha_c, "alpha_c", F32), nb, _dev(idx, "idx", (torch.int32,)), s,
+                                      _dev(packed_s, "packed_s", _words_dtypes()), _dev(alpha_r_s, "alpha_r_s", F32),
+                                      _dev(alpha_c_s, "alpha_c_s", F32), ns, n, k, g, _dev(x, "x", None),
+                                      _xdtype(x), batch, _dev(y, "y", F32), 1 if accumulate else 0, ws, wsb,
+                                      _stream()))
     return y
 
 
@@ -261,7 +305,7 @@ def extract_patterns(packed, nb: int, n: int, k: int, g: int = 8):
 
 
 def lut_gemv_geometry(packed, alpha_r, alpha_c, x, n: int, kv: int, y, *, idx=None, k=None, accumulate=False,
-                      rows_per_group=1, slices_per_group=1):
+                      rows_per_group=1, slices_per_group=1, workspace=None):
     """Main (idx None) or refinement (idx given, k = x's row length) GEMV with an explicit
     launch geometry; for tests and tuning."""
     torch = _torch()
@@ -275,7 +319,7 @@ def lut_gemv_geometry(packed, alpha_r, alpha_c, x, n: int, kv: int, y, *, idx=No
                                        _dev(idx, "idx", (torch.int32,)) if vcm else None, k if vcm else kv,
                                        _dev(x, "x", None), _xdtype(x), batch, _dev(y, "y", (torch.float32,)),
                                        1 if accumulate else 0, 1 if vcm else 0, rows_per_group, slices_per_group,
-                                       _stream()))
+                                       *_ws(workspace), _stream()))
     return y
 
 

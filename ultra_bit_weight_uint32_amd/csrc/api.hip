@@ -11,7 +11,7 @@ using namespace ubw;
 
 namespace {
 
-constexpr int kVersion = 1;
+constexpr int kVersion = 2;
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -33,7 +33,7 @@ void choose_geometry(int64_t NT, int64_t KT, int batch, int* rpl, int* spg) {
     *rpl = 1;
     *spg = 1;
     if (NT * KT <= target) return;
-    for (int r : {4, 2}) {
+    for (int r : {2}) {
         if (r <= max_rows_per_group(batch) && ceil_div(NT, r) * KT >= target) {
             *rpl = r;
             break;
@@ -55,15 +55,43 @@ int validate_gemv_common(const void* packed, const float* ar, const float* ac, i
     return UBW_OK;
 }
 
-int run_gemv(GemvArgs a, bool zero_first, hipStream_t s) {
-    const int64_t NT = ceil_div(a.N, kTileRows), KT = ceil_div(a.Kv, kSliceCols);
-    const int64_t n_kgroups = ceil_div(KT, a.slices_per_group);
-    if (zero_first && n_kgroups > 1) {
-        hipError_t e = launch_fill_zero(a.y, (int64_t)a.batch * a.N, s);
-        if (e != hipSuccess) return UBW_EHIP;
-    }
-    (void)NT;
-    return hip_status(launch_gemv8(a, s));
+// Workspace check: NULL with 0 bytes means "none" (the y = result mode then zero-fills y with
+// a separate launch); otherwise it must hold the counters for N rows.
+int check_workspace(void* ws, size_t ws_bytes, int64_t N, uint32_t** out) {
+    *out = nullptr;
+    if (ws == nullptr) return ws_bytes == 0 ? UBW_OK : UBW_EINVAL;
+    if (!aligned16(ws)) return UBW_EALIGN;
+    if (ws_bytes < (size_t)step_workspace_words(N) * 4) return UBW_ESIZE;
+    *out = static_cast<uint32_t*>(ws);
+    return UBW_OK;
+}
+
+Segment make_segment(const uint32_t* packed, const float* ar, const float* ac, const int32_t* idx, int nb,
+                     int64_t Kv) {
+    Segment g{};
+    g.packed = packed;
+    g.alpha_r = ar;
+    g.alpha_c = ac;
+    g.idx = idx;
+    g.nb = nb;
+    g.Kv = (int)Kv;
+    g.slices_per_group = 1;
+    return g;
+}
+
+StepArgs make_step(int64_t N, const void* x, int x_dtype, int64_t K, int batch, float* y, int accumulate,
+                   uint32_t* ws) {
+    StepArgs a{};
+    a.N = (int)N;
+    a.x = x;
+    a.x_dtype = x_dtype;
+    a.ldx = K;
+    a.batch = batch;
+    a.y = y;
+    a.accumulate = accumulate ? 1 : 0;
+    a.ws = ws;
+    a.rows_per_group = 1;
+    return a;
 }
 
 }  // namespace
@@ -122,62 +150,64 @@ int ubw_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, i
 int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out) {
     if (!out || nb < 1 || !fits_int(N) || !fits_int(K) || batch < 1 || batch > UBW_MAX_BATCH) return UBW_EINVAL;
     if (g != 8) return UBW_EUNSUPPORTED;
-    *out = 0;
+    *out = (size_t)step_workspace_words(N) * 4;
     return UBW_OK;
 }
 
 int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb, int64_t N,
                  int64_t K, int g, const void* x, int x_dtype, int batch, float* y, int accumulate,
                  void* workspace, size_t ws_bytes, void* stream) {
-    (void)workspace;
-    (void)ws_bytes;
     int st = validate_gemv_common(packed, alpha_r, alpha_c, nb, N, K, x, x_dtype, batch, y);
     if (st != UBW_OK) return st;
     if (g != 8) return UBW_EUNSUPPORTED;
-    GemvArgs a{};
-    a.packed = packed;
-    a.alpha_r = alpha_r;
-    a.alpha_c = alpha_c;
-    a.nb = nb;
-    a.N = (int)N;
-    a.Kv = (int)K;
-    a.x = x;
-    a.x_dtype = x_dtype;
-    a.ldx = K;
-    a.idx = nullptr;
-    a.batch = batch;
-    a.y = y;
-    a.accumulate = accumulate ? 1 : 0;
-    choose_geometry(ceil_div(N, kTileRows), ceil_div(K, kSliceCols), batch, &a.rows_per_group, &a.slices_per_group);
-    return run_gemv(a, !accumulate, as_stream(stream));
+    uint32_t* ws = nullptr;
+    if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
+    StepArgs a = make_step(N, x, x_dtype, K, batch, y, accumulate, ws);
+    a.nseg = 1;
+    a.seg[0] = make_segment(packed, alpha_r, alpha_c, nullptr, nb, K);
+    choose_geometry(ceil_div(N, kTileRows), ceil_div(K, kSliceCols), batch, &a.rows_per_group,
+                    &a.seg[0].slices_per_group);
+    return hip_status(launch_step(a, as_stream(stream)));
 }
 
 int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_s, const float* alpha_r_s,
                           const float* alpha_c_s, int ns, int64_t N, int64_t K, int g, const void* x,
                           int x_dtype, int batch, float* y, void* workspace, size_t ws_bytes, void* stream) {
-    (void)workspace;
-    (void)ws_bytes;
     if (!idx) return UBW_EINVAL;
     int st = validate_gemv_common(packed_s, alpha_r_s, alpha_c_s, ns, N, s, x, x_dtype, batch, y);
     if (st != UBW_OK) return st;
     if (!fits_int(K)) return UBW_EINVAL;
     if (g != 8) return UBW_EUNSUPPORTED;
-    GemvArgs a{};
-    a.packed = packed_s;
-    a.alpha_r = alpha_r_s;
-    a.alpha_c = alpha_c_s;
-    a.nb = ns;
-    a.N = (int)N;
-    a.Kv = (int)s;
-    a.x = x;
-    a.x_dtype = x_dtype;
-    a.ldx = K;
-    a.idx = idx;
-    a.batch = batch;
-    a.y = y;
-    a.accumulate = 1;
-    choose_geometry(ceil_div(N, kTileRows), ceil_div(s, kSliceCols), batch, &a.rows_per_group, &a.slices_per_group);
-    return run_gemv(a, false, as_stream(stream));
+    uint32_t* ws = nullptr;
+    if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
+    StepArgs a = make_step(N, x, x_dtype, K, batch, y, 1, ws);
+    a.nseg = 1;
+    a.seg[0] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
+    choose_geometry(ceil_div(N, kTileRows), ceil_div(s, kSliceCols), batch, &a.rows_per_group,
+                    &a.seg[0].slices_per_group);
+    return hip_status(launch_step(a, as_stream(stream)));
+}
+
+int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb,
+                         const int32_t* idx, int64_t s, const uint32_t* packed_s, const float* alpha_r_s,
+                         const float* alpha_c_s, int ns, int64_t N, int64_t K, int g, const void* x, int x_dtype,
+                         int batch, float* y, int accumulate, void* workspace, size_t ws_bytes, void* stream) {
+    int st = validate_gemv_common(packed, alpha_r, alpha_c, nb, N, K, x, x_dtype, batch, y);
+    if (st != UBW_OK) return st;
+    if (!idx) return UBW_EINVAL;
+    if ((st = validate_gemv_common(packed_s, alpha_r_s, alpha_c_s, ns, N, s, x, x_dtype, batch, y)) != UBW_OK)
+        return st;
+    if (g != 8) return UBW_EUNSUPPORTED;
+    uint32_t* ws = nullptr;
+    if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
+    StepArgs a = make_step(N, x, x_dtype, K, batch, y, accumulate, ws);
+    a.nseg = 2;
+    a.seg[0] = make_segment(packed, alpha_r, alpha_c, nullptr, nb, K);
+    a.seg[1] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
+    choose_geometry(ceil_div(N, kTileRows), ceil_div(K, kSliceCols), batch, &a.rows_per_group,
+                    &a.seg[0].slices_per_group);
+    // the refinement's few slices each get their own workgroup
+    return hip_status(launch_step(a, as_stream(stream)));
 }
 
 int ubw_check_indices(const int32_t* idx_host, int64_t s, int64_t K) {
@@ -200,30 +230,21 @@ int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, i
 int ubw_lut_gemv_geometry(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb, int64_t N,
                           int64_t Kv, const int32_t* idx, int64_t K, const void* x, int x_dtype, int batch,
                           float* y, int accumulate, int vcm, int rows_per_group, int slices_per_group,
-                          void* stream) {
+                          void* workspace, size_t ws_bytes, void* stream) {
     int st = validate_gemv_common(packed, alpha_r, alpha_c, nb, N, Kv, x, x_dtype, batch, y);
     if (st != UBW_OK) return st;
-    if (rows_per_group != 1 && rows_per_group != 2 && rows_per_group != 4) return UBW_ERANGE;
+    if (rows_per_group != 1 && rows_per_group != 2) return UBW_ERANGE;
     if (rows_per_group > max_rows_per_group(batch)) return UBW_ERANGE;
     if (slices_per_group < 1) return UBW_ERANGE;
-    if (vcm && (!idx || !accumulate || !fits_int(K))) return UBW_EINVAL;
-    GemvArgs a{};
-    a.packed = packed;
-    a.alpha_r = alpha_r;
-    a.alpha_c = alpha_c;
-    a.nb = nb;
-    a.N = (int)N;
-    a.Kv = (int)Kv;
-    a.x = x;
-    a.x_dtype = x_dtype;
-    a.ldx = vcm ? K : Kv;
-    a.idx = vcm ? idx : nullptr;
-    a.batch = batch;
-    a.y = y;
-    a.accumulate = accumulate ? 1 : 0;
+    if (vcm && (!idx || !fits_int(K))) return UBW_EINVAL;
+    uint32_t* ws = nullptr;
+    if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
+    StepArgs a = make_step(N, x, x_dtype, vcm ? K : Kv, batch, y, accumulate, ws);
+    a.nseg = 1;
+    a.seg[0] = make_segment(packed, alpha_r, alpha_c, vcm ? idx : nullptr, nb, Kv);
+    a.seg[0].slices_per_group = slices_per_group;
     a.rows_per_group = rows_per_group;
-    a.slices_per_group = slices_per_group;
-    return run_gemv(a, !accumulate, as_stream(stream));
+    return hip_status(launch_step(a, as_stream(stream)));
 }
 
 int ubw_bench_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream) {

@@ -30,23 +30,40 @@ constexpr int kThreads = 256;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-struct GemvArgs {
+// One matrix of a GEMV step: the main bases over all K columns, or the salient refinement
+// bases over the s virtual columns that idx maps onto activation columns.
+struct Segment {
     const uint32_t* packed;
     const float* alpha_r;   // [nb][N]
     const float* alpha_c;   // [nb][Kv]
+    const int32_t* idx;     // [Kv] virtual column -> activation column, or nullptr (identity)
     int nb;
+    int Kv;                 // columns of this matrix: K, or s
+    int slices_per_group;   // 256-column slices per workgroup (>= 1)
+};
+
+// One launch: up to two segments accumulated into the same y.
+struct StepArgs {
+    Segment seg[2];
+    int nseg;               // 1 or 2
     int N;
-    int Kv;                 // columns of the (virtual) matrix: K, or s for the refinement
     const void* x;          // [batch][ldx]
     int x_dtype;            // UBW_F32 / UBW_F16
     int64_t ldx;            // activation row length K
-    const int32_t* idx;     // salient columns (refinement only), else nullptr
     int batch;
     float* y;               // [batch][N]
     int accumulate;         // 0: y = result, 1: y += result
-    int rows_per_group;     // 1, 2, 4 row tiles per workgroup
-    int slices_per_group;   // >= 1 column slices per workgroup
+    uint32_t* ws;           // zero-initialised counters (single-launch y = result), or nullptr
+    int rows_per_group;     // 1 or 2 row tiles per workgroup (<= max_rows_per_group(batch))
 };
+
+// Workspace of the single-launch y = result mode: a 16-word header (word 0: error flag), then
+// 64 words (256 bytes) per 256-row group: the arrival counter at word 0 and the zeroer's flag
+// at word 32, on separate cache lines.
+constexpr int kWsHeaderWords = 16;
+constexpr int kWsRowGroupWords = 64;
+constexpr int kWsFlagOffset = 32;
+inline int64_t step_workspace_words(int64_t N) { return kWsHeaderWords + kWsRowGroupWords * ceil_div(N, kTileRows); }
 
 hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t s);
 hipError_t launch_pack(const void* src, int src_fmt, int nb, int N, int K, uint32_t* dst, hipStream_t s);
@@ -55,9 +72,9 @@ hipError_t launch_ternary(const int8_t* w, const float* scale, int N, int K, uin
 hipError_t launch_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, int nb, int K,
                             int g, float* lut, hipStream_t s);
 hipError_t launch_extract(const uint32_t* packed, int nb, int N, int K, int g, uint16_t* out, hipStream_t s);
-hipError_t launch_gemv8(const GemvArgs& a, hipStream_t s);
+hipError_t launch_step(const StepArgs& a, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
-// Largest rows_per_group the GEMV instances support for this batch (1, 2 or 4).
+// Largest rows_per_group the GEMV instances support for this batch (1 or 2).
 int max_rows_per_group(int batch);
 
 }  // namespace ubw
