@@ -119,12 +119,12 @@ int ubw_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, i
 /*
  * Workspace bytes the GEMV calls use for this shape (64 + 256 * ceil(N / 256)). *out is a
  * host pointer.
- * A workspace lets a call that overwrites y (accumulate = 0) run as ONE launch when the whole
- * grid fits on the device at once: the column slices of a row are combined with fp32 atomics,
- * the workgroup of each 256-row group's first column slices zeroes those rows and raises a
- * flag in the workspace, and the group's other workgroups read the flag before adding.
- * Without a workspace (NULL, 0 bytes), or for grids larger than the device holds at once, the
- * library zero-fills y with a separate launch first. Rules: zero-fill the workspace once after allocating it (the kernels leave it
+ * A workspace lets a call that overwrites y (accumulate = 0) run as ONE launch: the kernel's
+ * persistent workgroups (never more than the device holds at once) combine partial sums with
+ * fp32 atomics; at its start each workgroup zeroes the rows of the row groups it owns and
+ * raises their flags in the workspace, and a workgroup reads a row group's flag before adding
+ * into it. Without a workspace (NULL, 0 bytes) the library zero-fills y with a separate
+ * launch first. Rules: zero-fill the workspace once after allocating it (the kernels leave it
  * consistent after every call, whatever the shape); a workspace serves calls on one stream at a
  * time (calls that may run concurrently need separate workspaces); word 0 becomes nonzero only
  * if a wait gave up (an internal error that should never occur).
@@ -196,16 +196,18 @@ int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, i
 
 /*
  * Test and tuning export: ubw_lut_gemv (vcm = 0) or ubw_vcm_gather_refine (vcm = 1) with an
- * explicit launch geometry. rows_per_group in {1, 2} row tiles of 256 rows per workgroup;
- * slices_per_group >= 1 column slices of 256 columns per workgroup. Results
- * equal the default geometry's up to fp32 summation order. For vcm = 0, idx is ignored and
- * Kv = K; for vcm = 1, Kv = s. rows_per_group must be 1 for batch above 2 (UBW_ERANGE
- * otherwise). workspace as ubw_lut_gemv.
+ * explicit launch geometry. The kernel walks a list of units (a unit: rows_per_group tiles of
+ * 256 rows x two (256-column slice, base) items) split into equal contiguous ranges over
+ * `workgroups` persistent workgroups (0 = as many as the device holds at once; larger values
+ * are capped to that). rows_per_group is 1, 2 or 4 for batch 1, at most 2 for batch 2 and 1
+ * above (UBW_ERANGE otherwise). Results equal the default geometry's up to fp32 summation
+ * order. For vcm = 0, idx is ignored and Kv = K; for vcm = 1, Kv = s. workspace as
+ * ubw_lut_gemv.
  */
 int ubw_lut_gemv_geometry(const uint32_t* packed, const float* alpha_r, const float* alpha_c,
                           int nb, int64_t N, int64_t Kv, const int32_t* idx, int64_t K,
                           const void* x, int x_dtype, int batch, float* y, int accumulate,
-                          int vcm, int rows_per_group, int slices_per_group, void* workspace,
+                          int vcm, int rows_per_group, int workgroups, void* workspace,
                           size_t ws_bytes, void* stream);
 
 /*

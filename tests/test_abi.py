@@ -97,9 +97,12 @@ def test_geometry_rejects():
     L = ubw.lib()
     base = [FAKE, FAKE, FAKE, 2, 64, 64, None, 64, FAKE, 1, 1, FAKE, 0, 0]
     tail = [None, 0, None]
-    assert L.ubw_lut_gemv_geometry(*base, 3, 1, *tail) == ERANGE      # rows_per_group not in {1,2}
-    assert L.ubw_lut_gemv_geometry(*base, 4, 1, *tail) == ERANGE
-    assert L.ubw_lut_gemv_geometry(*base, 1, 0, *tail) == ERANGE      # slices_per_group < 1
+    assert L.ubw_lut_gemv_geometry(*base, 3, 1, *tail) == ERANGE      # rows_per_group not in {1,2,4}
+    assert L.ubw_lut_gemv_geometry(*base, 8, 1, *tail) == ERANGE
+    assert L.ubw_lut_gemv_geometry(*base, 1, -1, *tail) == ERANGE     # workgroups < 0
+    b2 = list(base)
+    b2[10] = 2                                                        # batch 2 allows up to 2 row tiles
+    assert L.ubw_lut_gemv_geometry(*b2, 4, 1, *tail) == ERANGE
     b4 = list(base)
     b4[10] = 4                                                        # batch 4 allows only 1 row tile
     assert L.ubw_lut_gemv_geometry(*b4, 2, 1, *tail) == ERANGE

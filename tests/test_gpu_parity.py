@@ -168,19 +168,28 @@ def test_gemv_integer_exact(n, k, nb, batch):
         assert np.array_equal(gpu_gemv(g, mode=mode), oracle_gemv(g)), mode
 
 
-@pytest.mark.parametrize("rpg", [1, 2])
-@pytest.mark.parametrize("spg", [1, 2, 3, 7])
-def test_gemv_geometries_integer_exact(rpg, spg):
-    """Every workgroup shape gives the same exact result (5 row tiles x 7 column slices, both
-    ragged at the edge)."""
-    rng = np.random.default_rng(rpg * 10 + spg)
+@pytest.mark.parametrize("rpg", [1, 2, 4])
+@pytest.mark.parametrize("wgs", [1, 2, 3, 5, 7, 0, 100000])
+def test_gemv_geometries_integer_exact(rpg, wgs):
+    """Every split of the unit list over workgroups gives the same exact result (5 row tiles x
+    7 column slices, both ragged; 1, 2, 3 bases), overwriting NaN garbage or accumulating."""
+    rng = np.random.default_rng(rpg * 10 + wgs % 97)
     n, k = 4 * 256 + 100, 6 * 256 + 77
-    g = make_integer_gemv(rng, n, k, 2, batch=1)
-    for ws in (None, ubw.workspace(n, DEV)):
-        y = torch.full((1, n), float("nan"), device=DEV)
-        ubw.lut_gemv_geometry(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y,
-                              rows_per_group=rpg, slices_per_group=spg, workspace=ws)
-        assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g))
+    for nb in (1, 2, 3):
+        g = make_integer_gemv(rng, n, k, nb, batch=1)
+        packed = pack(g.bits, k)
+        for ws in (None, ubw.workspace(n, DEV)):
+            y = torch.full((1, n), float("nan"), device=DEV)
+            ubw.lut_gemv_geometry(packed, dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y,
+                                  rows_per_group=rpg, workgroups=wgs, workspace=ws)
+            assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g)), (nb, ws is None)
+            if ws is not None:
+                assert host(ws)[0] == 0
+        y0 = rng.integers(-50, 50, (1, n)).astype(np.float32)
+        y = dev(y0)
+        ubw.lut_gemv_geometry(packed, dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y, accumulate=True,
+                              rows_per_group=rpg, workgroups=wgs)
+        assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g) + y0)
 
 
 @pytest.mark.parametrize("batch", [2, 4, 8, 16])
@@ -191,10 +200,11 @@ def test_gemv_geometries_batched(batch):
     for rpg in (1, 2):
         if rpg > 1 and batch > 2:
             continue
-        y = torch.zeros((batch, n), device=DEV)
-        ubw.lut_gemv_geometry(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y,
-                              rows_per_group=rpg, slices_per_group=2)
-        assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g))
+        for wgs in (1, 4, 0):
+            y = torch.zeros((batch, n), device=DEV)
+            ubw.lut_gemv_geometry(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y,
+                                  rows_per_group=rpg, workgroups=wgs, workspace=ubw.workspace(n, DEV))
+            assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g))
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -272,14 +282,14 @@ def test_vcm_geometries_integer_exact():
     g = make_integer_gemv(rng, n, k, 1, s=s, ns=2, batch=2)
     ps = pack(g.bits_s, s)
     want = oracle_gemv(g) - oracle_gemv(g, refine=False)
-    for rpg, spg in ((1, 1), (2, 2), (1, 3)):
+    for rpg, wgs in ((1, 0), (2, 3), (1, 1), (2, 0)):
         y = torch.zeros((2, n), device=DEV)
         ubw.lut_gemv_geometry(ps, dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), n, s, y, idx=dev(g.idx), k=k,
-                              accumulate=True, rows_per_group=rpg, slices_per_group=spg)
+                              accumulate=True, rows_per_group=rpg, workgroups=wgs)
         assert np.array_equal(host(y).astype(np.float64), want)
         y = torch.full((2, n), float("nan"), device=DEV)
         ubw.lut_gemv_geometry(ps, dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), n, s, y, idx=dev(g.idx), k=k,
-                              accumulate=False, rows_per_group=rpg, slices_per_group=spg,
+                              accumulate=False, rows_per_group=rpg, workgroups=wgs,
                               workspace=ubw.workspace(n, DEV))
         assert np.array_equal(host(y).astype(np.float64), want)
 

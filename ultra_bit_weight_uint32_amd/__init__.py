@@ -305,7 +305,7 @@ def extract_patterns(packed, nb: int, n: int, k: int, g: int = 8):
 
 
 def lut_gemv_geometry(packed, alpha_r, alpha_c, x, n: int, kv: int, y, *, idx=None, k=None, accumulate=False,
-                      rows_per_group=1, slices_per_group=1, workspace=None):
+                      rows_per_group=1, workgroups=0, workspace=None):
     """Main (idx None) or refinement (idx given, k = x's row length) GEMV with an explicit
     launch geometry; for tests and tuning."""
     torch = _torch()
@@ -318,7 +318,7 @@ def lut_gemv_geometry(packed, alpha_r, alpha_c, x, n: int, kv: int, y, *, idx=No
                                        _dev(alpha_c, "alpha_c", (torch.float32,)), nb, n, kv,
                                        _dev(idx, "idx", (torch.int32,)) if vcm else None, k if vcm else kv,
                                        _dev(x, "x", None), _xdtype(x), batch, _dev(y, "y", (torch.float32,)),
-                                       1 if accumulate else 0, 1 if vcm else 0, rows_per_group, slices_per_group,
+                                       1 if accumulate else 0, 1 if vcm else 0, rows_per_group, workgroups,
                                        *_ws(workspace), _stream()))
     return y
 

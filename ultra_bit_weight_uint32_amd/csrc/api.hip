@@ -22,28 +22,18 @@ int64_t packed_words_of(int nb, int64_t N, int64_t K) {
     return (int64_t)nb * ceil_div(N, kTileRows) * ceil_div(K, kSliceCols) * kTileWords;
 }
 
-// Launch geometry: row tiles and column slices per workgroup. A workgroup needs 64 KiB of
-// tables plus its activation buffer, so two fit on a CU. Prefer at least 512 workgroups
-// (two per CU on 256 CUs) when the matrix is large enough; beyond that, give each workgroup
-// more row tiles (tables are built once per slice and activation row, so more rows per
-// workgroup means fewer table entries per lookup), then more slices (fewer partial sums
-// combined by atomics).
-void choose_geometry(int64_t NT, int64_t KT, int batch, int* rpl, int* spg) {
-    const int64_t target = 512;
-    *rpl = 1;
-    *spg = 1;
-    if (NT * KT <= target) return;
-    for (int r : {2}) {
-        if (r <= max_rows_per_group(batch) && ceil_div(NT, r) * KT >= target) {
-            *rpl = r;
-            break;
-        }
+// Rows per unit: the largest of 4, 2, 1 row tiles (within what the batch allows) that still
+// leaves at least two units per CU on a 256-CU device. Tables are built once per unit and
+// activation row, so more rows per unit means fewer table entries per lookup; enough units
+// keep every workgroup's prefetch pipeline busy.
+int choose_rows(int64_t NT, int64_t units_per_tile_row_group, int batch) {
+    for (int r : {4, 2}) {
+        if (r <= max_rows_per_group(batch) && ceil_div(NT, r) * units_per_tile_row_group >= 512) return r;
     }
-    for (int64_t s2 = 2; s2 <= KT; ++s2) {
-        if (ceil_div(NT, *rpl) * ceil_div(KT, s2) >= target) *spg = (int)s2;
-        else break;
-    }
+    return 1;
 }
+
+int64_t units_of(int64_t Kv, int nb) { return ceil_div(ceil_div(Kv, kSliceCols) * nb, 2); }
 
 int validate_gemv_common(const void* packed, const float* ar, const float* ac, int nb, int64_t N, int64_t Kv,
                          const void* x, int x_dtype, int batch, const float* y) {
@@ -75,7 +65,6 @@ Segment make_segment(const uint32_t* packed, const float* ar, const float* ac, c
     g.idx = idx;
     g.nb = nb;
     g.Kv = (int)Kv;
-    g.slices_per_group = 1;
     return g;
 }
 
@@ -91,6 +80,7 @@ StepArgs make_step(int64_t N, const void* x, int x_dtype, int64_t K, int batch, 
     a.accumulate = accumulate ? 1 : 0;
     a.ws = ws;
     a.rows_per_group = 1;
+    a.workgroups = 0;
     return a;
 }
 
@@ -165,8 +155,7 @@ int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alph
     StepArgs a = make_step(N, x, x_dtype, K, batch, y, accumulate, ws);
     a.nseg = 1;
     a.seg[0] = make_segment(packed, alpha_r, alpha_c, nullptr, nb, K);
-    choose_geometry(ceil_div(N, kTileRows), ceil_div(K, kSliceCols), batch, &a.rows_per_group,
-                    &a.seg[0].slices_per_group);
+    a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(K, nb), batch);
     return hip_status(launch_step(a, as_stream(stream)));
 }
 
@@ -183,8 +172,7 @@ int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_
     StepArgs a = make_step(N, x, x_dtype, K, batch, y, 1, ws);
     a.nseg = 1;
     a.seg[0] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
-    choose_geometry(ceil_div(N, kTileRows), ceil_div(s, kSliceCols), batch, &a.rows_per_group,
-                    &a.seg[0].slices_per_group);
+    a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(s, ns), batch);
     return hip_status(launch_step(a, as_stream(stream)));
 }
 
@@ -204,9 +192,7 @@ int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const flo
     a.nseg = 2;
     a.seg[0] = make_segment(packed, alpha_r, alpha_c, nullptr, nb, K);
     a.seg[1] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
-    choose_geometry(ceil_div(N, kTileRows), ceil_div(K, kSliceCols), batch, &a.rows_per_group,
-                    &a.seg[0].slices_per_group);
-    // the refinement's few slices each get their own workgroup
+    a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(K, nb) + units_of(s, ns), batch);
     return hip_status(launch_step(a, as_stream(stream)));
 }
 
@@ -229,21 +215,21 @@ int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, i
 
 int ubw_lut_gemv_geometry(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb, int64_t N,
                           int64_t Kv, const int32_t* idx, int64_t K, const void* x, int x_dtype, int batch,
-                          float* y, int accumulate, int vcm, int rows_per_group, int slices_per_group,
+                          float* y, int accumulate, int vcm, int rows_per_group, int workgroups,
                           void* workspace, size_t ws_bytes, void* stream) {
     int st = validate_gemv_common(packed, alpha_r, alpha_c, nb, N, Kv, x, x_dtype, batch, y);
     if (st != UBW_OK) return st;
-    if (rows_per_group != 1 && rows_per_group != 2) return UBW_ERANGE;
+    if (rows_per_group != 1 && rows_per_group != 2 && rows_per_group != 4) return UBW_ERANGE;
     if (rows_per_group > max_rows_per_group(batch)) return UBW_ERANGE;
-    if (slices_per_group < 1) return UBW_ERANGE;
+    if (workgroups < 0) return UBW_ERANGE;
     if (vcm && (!idx || !fits_int(K))) return UBW_EINVAL;
     uint32_t* ws = nullptr;
     if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
     StepArgs a = make_step(N, x, x_dtype, vcm ? K : Kv, batch, y, accumulate, ws);
     a.nseg = 1;
     a.seg[0] = make_segment(packed, alpha_r, alpha_c, vcm ? idx : nullptr, nb, Kv);
-    a.seg[0].slices_per_group = slices_per_group;
     a.rows_per_group = rows_per_group;
+    a.workgroups = workgroups;
     return hip_status(launch_step(a, as_stream(stream)));
 }
 

@@ -320,28 +320,42 @@ __global__ void k_extract4(const uint32_t* __restrict__ packed, int nb, int N, i
 }
 
 // ---------------------------------------------------------------------------------------
-// The GEMV step (g = 8).
+// The GEMV step (g = 8): a persistent, stream-K style kernel.
 //
-// Grid: C workgroups of 512 threads per row group (RPL tiles of 256 rows), one per
-// (segment, group of column slices); C = sum over segments of ceil(KT / slices_per_group).
-// A workgroup's work is a list of items (slice, base) of its slices; a unit is two
-// consecutive items, one per half of every wave: lane l of half h in wave w owns tile row
-// 32 w + l for item h. Per unit and activation row b: stage v = alpha_c * x for both items,
-// build each item's 32 tables (half h writes LDS columns 32 h .. 32 h + 31), barrier, look
-// up every owned row, accumulate alpha_r * sum, barrier. The two halves of a row (different
-// items) are added with a cross-lane swap at the end. Weights, scales and activations of
-// the next units are in flight while a unit is processed (three register slots).
+// Work list: for each row group rg (RPL tiles of 256 rows), the units of each segment in
+// order. A segment's items are (slice, base) pairs, slice-major; a unit is two consecutive
+// items, one per half of every wave: lane l of half h in wave w owns tile row 32 w + l for
+// item h. The list holds U = NRG * Urg units; workgroup g of G takes units
+// [g U / G, (g + 1) U / G), keeps per-row partial sums across consecutive units of one row
+// group and adds them into y with fp32 atomics when its range leaves that row group.
+// Per unit and activation row b: stage v = alpha_c * x for both items, build each item's 32
+// tables (half h writes LDS columns 32 h .. 32 h + 31), barrier, look up every owned row,
+// accumulate alpha_r * sum, barrier. The two halves of a row (different items) are added with
+// a cross-lane swap when flushing. The weights, scales and activations of the next units are
+// in flight while a unit is processed (three register slots, reloaded in place).
+//
+// y = result in one launch (kModeFirst): at its start workgroup g zeroes the rows of every
+// row group rg with rg mod G == g and raises that row group's flag; a workgroup reads the flag
+// of a row group before adding into it. Zeroing depends on nothing and the grid never exceeds
+// what the device holds at once, so every wait ends. Per row group, 256 bytes of workspace:
+// word 0 = (generation << 12) | arrivals, word 32 = flag.
 
 enum { kModeStore = 0, kModeAdd = 1, kModeAtomic = 2, kModeFirst = 3 };
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kStepThreads = 512;
+constexpr uint32_t kArrBits = 12;
+constexpr uint32_t kArrMask = (1u << kArrBits) - 1u;
+constexpr uint32_t kGenMask = (1u << (32 - kArrBits)) - 1u;
 
 struct StepParams {
     StepArgs a;
     int NT;
-    int C;            // workgroups per row group
+    int NRG;          // row groups
     int KT[2];        // slices per segment
-    int nkg[2];       // slice groups per segment
+    int US[2];        // units per row group per segment
+    int Urg;          // units per row group
+    int U;            // units in the whole list (U * G < 2^32, checked on the host)
+    int G;            // workgroups
     int mode;
 };
 
@@ -353,49 +367,80 @@ struct Unit {
     XT xv[BMAX];       // staging: activations at the staged column
 };
 
-// Item `it` (slice ks0 + it / nb, base it % nb) of the workgroup's list, or none.
-struct Item {
-    int ks, k;
-    bool valid;
+// Where unit x of the list lives.
+struct UnitPos {
+    int rg;     // row group
+    int si;     // segment
+    int pair;   // unit within the segment's units of this row group
 };
 
-__device__ __forceinline__ Item item_of(int it, int nitems, int ks0, int nb) {
-    Item r;
-    r.valid = it < nitems;
-    const int q = r.valid ? it : 0;
-    r.ks = ks0 + q / nb;
-    r.k = q - (q / nb) * nb;
+// (row group, unit within the row group) of a cursor walking the list.
+struct Cursor {
+    int rg, q;
+};
+
+__device__ __forceinline__ void advance(Cursor& cu, int Urg) {
+    if (++cu.q == Urg) {
+        cu.q = 0;
+        ++cu.rg;
+    }
+}
+
+__device__ __forceinline__ UnitPos unit_pos(const StepParams& P, Cursor cu) {
+    UnitPos r;
+    r.rg = cu.rg;
+    r.si = cu.q < P.US[0] ? 0 : 1;
+    r.pair = r.si ? cu.q - P.US[0] : cu.q;
     return r;
 }
 
 template <typename XT, int RPL, int BMAX>
-__device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX>& U, const Segment& sg, const StepArgs& a, int KT,
-                                          int NT, int u, int nitems, int ks0, int rt0, int h, int rho, int tid) {
-    // staging role: thread tid stages column (tid mod 256) of item 2u + tid / 256
-    const Item st = item_of(2 * u + (tid >> 8), nitems, ks0, sg.nb);
-    const int col = st.ks * kSliceCols + (tid & 255);
-    const bool cvalid = st.valid && col < sg.Kv;
+__device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX>& U, const StepParams& P, Cursor cu, int h, int rho,
+                                          int tid) {
+    const StepArgs& a = P.a;
+    const UnitPos up = unit_pos(P, cu);
+    const Segment& sg = a.seg[up.si];
+    const int KT = P.KT[up.si];
+    const int nitems = KT * sg.nb;
+    const int rt0 = up.rg * RPL;
+    // staging role: thread tid stages column (tid mod 256) of item 2 pair + tid / 256
+    const int its = 2 * up.pair + (tid >> 8);
+    const bool sval = its < nitems;
+    const int sks = sval ? its / sg.nb : 0, sk = sval ? its - sks * sg.nb : 0;
+    const int col = sks * kSliceCols + (tid & 255);
+    const bool cvalid = sval && col < sg.Kv;
     int xcol = col;
     if (sg.idx) xcol = cvalid ? sg.idx[col] : 0;  // requested first: the gather below waits on it
-    // lookup role: item 2u + h for tile row rho
-    const Item lk = item_of(2 * u + h, nitems, ks0, sg.nb);
+    // lookup role: item 2 pair + h for tile row rho
+    const int itl = 2 * up.pair + h;
+    const bool lval = itl < nitems;
+    const int lks = lval ? itl / sg.nb : 0, lk = lval ? itl - lks * sg.nb : 0;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
         const int rt = rt0 + j;
         U.w[j][0] = U.w[j][1] = make_uint4(0, 0, 0, 0);
-        if (lk.valid && rt < NT) {
+        if (lval && rt < P.NT) {
             const uint4* tp =
-                reinterpret_cast<const uint4*>(sg.packed + ((int64_t)(rt * KT + lk.ks) * sg.nb + lk.k) * kTileWords);
+                reinterpret_cast<const uint4*>(sg.packed + ((int64_t)(rt * KT + lks) * sg.nb + lk) * kTileWords);
             U.w[j][0] = tp[rho];
             U.w[j][1] = tp[kTileRows + rho];
         }
         const int row = rt * kTileRows + rho;
-        U.ar[j] = (lk.valid && rt < NT && row < a.N) ? sg.alpha_r[(int64_t)lk.k * a.N + row] : 0.f;
+        U.ar[j] = (lval && rt < P.NT && row < a.N) ? sg.alpha_r[(int64_t)lk * a.N + row] : 0.f;
     }
-    U.ac = cvalid ? sg.alpha_c[(int64_t)st.k * sg.Kv + col] : 0.f;
+    U.ac = cvalid ? sg.alpha_c[(int64_t)sk * sg.Kv + col] : 0.f;
     const XT* xp = reinterpret_cast<const XT*>(a.x);
 #pragma unroll
     for (int b = 0; b < BMAX; ++b) U.xv[b] = (b < a.batch && cvalid) ? xp[(int64_t)b * a.ldx + xcol] : XT(0.f);
+}
+
+// First unit of workgroup g's range, and the workgroup whose range holds unit x (the largest g
+// with start(g) <= x). 32-bit: the host guarantees U * G < 2^32.
+__device__ __forceinline__ uint32_t range_start(const StepParams& P, uint32_t g) {
+    return g * (uint32_t)P.U / (uint32_t)P.G;
+}
+__device__ __forceinline__ int owner_of(const StepParams& P, uint32_t x) {
+    return (int)(((x + 1) * (uint32_t)P.G - 1) / (uint32_t)P.U);
 }
 
 template <typename XT, int RPL, int BMAX>
@@ -423,67 +468,110 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
 #pragma unroll
     for (int i = 0; i < 8; ++i) lc[i] += 0x80808080u * (uint32_t)h;  // half h's tables: +128 bytes
 
-    const int rg = blockIdx.x / P.C;
-    const int kslot = blockIdx.x - rg * P.C;
-    const int si = kslot < P.nkg[0] ? 0 : 1;
-    const int kg = si ? kslot - P.nkg[0] : kslot;
-    const Segment sg = a.seg[si];
-    const int KT = P.KT[si];
-    const int rt0 = rg * RPL;
-    const int ks0 = kg * sg.slices_per_group;
-    const int ks1 = min(ks0 + sg.slices_per_group, KT);
-    const int nitems = (ks1 - ks0) * sg.nb;
-    const int nunits = (nitems + 1) >> 1;
+    const int g = blockIdx.x;
+    const int x0 = (int)range_start(P, g);
+    const int x1 = (int)range_start(P, g + 1);
+    Cursor lcur{x0 / P.Urg, x0 % P.Urg};  // next unit to load
+    Cursor pcur = lcur;                     // next unit to process
 
     // The first units' weights, scales and activations are requested before anything waits.
-    Unit<XT, RPL, BMAX> cur, n1, n2;
-    if (nunits > 0) load_unit(cur, sg, a, KT, P.NT, 0, nitems, ks0, rt0, h, rho, tid);
-    if (nunits > 1) load_unit(n1, sg, a, KT, P.NT, 1, nitems, ks0, rt0, h, rho, tid);
-    if (nunits > 2) load_unit(n2, sg, a, KT, P.NT, 2, nitems, ks0, rt0, h, rho, tid);
+    Unit<XT, RPL, BMAX> s0, s1, s2;
+    if (x0 < x1) { load_unit(s0, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
+    if (x0 + 1 < x1) { load_unit(s1, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
+    if (x0 + 2 < x1) { load_unit(s2, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
 
-    // y = result with several contributors per row (kModeFirst): the row group's workgroup for
-    // the first column-slice group (kslot 0) zeroes the rows and raises the row group's flag;
-    // every other contributor reads the flag before its atomics. The arrival counter only
-    // supplies the call's generation, so nobody waits on it early. Per row group, 256 bytes
-    // of workspace: word 0 = (generation << 8) | arrivals, word 32 = flag (separate lines).
-    const bool zeroer = P.mode == kModeFirst && kslot == 0;
-    uint32_t* cnt = a.ws + kWsHeaderWords + kWsRowGroupWords * rg;
-    uint32_t* flag = cnt + kWsFlagOffset;
-    uint32_t arrived = 0;  // thread 0: the counter's value before this workgroup's arrival
-    if (P.mode == kModeFirst && tid == 0) arrived = atomicAdd(cnt, 1u);
-    if (zeroer) {
-        float sink = 0.f;
-        if (tid < kTileRows) {
+    const bool first_mode = P.mode == kModeFirst;
+    if (first_mode) {
+        // zero the rows of the row groups this workgroup owns and raise their flags
+        for (int rg = g; rg < P.NRG; rg += P.G) {
+            uint32_t* cnt = a.ws + kWsHeaderWords + kWsRowGroupWords * rg;
+            float sink = 0.f;
+            uint32_t gen = 0;
+            if (tid == 0) gen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> kArrBits;
+            if (tid < kTileRows) {
 #pragma unroll
-            for (int j = 0; j < RPL; ++j) {
-                const int row = (rt0 + j) * kTileRows + tid;
-                if (rt0 + j >= P.NT || row >= a.N) continue;
-                for (int b = 0; b < a.batch; ++b)
-                    sink += __hip_atomic_exchange(a.y + (int64_t)b * a.N + row, 0.f, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
+                for (int j = 0; j < RPL; ++j) {
+                    const int rt = rg * RPL + j;
+                    const int row = rt * kTileRows + tid;
+                    if (rt >= P.NT || row >= a.N) continue;
+                    for (int b = 0; b < a.batch; ++b)
+                        sink += __hip_atomic_exchange(a.y + (int64_t)b * a.N + row, 0.f, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
+            // depend on every returned value (so each exchange has been performed before the
+            // barrier); the store itself is harmless scratch in an unused workspace word
+            if (sink == 1.5e38f) a.ws[1] = 1u;
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_exchange(cnt + kWsFlagOffset, (gen + 1) & kGenMask, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
         }
-        // depend on every returned value (so each exchange has been performed before the
-        // barrier); the store itself is harmless scratch in an unused workspace word
-        if (sink == 1.5e38f) a.ws[1] = 1u;
-        __syncthreads();
-        if (tid == 0)
-            __hip_atomic_exchange(flag, ((arrived >> 8) + 1) & 0xFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    uint32_t seen = 0;
 
     float acc[RPL][kAccLds ? 1 : BMAX];
+    auto clear_acc = [&]() {
 #pragma unroll
-    for (int j = 0; j < RPL; ++j)
+        for (int j = 0; j < RPL; ++j)
 #pragma unroll
-        for (int b = 0; b < (kAccLds ? 1 : BMAX); ++b) acc[j][b] = 0.f;
-    if (kAccLds) {
+            for (int b = 0; b < (kAccLds ? 1 : BMAX); ++b) acc[j][b] = 0.f;
+        if (kAccLds) {
 #pragma unroll
-        for (int i = 0; i < RPL * BMAX; ++i) sacc[i * kStepThreads + tid] = 0.f;  // own slots only
-    }
+            for (int i = 0; i < RPL * BMAX; ++i) sacc[i * kStepThreads + tid] = 0.f;  // own slots only
+        }
+    };
+    clear_acc();
 
-    // One activation row of one unit: build the tables, barrier, look up, accumulate, barrier.
-    auto row_pass = [&](const Unit<XT, RPL, BMAX>& U, int u, int b, bool mine, float S[RPL]) {
+    // Row-group bookkeeping (thread 0): arrival counter value and the flag as last read.
+    int cur_rg = -1;
+    uint32_t arrived = 0, seen = 0;
+
+    // Add this workgroup's partial sums of row group rg into y.
+    auto flush = [&](int rg) {
+        uint32_t* cnt = a.ws + kWsHeaderWords + kWsRowGroupWords * rg;
+        if (first_mode) {
+            if (tid == 0) {
+                const uint32_t want = ((arrived >> kArrBits) + 1) & kGenMask;
+                int n = 0;
+                while (seen != want) {
+                    __builtin_amdgcn_s_sleep(2);
+                    seen = __hip_atomic_load(cnt + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (++n > kSpinLimit) {  // cannot happen while the owner runs; never hang
+                        atomicOr(a.ws, 1u);
+                        break;
+                    }
+                }
+                // contributors of rg: the workgroups whose ranges meet rg's units
+                const int cg = owner_of(P, (uint32_t)(rg + 1) * P.Urg - 1) - owner_of(P, (uint32_t)rg * P.Urg) + 1;
+                if ((arrived & kArrMask) + 1 == (uint32_t)cg)  // last to arrive: arrivals 0, next generation
+                    atomicAdd(cnt, (1u << kArrBits) - (uint32_t)cg);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < RPL; ++j) {
+            const int rt = rg * RPL + j;
+            const int row = rt * kTileRows + rho;
+            const bool rv = rt < P.NT && row < a.N;
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) {
+                if (b >= a.batch) continue;
+                const float part = kAccLds ? sacc[(j * BMAX + b) * kStepThreads + tid] : acc[j][kAccLds ? 0 : b];
+                const uint32_t pv = __float_as_uint(part);
+                const auto sw = __builtin_amdgcn_permlane32_swap(pv, pv, false, false);
+                const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                if (h == 0 && rv) {
+                    float* dst = a.y + (int64_t)b * a.N + row;
+                    if (P.mode == kModeStore) *dst = total;
+                    else if (P.mode == kModeAdd) *dst += total;
+                    else atomicAdd(dst, total);
+                }
+            }
+        }
+    };
+
+    // One activation row of one unit: build the tables, barrier, look up.
+    auto row_pass = [&](const Unit<XT, RPL, BMAX>& U, bool mine, bool poll, int rg, int b, float S[RPL]) {
         if (mine) {
             float v[8];
 #pragma unroll
@@ -494,15 +582,26 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
             for (int pp = 0; pp < 32; ++pp) tab[(p0 + pp) * 64 + 32 * h + l] = lut8_entry(lo, hi0, hi1, pp);
         }
         __syncthreads();
-        // look at the zeroer's flag while the last lookups run; used after the loop
-        if (P.mode == kModeFirst && !zeroer && tid == 0 && u + 1 == nunits && b == 0)
-            seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // look at the row group's flag while the last lookups before a flush run
+        if (poll && tid == 0 && b == 0)
+            seen = __hip_atomic_load(a.ws + kWsHeaderWords + kWsRowGroupWords * rg + kWsFlagOffset, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int j = 0; j < RPL; ++j) S[j] = mine ? U.ar[j] * lookup_row(tb, U.w[j][0], U.w[j][1], lc, c) : 0.f;
     };
-    // One unit: stage v for both items, then every activation row.
-    auto process = [&](const Unit<XT, RPL, BMAX>& U, int u) {
-        const bool mine = 2 * u + h < nitems;  // this half has an item in this unit
+
+    // One unit of the list (the one at pcur, which it then advances).
+    auto process = [&](const Unit<XT, RPL, BMAX>& U, int x) {
+        const UnitPos up = unit_pos(P, pcur);
+        if (up.rg != cur_rg) {  // entering a row group: arrive on its counter
+            cur_rg = up.rg;
+            if (first_mode && tid == 0)
+                arrived = atomicAdd(a.ws + kWsHeaderWords + kWsRowGroupWords * up.rg, 1u);
+        }
+        const int nitems = P.KT[up.si] * a.seg[up.si].nb;
+        const bool mine = 2 * up.pair + h < nitems;  // this half has an item in this unit
+        const bool last_of_rg = x + 1 == x1 || pcur.q + 1 == P.Urg;
+        advance(pcur, P.Urg);
         // scaled activations of both items: v = alpha_c * x (LUT-BSF folds alpha_c here)
 #pragma unroll
         for (int b = 0; b < BMAX; ++b)
@@ -513,7 +612,7 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
             for (int b = 0; b < BMAX; ++b) {
                 if (b < a.batch) {
                     float S[RPL];
-                    row_pass(U, u, b, mine, S);
+                    row_pass(U, mine, first_mode && last_of_rg, up.rg, b, S);
 #pragma unroll
                     for (int j = 0; j < RPL; ++j) acc[j][kAccLds ? 0 : b] += S[j];
                     __syncthreads();
@@ -522,66 +621,30 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
         } else {
             for (int b = 0; b < a.batch; ++b) {
                 float S[RPL];
-                row_pass(U, u, b, mine, S);
+                row_pass(U, mine, first_mode && last_of_rg, up.rg, b, S);
 #pragma unroll
                 for (int j = 0; j < RPL; ++j) sacc[(j * BMAX + b) * kStepThreads + tid] += S[j];
                 __syncthreads();
             }
         }
+        if (last_of_rg) {
+            flush(up.rg);
+            clear_acc();
+        }
     };
+
     // Three register slots, each reloaded in place three units ahead (no copies between
     // slots, which would wait on loads still in flight).
-    for (int u = 0; u < nunits; u += 3) {
-        process(cur, u);
-        if (u + 3 < nunits) load_unit(cur, sg, a, KT, P.NT, u + 3, nitems, ks0, rt0, h, rho, tid);
-        if (u + 1 < nunits) {
-            process(n1, u + 1);
-            if (u + 4 < nunits) load_unit(n1, sg, a, KT, P.NT, u + 4, nitems, ks0, rt0, h, rho, tid);
+    for (int x = x0; x < x1; x += 3) {
+        process(s0, x);
+        if (x + 3 < x1) { load_unit(s0, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
+        if (x + 1 < x1) {
+            process(s1, x + 1);
+            if (x + 4 < x1) { load_unit(s1, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
         }
-        if (u + 2 < nunits) {
-            process(n2, u + 2);
-            if (u + 5 < nunits) load_unit(n2, sg, a, KT, P.NT, u + 5, nitems, ks0, rt0, h, rho, tid);
-        }
-    }
-
-    if (P.mode == kModeFirst && tid == 0 && (arrived & 0xFFu) + 1 == (uint32_t)P.C)
-        atomicAdd(cnt, 0x100u - (uint32_t)P.C);  // last to arrive: arrivals back to 0, next generation
-    if (P.mode == kModeFirst && !zeroer) {
-        if (tid == 0) {
-            const uint32_t want = ((arrived >> 8) + 1) & 0xFFFFFFu;
-            int n = 0;
-            while (seen != want) {
-                __builtin_amdgcn_s_sleep(2);
-                seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (++n > kSpinLimit) {  // cannot happen while the zeroer runs; never hang
-                    atomicOr(a.ws, 1u);
-                    break;
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    // The two halves of every row hold different items' sums: add them across lanes l, l + 32,
-    // then the first half writes.
-#pragma unroll
-    for (int j = 0; j < RPL; ++j) {
-        const int rt = rt0 + j;
-        const int row = rt * kTileRows + rho;
-        const bool rv = rt < P.NT && row < a.N;
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b) {
-            if (b >= a.batch) continue;
-            const float part = kAccLds ? sacc[(j * BMAX + b) * kStepThreads + tid] : acc[j][kAccLds ? 0 : b];
-            const uint32_t pv = __float_as_uint(part);
-            const auto sw = __builtin_amdgcn_permlane32_swap(pv, pv, false, false);
-            const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            if (h == 0 && rv) {
-                float* dst = a.y + (int64_t)b * a.N + row;
-                if (P.mode == kModeStore) *dst = total;
-                else if (P.mode == kModeAdd) *dst += total;
-                else atomicAdd(dst, total);
-            }
+        if (x + 2 < x1) {
+            process(s2, x + 2);
+            if (x + 5 < x1) { load_unit(s2, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
         }
     }
 }
@@ -680,70 +743,75 @@ static int64_t resident_capacity() {
     return cap;
 }
 
+static inline bool a_ws_missing(const StepParams& P) { return P.a.ws == nullptr; }
+
 template <typename XT, int RPL, int BMAX>
-static hipError_t launch_step_t(StepParams P, int n_rgroups, hipStream_t s) {
-    const int64_t grid = (int64_t)n_rgroups * P.C;
-    if (P.mode == kModeFirst && grid > resident_capacity<XT, RPL, BMAX>()) {
-        // Waiting on another workgroup is safe only when the whole grid is resident at once;
-        // otherwise zero y with a separate launch and let every workgroup add.
+static hipError_t launch_step_t(StepParams P, hipStream_t s) {
+    const int64_t cap = resident_capacity<XT, RPL, BMAX>();
+    if (cap <= 0) return hipErrorInvalidConfiguration;
+    // Never more workgroups than the device holds at once: the flag waits rely on it.
+    int64_t G = P.a.workgroups > 0 ? P.a.workgroups : cap;
+    G = G < cap ? G : cap;
+    G = G < P.U ? G : P.U;
+    P.G = (int)G;
+    if ((uint64_t)P.U * (uint64_t)P.G >= (1ull << 32)) return hipErrorInvalidValue;  // 32-bit range math
+    if (P.mode == kModeFirst && P.G == P.NRG) {
+        P.mode = kModeStore;  // every workgroup holds exactly one whole row group: plain stores
+    }
+    // the arrival field counts contributors of a row group: at most Urg + 1 workgroups
+    if (P.mode == kModeFirst && (a_ws_missing(P) || P.Urg + 1 > (int)kArrMask)) {
         hipError_t e = launch_fill_zero(P.a.y, (int64_t)P.a.batch * P.a.N, s);
         if (e != hipSuccess) return e;
         P.mode = kModeAtomic;
     }
-    hipLaunchKernelGGL((k_gemv8<XT, RPL, BMAX>), dim3((unsigned)grid), dim3(kStepThreads), 0, s, P);
+    if (P.mode == kModeAdd && P.G != P.NRG) P.mode = kModeAtomic;
+    hipLaunchKernelGGL((k_gemv8<XT, RPL, BMAX>), dim3((unsigned)P.G), dim3(kStepThreads), 0, s, P);
     return hipGetLastError();
 }
 
 // Instances: (row tiles per workgroup, batch bound) pairs whose registers fit without spills;
 // max_rows_per_group() is the host-side rule that keeps requests inside this set.
 template <typename XT>
-static hipError_t launch_step_x(const StepParams& P, int n_rgroups, int rpl, hipStream_t s) {
+static hipError_t launch_step_x(const StepParams& P, int rpl, hipStream_t s) {
     const int batch = P.a.batch;
     if (batch <= 1) {
-        if (rpl >= 2) return launch_step_t<XT, 2, 1>(P, n_rgroups, s);
-        return launch_step_t<XT, 1, 1>(P, n_rgroups, s);
+        if (rpl >= 4) return launch_step_t<XT, 4, 1>(P, s);
+        if (rpl >= 2) return launch_step_t<XT, 2, 1>(P, s);
+        return launch_step_t<XT, 1, 1>(P, s);
     }
     if (batch <= 2) {
-        if (rpl >= 2) return launch_step_t<XT, 2, 2>(P, n_rgroups, s);
-        return launch_step_t<XT, 1, 2>(P, n_rgroups, s);
+        if (rpl >= 2) return launch_step_t<XT, 2, 2>(P, s);
+        return launch_step_t<XT, 1, 2>(P, s);
     }
-    if (batch <= 4) return launch_step_t<XT, 1, 4>(P, n_rgroups, s);
-    if (batch <= 8) return launch_step_t<XT, 1, 8>(P, n_rgroups, s);
-    return launch_step_t<XT, 1, 16>(P, n_rgroups, s);
+    if (batch <= 4) return launch_step_t<XT, 1, 4>(P, s);
+    if (batch <= 8) return launch_step_t<XT, 1, 8>(P, s);
+    return launch_step_t<XT, 1, 16>(P, s);
 }
 
-int max_rows_per_group(int batch) { return batch <= 2 ? 2 : 1; }
+int max_rows_per_group(int batch) { return batch <= 1 ? 4 : (batch <= 2 ? 2 : 1); }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t s) {
     StepParams P{};
     P.a = a;
+    const int rpl = a.rows_per_group;
     P.NT = (int)ceil_div(a.N, kTileRows);
-    P.C = 0;
+    P.NRG = (int)ceil_div(P.NT, rpl);
+    P.Urg = 0;
     for (int i = 0; i < 2; ++i) {
         if (i < a.nseg) {
             P.KT[i] = (int)ceil_div(a.seg[i].Kv, kSliceCols);
-            P.nkg[i] = (int)ceil_div(P.KT[i], a.seg[i].slices_per_group);
+            P.US[i] = (int)ceil_div((int64_t)P.KT[i] * a.seg[i].nb, 2);
         } else {
             P.KT[i] = 0;
-            P.nkg[i] = 0;
+            P.US[i] = 0;
         }
-        P.C += P.nkg[i];
+        P.Urg += P.US[i];
     }
-    const int rpl = a.rows_per_group;
-    const int n_rgroups = (int)ceil_div(P.NT, rpl);
-    if (a.accumulate) {
-        P.mode = P.C > 1 ? kModeAtomic : kModeAdd;
-    } else if (P.C == 1) {
-        P.mode = kModeStore;
-    } else if (a.ws != nullptr && P.C <= 255) {
-        P.mode = kModeFirst;
-    } else {
-        hipError_t e = launch_fill_zero(a.y, (int64_t)a.batch * a.N, s);
-        if (e != hipSuccess) return e;
-        P.mode = kModeAtomic;
-    }
-    if (a.x_dtype == UBW_F16) return launch_step_x<__half>(P, n_rgroups, rpl, s);
-    return launch_step_x<float>(P, n_rgroups, rpl, s);
+    if ((int64_t)P.NRG * P.Urg > INT32_MAX / 1024) return hipErrorInvalidValue;
+    P.U = P.NRG * P.Urg;
+    P.mode = a.accumulate ? kModeAdd : kModeFirst;
+    if (a.x_dtype == UBW_F16) return launch_step_x<__half>(P, rpl, s);
+    return launch_step_x<float>(P, rpl, s);
 }
 
 }  // namespace ubw

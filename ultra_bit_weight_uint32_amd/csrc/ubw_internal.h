@@ -39,7 +39,6 @@ struct Segment {
     const int32_t* idx;     // [Kv] virtual column -> activation column, or nullptr (identity)
     int nb;
     int Kv;                 // columns of this matrix: K, or s
-    int slices_per_group;   // 256-column slices per workgroup (>= 1)
 };
 
 // One launch: up to two segments accumulated into the same y.
@@ -54,12 +53,13 @@ struct StepArgs {
     float* y;               // [batch][N]
     int accumulate;         // 0: y = result, 1: y += result
     uint32_t* ws;           // zero-initialised counters (single-launch y = result), or nullptr
-    int rows_per_group;     // 1 or 2 row tiles per workgroup (<= max_rows_per_group(batch))
+    int rows_per_group;     // row tiles per unit: 1, 2 or 4 (<= max_rows_per_group(batch))
+    int workgroups;         // persistent workgroups to launch, 0 = as many as fit at once
 };
 
 // Workspace of the single-launch y = result mode: a 16-word header (word 0: error flag), then
-// 64 words (256 bytes) per 256-row group: the arrival counter at word 0 and the zeroer's flag
-// at word 32, on separate cache lines.
+// 64 words (256 bytes) per row group (at most one per 256-row tile): the arrival counter at
+// word 0 and the zeroing flag at word 32, on separate cache lines.
 constexpr int kWsHeaderWords = 16;
 constexpr int kWsRowGroupWords = 64;
 constexpr int kWsFlagOffset = 32;
@@ -74,7 +74,7 @@ hipError_t launch_build_lut(const void* x, int x_dtype, int batch, const float* 
 hipError_t launch_extract(const uint32_t* packed, int nb, int N, int K, int g, uint16_t* out, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
-// Largest rows_per_group the GEMV instances support for this batch (1 or 2).
+// Largest rows_per_group the GEMV instances support for this batch (4, 2 or 1).
 int max_rows_per_group(int batch);
 
 }  // namespace ubw
