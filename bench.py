@@ -37,7 +37,31 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="for hardware-counter runs: a 64 MiB device copy (known bytes, to scale the counters) "
+                         "then --steps cold steps; prints one line, no timing")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemv8_proj4096_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "ultra_bit_weight_uint32_amd", "csrc", "kernels.hip")
+
+
+def measured_traffic():
+    """HBM bytes per step-kernel launch from the committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    import hashlib
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+    except OSError:
+        return None
+    digest = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256", "").strip() != digest:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -101,6 +125,17 @@ def main():
         step(copies[i % ncopy])
     torch.cuda.synchronize()
 
+    if args.profile_run:
+        src = torch.ones(16 << 20, dtype=torch.float32, device=dev)   # 64 MiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        for i in range(args.steps):
+            step(copies[i % ncopy])
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": True, "steps": args.steps, "copy_bytes": src.numel() * 4}), flush=True)
+        return
+
     # A. the timed region: exactly K steps, synchronized on both sides, queued behind a GPU
     # sleep so the GPU runs them back to back (host launch overhead would otherwise dominate).
     # A step is one launch of the step kernel, so the time per step is also that kernel's
@@ -158,7 +193,7 @@ def main():
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "bytes_per_launch": step_bytes,
             "us_per_launch": round(step_mean, 3),
             "timing": "K back-to-back launches between two events on the launch stream, divided by K",
