@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the headline line: time every GEMV and layer of the 7B MLP (config 4) and the "
+                         "70B layer (config 5) at their batches, same protocol, one JSON line each")
     ap.add_argument("--profile-run", action="store_true",
                     help="for hardware-counter runs: a 64 MiB device copy (known bytes, to scale the counters) "
                          "then --steps cold steps; prints one line, no timing")
@@ -78,6 +81,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.configs:
+        config_sweep(torch, ubw, dev)
+        return
     wl = config3(seed=0)
     g = wl.gemvs[0]
     n, k, nb, s, ns, batch = g.n, g.k, g.nb, g.s, g.ns, g.batch
@@ -238,6 +244,56 @@ def run_queued(torch, launch, count):
             return start.elapsed_time(end)
         cycles *= 4
     raise RuntimeError("could not queue the timed launches ahead of the GPU")
+
+
+def config_sweep(torch, ubw, dev):
+    """Per-GEMV and per-layer times of configs 4 and 5 (cold: each timed loop rotates through at least
+    COLD_BYTES of distinct copies), printed as one JSON line per measurement."""
+    from workloads import algorithmic_bytes, config4, config5
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a).to(dev)
+
+    for label, wl in (("7B MLP (config 4)", config4(seed=0)), ("70B decoder layer (config 5)", config5(seed=0))):
+        base = []
+        for g in wl.gemvs:
+            base.append(dict(packed=ubw.pack_bases(t(g.bits), g.nb, g.n, g.k), ar=t(g.alpha_r), ac=t(g.alpha_c),
+                             x=t(g.x), packed_s=ubw.pack_bases(t(g.bits_s), g.ns, g.n, g.s), ar_s=t(g.alpha_r_s),
+                             ac_s=t(g.alpha_c_s), idx=t(g.idx), ws=ubw.workspace(g.n, dev)))
+        size = [sum(v.numel() * v.element_size() for v in d.values()) for d in base]
+
+        def copies_of(gis):
+            n = max(2, -(-COLD_BYTES // sum(size[i] for i in gis)))
+            return [[{k: v.clone() for k, v in base[i].items()} for i in gis] for _ in range(n)]
+
+        def call(d, g, b, y):
+            ubw.lut_gemv_refined(d["packed"], d["ar"], d["ac"], d["idx"], d["packed_s"], d["ar_s"], d["ac_s"],
+                                 d["x"][:b], g.n, g.k, y=y, workspace=d["ws"])
+
+        for gis, name in [(list(range(len(wl.gemvs))), "layer")] + [([i], g.name) for i, g in enumerate(wl.gemvs)]:
+            C = copies_of(gis)
+            for b in wl.batches:
+                ys = [torch.zeros((b, wl.gemvs[i].n), device=dev) for i in gis]
+
+                def launch(k):
+                    c = C[k % len(C)]
+                    for j, i in enumerate(gis):
+                        call(c[j], wl.gemvs[i], b, ys[j])
+
+                for k in range(len(C)):
+                    launch(k)
+                reps = 100 if sum(size[i] for i in gis) < (64 << 20) else 20
+                us = run_queued(torch, launch, reps) * 1e3 / reps
+                by = sum(algorithmic_bytes(wl.gemvs[i].n, wl.gemvs[i].k, wl.gemvs[i].nb, b, 2, wl.gemvs[i].s,
+                                           wl.gemvs[i].ns) for i in gis)
+                print(json.dumps({"sweep": label, "gemv": name, "batch": b, "us": round(us, 2),
+                                  "GBps": round(by / us / 1e3, 1), "pct_of_peak": round(by / us / 1e3 / PEAK_GBS * 100, 2),
+                                  "algorithmic_bytes": by, "cold_copies": len(C)}), flush=True)
+            del C
+            torch.cuda.empty_cache()
+        del base
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(g, step_bytes, seconds):

@@ -121,13 +121,14 @@ int ubw_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, i
  * host pointer.
  * A workspace lets a call that overwrites y (accumulate = 0) run as ONE launch: the kernel's
  * persistent workgroups (never more than the device holds at once) combine partial sums with
- * fp32 atomics; at its start each workgroup zeroes the rows of the row groups it owns and
- * raises their flags in the workspace, and a workgroup reads a row group's flag before adding
- * into it. Without a workspace (NULL, 0 bytes) the library zero-fills y with a separate
+ * fp32 atomics; each workgroup zeroes the rows of the row groups it owns and, once the zeroing
+ * has been performed, raises their flags in the workspace; a workgroup reads a row group's
+ * flag before adding into it. Without a workspace (NULL, 0 bytes) the library zero-fills y with a separate
  * launch first. Rules: zero-fill the workspace once after allocating it (the kernels leave it
  * consistent after every call, whatever the shape); a workspace serves calls on one stream at a
  * time (calls that may run concurrently need separate workspaces); word 0 becomes nonzero only
- * if a wait gave up (an internal error that should never occur).
+ * if a wait gave up (an internal error that should never occur), after which the workspace
+ * must be zero-filled again.
  */
 int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out);
 
@@ -141,7 +142,8 @@ int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* 
  *   accumulate   0: y = result; 1: y += result
  *   workspace    ubw_workspace_bytes() bytes, or NULL with ws_bytes == 0 (see there)
  * Errors: UBW_EINVAL (null, nb < 1, N < 1, K < 1, batch not in [1, UBW_MAX_BATCH], workspace
- *         NULL with ws_bytes != 0), UBW_EUNSUPPORTED (g != 8, dtype), UBW_EALIGN (packed or
+ *         NULL with ws_bytes != 0), UBW_EUNSUPPORTED (g != 8, dtype, or an operand of 2 GiB or
+ *         more: the kernel addresses each operand with 32-bit offsets), UBW_EALIGN (packed or
  *         workspace), UBW_ESIZE (ws_bytes too small), UBW_EHIP.
  */
 int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb,
@@ -158,8 +160,9 @@ int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alph
  *   packed_s     from ubw_pack_bases(ns, N, s, g=8) of the refinement bases [ns][N][s]
  *   alpha_r_s    fp32 [ns][N];  alpha_c_s fp32 [ns][s]
  *   K            columns of x (the activation row length)
- * Indices are not range-checked on the device (the page's VCM carries no metadata checks);
- * ubw_check_indices validates them when the caller wants that.
+ * Indices are not validated on the device (the page's VCM carries no metadata checks): an
+ * index outside [0, K) is clamped to K - 1, so it never reads outside x but gives a wrong
+ * result; ubw_check_indices validates them when the caller wants that.
  * Errors: as ubw_lut_gemv; s < 1 is UBW_EINVAL.
  */
 int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_s,
@@ -199,8 +202,8 @@ int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, i
  * explicit launch geometry. The kernel walks a list of units (a unit: rows_per_group tiles of
  * 256 rows x two (256-column slice, base) items) split into equal contiguous ranges over
  * `workgroups` persistent workgroups (0 = as many as the device holds at once; larger values
- * are capped to that). rows_per_group is 1, 2 or 4 for batch 1, at most 2 for batch 2 and 1
- * above (UBW_ERANGE otherwise). Results equal the default geometry's up to fp32 summation
+ * are capped to that). rows_per_group is 1, 2 or 4 for batch 1 and 1 above (UBW_ERANGE
+ * otherwise). Results equal the default geometry's up to fp32 summation
  * order. For vcm = 0, idx is ignored and Kv = K; for vcm = 1, Kv = s. workspace as
  * ubw_lut_gemv.
  */

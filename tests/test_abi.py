@@ -101,8 +101,9 @@ def test_geometry_rejects():
     assert L.ubw_lut_gemv_geometry(*base, 8, 1, *tail) == ERANGE
     assert L.ubw_lut_gemv_geometry(*base, 1, -1, *tail) == ERANGE     # workgroups < 0
     b2 = list(base)
-    b2[10] = 2                                                        # batch 2 allows up to 2 row tiles
+    b2[10] = 2                                                        # batch 2 allows only 1 row tile
     assert L.ubw_lut_gemv_geometry(*b2, 4, 1, *tail) == ERANGE
+    assert L.ubw_lut_gemv_geometry(*b2, 2, 1, *tail) == ERANGE
     b4 = list(base)
     b4[10] = 4                                                        # batch 4 allows only 1 row tile
     assert L.ubw_lut_gemv_geometry(*b4, 2, 1, *tail) == ERANGE

@@ -198,7 +198,7 @@ def test_gemv_geometries_batched(batch):
     n, k = 3 * 256 + 5, 3 * 256 + 1
     g = make_integer_gemv(rng, n, k, 3, batch=batch)
     for rpg in (1, 2):
-        if rpg > 1 and batch > 2:
+        if rpg > 1 and batch > 1:
             continue
         for wgs in (1, 4, 0):
             y = torch.zeros((batch, n), device=DEV)
@@ -277,21 +277,21 @@ def test_vcm_integer_exact(k, s, batch, ns):
 
 
 def test_vcm_geometries_integer_exact():
-    rng = np.random.default_rng(21)
     n, k, s = 600, 3000, 700
-    g = make_integer_gemv(rng, n, k, 1, s=s, ns=2, batch=2)
-    ps = pack(g.bits_s, s)
-    want = oracle_gemv(g) - oracle_gemv(g, refine=False)
-    for rpg, wgs in ((1, 0), (2, 3), (1, 1), (2, 0)):
-        y = torch.zeros((2, n), device=DEV)
+    for batch, rpg, wgs in ((2, 1, 0), (2, 1, 1), (2, 1, 3), (1, 2, 3), (1, 2, 0), (1, 4, 5), (1, 1, 7)):
+        rng = np.random.default_rng(21 + batch)
+        g = make_integer_gemv(rng, n, k, 1, s=s, ns=2, batch=batch)
+        ps = pack(g.bits_s, s)
+        want = oracle_gemv(g) - oracle_gemv(g, refine=False)
+        y = torch.zeros((batch, n), device=DEV)
         ubw.lut_gemv_geometry(ps, dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), n, s, y, idx=dev(g.idx), k=k,
                               accumulate=True, rows_per_group=rpg, workgroups=wgs)
-        assert np.array_equal(host(y).astype(np.float64), want)
-        y = torch.full((2, n), float("nan"), device=DEV)
+        assert np.array_equal(host(y).astype(np.float64), want), (batch, rpg, wgs)
+        y = torch.full((batch, n), float("nan"), device=DEV)
         ubw.lut_gemv_geometry(ps, dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), n, s, y, idx=dev(g.idx), k=k,
                               accumulate=False, rows_per_group=rpg, workgroups=wgs,
                               workspace=ubw.workspace(n, DEV))
-        assert np.array_equal(host(y).astype(np.float64), want)
+        assert np.array_equal(host(y).astype(np.float64), want), (batch, rpg, wgs)
 
 
 def test_vcm_every_column_salient_doubles():

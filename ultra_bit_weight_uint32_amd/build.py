@@ -16,6 +16,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 instructions stay off: hipcc would otherwise emit them from scalar code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a wave-uniform atomic with a returned value would otherwise be rewritten into a wave
+    # reduction that waits for the value at once (and for every load issued before it)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -84,6 +84,13 @@ StepArgs make_step(int64_t N, const void* x, int x_dtype, int64_t K, int batch, 
     return a;
 }
 
+// Launches a step. The main segment goes in seg[0] (no idx) and a refinement segment in
+// seg[1] (with idx); a refinement-only step leaves seg[0] empty.
+int run_step(StepArgs& a, void* stream) {
+    if (!step_buffers_fit(a)) return UBW_EUNSUPPORTED;
+    return hip_status(launch_step(a, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,7 +163,7 @@ int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alph
     a.nseg = 1;
     a.seg[0] = make_segment(packed, alpha_r, alpha_c, nullptr, nb, K);
     a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(K, nb), batch);
-    return hip_status(launch_step(a, as_stream(stream)));
+    return run_step(a, stream);
 }
 
 int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_s, const float* alpha_r_s,
@@ -170,10 +177,10 @@ int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_
     uint32_t* ws = nullptr;
     if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
     StepArgs a = make_step(N, x, x_dtype, K, batch, y, 1, ws);
-    a.nseg = 1;
-    a.seg[0] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
+    a.nseg = 2;
+    a.seg[1] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
     a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(s, ns), batch);
-    return hip_status(launch_step(a, as_stream(stream)));
+    return run_step(a, stream);
 }
 
 int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb,
@@ -193,7 +200,7 @@ int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const flo
     a.seg[0] = make_segment(packed, alpha_r, alpha_c, nullptr, nb, K);
     a.seg[1] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
     a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(K, nb) + units_of(s, ns), batch);
-    return hip_status(launch_step(a, as_stream(stream)));
+    return run_step(a, stream);
 }
 
 int ubw_check_indices(const int32_t* idx_host, int64_t s, int64_t K) {
@@ -226,11 +233,16 @@ int ubw_lut_gemv_geometry(const uint32_t* packed, const float* alpha_r, const fl
     uint32_t* ws = nullptr;
     if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
     StepArgs a = make_step(N, x, x_dtype, vcm ? K : Kv, batch, y, accumulate, ws);
-    a.nseg = 1;
-    a.seg[0] = make_segment(packed, alpha_r, alpha_c, vcm ? idx : nullptr, nb, Kv);
+    if (vcm) {
+        a.nseg = 2;
+        a.seg[1] = make_segment(packed, alpha_r, alpha_c, idx, nb, Kv);
+    } else {
+        a.nseg = 1;
+        a.seg[0] = make_segment(packed, alpha_r, alpha_c, nullptr, nb, Kv);
+    }
     a.rows_per_group = rows_per_group;
     a.workgroups = workgroups;
-    return hip_status(launch_step(a, as_stream(stream)));
+    return run_step(a, stream);
 }
 
 int ubw_bench_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream) {

@@ -25,6 +25,9 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
+#include <type_traits>
+
 #include "../../include/ubw.h"
 #include "ubw_internal.h"
 
@@ -32,6 +35,21 @@ namespace ubw {
 
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) const char lds_cchar;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// Element i of an activation block held in LDS, as fp32.
+template <typename XT>
+__device__ __forceinline__ float lds_x(lds_cchar* base, uint32_t i);
+template <>
+__device__ __forceinline__ float lds_x<float>(lds_cchar* base, uint32_t i) {
+    return *(const __attribute__((address_space(3))) float*)(base + 4 * i);
+}
+template <>
+__device__ __forceinline__ float lds_x<__half>(lds_cchar* base, uint32_t i) {
+    const unsigned short v = *(const __attribute__((address_space(3))) unsigned short*)(base + 2 * i);
+    return __half2float(__builtin_bit_cast(__half, v));
+}
 
 // ---------------------------------------------------------------------------------------
 // Small helpers shared by several kernels.
@@ -322,30 +340,49 @@ __global__ void k_extract4(const uint32_t* __restrict__ packed, int nb, int N, i
 // ---------------------------------------------------------------------------------------
 // The GEMV step (g = 8): a persistent, stream-K style kernel.
 //
-// Work list: for each row group rg (RPL tiles of 256 rows), the units of each segment in
-// order. A segment's items are (slice, base) pairs, slice-major; a unit is two consecutive
-// items, one per half of every wave: lane l of half h in wave w owns tile row 32 w + l for
-// item h. The list holds U = NRG * Urg units; workgroup g of G takes units
-// [g U / G, (g + 1) U / G), keeps per-row partial sums across consecutive units of one row
-// group and adds them into y with fp32 atomics when its range leaves that row group.
+// Work list: the units of segment 0 (the main bases) row group by row group, then those of
+// segment 1 (the salient refinement, if any) row group by row group. For each row group (RPL
+// tiles of 256 rows) a segment's items are its (slice, base) pairs, slice-major; a unit is two
+// consecutive items, one per half of every wave: lane l of half h in wave w owns tile row
+// 32 w + l for item h. Workgroup g of G takes units [g U / G, (g + 1) U / G): at most one run
+// of main units and one run of refinement units, each processed by its own loop, so that every
+// unit of a loop reads its activations the same way. Per-row partial sums stay in registers
+// across consecutive units of one row group and go into y with fp32 atomics when the run leaves
+// that row group.
 // Per unit and activation row b: stage v = alpha_c * x for both items, build each item's 32
 // tables (half h writes LDS columns 32 h .. 32 h + 31), barrier, look up every owned row,
-// accumulate alpha_r * sum, barrier. The two halves of a row (different items) are added with
-// a cross-lane swap when flushing. The weights, scales and activations of the next units are
-// in flight while a unit is processed (three register slots, reloaded in place).
+// accumulate alpha_r * sum, barrier. The two halves of a row (different items) are added with a
+// cross-lane swap when flushing. The data of the next three units are in flight while a unit
+// is processed (three register slots, reloaded in place).
 //
 // y = result in one launch (kModeFirst): at its start workgroup g zeroes the rows of every
-// row group rg with rg mod G == g and raises that row group's flag; a workgroup reads the flag
-// of a row group before adding into it. Zeroing depends on nothing and the grid never exceeds
-// what the device holds at once, so every wait ends. Per row group, 256 bytes of workspace:
-// word 0 = (generation << 12) | arrivals, word 32 = flag.
+// row group rg with rg mod G == g, and raises that row group's flag once the zeroing has been
+// performed (at its first staging barrier); a workgroup reads the flag of a row group before
+// adding into it. Zeroing depends on nothing and the grid never exceeds what the device holds
+// at once, so every wait ends. Per row group, 256 bytes of workspace: word 0 =
+// (generation << 12) | arrivals, word 32 = flag (launches that zeroed the row group).
 
-enum { kModeStore = 0, kModeAdd = 1, kModeAtomic = 2, kModeFirst = 3 };
+enum { kModeStore = 0, kModeAtomic = 2, kModeFirst = 3 };
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kStepThreads = 512;
 constexpr uint32_t kArrBits = 12;
 constexpr uint32_t kArrMask = (1u << kArrBits) - 1u;
 constexpr uint32_t kGenMask = (1u << (32 - kArrBits)) - 1u;
+
+// Division by a divisor fixed for the launch: q = (n * m) >> sh for 0 <= n < 2^31, with
+// sh = 31 + ceil(log2 d) and m = ceil(2^sh / d) (the rounding error stays below 1 / d).
+struct FastDiv {
+    uint32_t m, sh;
+};
+__host__ __device__ inline FastDiv fast_div(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t p = 1ull << (31 + l);
+    return FastDiv{(uint32_t)((p + d - 1) / d), 31 + l};
+}
+__device__ __forceinline__ uint32_t div_by(uint32_t n, FastDiv f) {
+    return (uint32_t)(((uint64_t)n * f.m) >> f.sh);
+}
 
 struct StepParams {
     StepArgs a;
@@ -353,97 +390,182 @@ struct StepParams {
     int NRG;          // row groups
     int KT[2];        // slices per segment
     int US[2];        // units per row group per segment
-    int Urg;          // units per row group
-    int U;            // units in the whole list (U * G < 2^32, checked on the host)
+    int Urg;          // units per row group, both segments
+    int U;            // units in the whole list (< 2^31)
     int G;            // workgroups
     int mode;
+    int Q, R;         // U = Q G + R: workgroup g takes Q units, plus one if g < R
+    FastDiv dUS[2];   // division by US[si]
+    FastDiv dNb[2];   // division by seg[si].nb
 };
 
-template <typename XT, int RPL, int BMAX>
+// XL: the refinement segment gathers x through LDS (the whole activation block, at most
+// kXlBytes, is loaded with the unit and the gather reads it there), so its units wait for one
+// memory round trip instead of two (idx, then x at idx).
+constexpr uint32_t kXlBytes = 16 * kStepThreads;
+template <typename XT, int RPL, int BMAX, bool XL>
 struct Unit {
     uint4 w[RPL][2];   // this lane's item: its rows' 8 words (two 16-byte halves of the slice)
     float ar[RPL];     // alpha_r of the item's base at the lane's rows
     float ac;          // staging: alpha_c of the staged item's base at the staged column
-    XT xv[BMAX];       // staging: activations at the staged column
+    XT xv[BMAX];       // staging: activations of the staged column (0 for rows >= batch)
+    uint4 xb;          // XL: this thread's 16 bytes of the activation block
+    uint32_t xc;       // XL: idx of the staged column (read at staging, so nothing waits for it here)
+    bool cv;           // XL: the staged column exists
 };
 
-// Where unit x of the list lives.
-struct UnitPos {
-    int rg;     // row group
-    int si;     // segment
-    int pair;   // unit within the segment's units of this row group
-};
-
-// (row group, unit within the row group) of a cursor walking the list.
+// A unit within its segment's part of the list: row group, unit within the row group, and the
+// slice and base of the unit's first item (item 2 q), kept incrementally so that walking the
+// list needs no division.
 struct Cursor {
-    int rg, q;
+    int rg, q, ks, k;
 };
 
-__device__ __forceinline__ void advance(Cursor& cu, int Urg) {
-    if (++cu.q == Urg) {
+__device__ __forceinline__ Cursor cursor_at(uint32_t u, int US, FastDiv dUS, int nb, FastDiv dNb) {
+    Cursor cu;
+    cu.rg = (int)div_by(u, dUS);
+    cu.q = (int)(u - (uint32_t)cu.rg * (uint32_t)US);
+    cu.ks = (int)div_by(2u * (uint32_t)cu.q, dNb);
+    cu.k = 2 * cu.q - cu.ks * nb;
+    return cu;
+}
+
+__device__ __forceinline__ void advance(Cursor& cu, int US, int nb) {
+    if (++cu.q == US) {
         cu.q = 0;
+        cu.ks = 0;
+        cu.k = 0;
         ++cu.rg;
+        return;
     }
+    cu.k += 2;  // two items on; nb may be 1
+    if (cu.k >= nb) { cu.k -= nb; ++cu.ks; }
+    if (cu.k >= nb) { cu.k -= nb; ++cu.ks; }
 }
 
-__device__ __forceinline__ UnitPos unit_pos(const StepParams& P, Cursor cu) {
-    UnitPos r;
-    r.rg = cu.rg;
-    r.si = cu.q < P.US[0] ? 0 : 1;
-    r.pair = r.si ? cu.q - P.US[0] : cu.q;
-    return r;
+// Slice and base of item 2 q + d (d = 0 or 1) of the cursor's unit.
+__device__ __forceinline__ void item_of(const Cursor& cu, int d, int nb, int& ks, int& k) {
+    k = cu.k + d;
+    ks = cu.ks;
+    if (k >= nb) { k -= nb; ++ks; }
 }
 
-template <typename XT, int RPL, int BMAX>
-__device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX>& U, const StepParams& P, Cursor cu, int h, int rho,
-                                          int tid) {
+// Raw buffer access: a load whose offset lies at or beyond the descriptor's size returns 0 and
+// touches no memory. Every buffer the step reads is below 2 GiB (checked on the host), so
+// kOob is out of range for all of them, and a descriptor of size 0 turns all its loads off.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;
+// Descriptor fields must sit in scalar registers. Every caller passes values that are uniform
+// over the workgroup, but some are computed on the vector unit (divisions, 64-bit products), where
+// the compiler cannot prove it and would wrap each load in a loop over distinct descriptors;
+// readfirstlane states the uniformity.
+__device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* base = (void*)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ float buf_f32(Rsrc r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint4 buf_u128(Rsrc r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void buf_x(Rsrc r, uint32_t off, float& v) { v = buf_f32(r, off); }
+__device__ __forceinline__ void buf_x(Rsrc r, uint32_t off, __half& v) {
+    v = __builtin_bit_cast(__half, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+}
+
+// Requests one unit of segment SI (1: the columns go through idx). Every load is issued on every
+// path, out-of-range items, rows and columns reading 0 through the buffer bounds, so the
+// compiler's waits stay exact: a unit waits for its own data only, never for the units requested
+// after it. Order: alpha_c and x first (for idx segments: idx, alpha_c and, with XL, the whole
+// activation block), so the tables can be built while the weights are still arriving; then the
+// weights and alpha_r; for idx segments without XL the gather of x last, so that only it waits
+// for idx. A unit past the run (!valid) issues the
+// same loads through empty descriptors: they read nothing. (Branching around them instead
+// makes the compiler merge two register assignments with copies that wait for everything.)
+// Per-lane constants of the loads, computed once: a unit's offsets are then a scalar (uniform)
+// part plus one of these, so each unit costs a handful of vector instructions.
+struct LaneC {
+    uint32_t sd;      // staged item within the unit (tid / 256): uniform over a wave
+    uint32_t colL;    // staged column within the slice (tid mod 256)
+    uint32_t hsel;    // lookup item within the unit (half of the wave)
+    uint32_t wl;      // byte offset of this lane's row in its item's tile, item 2 q + h relative to 2 q
+    uint32_t rho;     // tile row
+};
+
+template <int SI, bool XL, typename XT, int RPL, int BMAX>
+__device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const StepParams& P, Cursor cu, bool valid,
+                                          const LaneC& lcn, int tid) {
     const StepArgs& a = P.a;
-    const UnitPos up = unit_pos(P, cu);
-    const Segment& sg = a.seg[up.si];
-    const int KT = P.KT[up.si];
-    const int nitems = KT * sg.nb;
-    const int rt0 = up.rg * RPL;
-    // staging role: thread tid stages column (tid mod 256) of item 2 pair + tid / 256
-    const int its = 2 * up.pair + (tid >> 8);
-    const bool sval = its < nitems;
-    const int sks = sval ? its / sg.nb : 0, sk = sval ? its - sks * sg.nb : 0;
-    const int col = sks * kSliceCols + (tid & 255);
-    const bool cvalid = sval && col < sg.Kv;
-    int xcol = col;
-    if (sg.idx) xcol = cvalid ? sg.idx[col] : 0;  // requested first: the gather below waits on it
-    // lookup role: item 2 pair + h for tile row rho
-    const int itl = 2 * up.pair + h;
-    const bool lval = itl < nitems;
-    const int lks = lval ? itl / sg.nb : 0, lk = lval ? itl - lks * sg.nb : 0;
+    const Segment& sg = a.seg[SI];
+    const int nitems = P.KT[SI] * sg.nb;
+    const uint32_t xs = sizeof(XT);
+    const uint32_t ldx = (uint32_t)a.ldx;
+    const Rsrc r_x = make_rsrc(a.x, valid ? (uint32_t)a.batch * ldx * xs : 0u);
+    // the unit's two items (slice, base): item 2 q and item 2 q + 1
+    int ks1, k1;
+    item_of(cu, 1, sg.nb, ks1, k1);
+    // staging role: column (tid mod 256) of item 2 q + tid / 256 (scalar per wave)
+    const int sks = lcn.sd ? ks1 : cu.ks, sk = lcn.sd ? k1 : cu.k;
+    const bool its_ok = 2 * cu.q + (int)lcn.sd < nitems;
+    const uint32_t colBase = (uint32_t)sks * kSliceCols;
+    const bool cvalid = its_ok && colBase + lcn.colL < (uint32_t)sg.Kv;
+    // idx of the staged column; with XL it is loaded straight into the unit (a copy of a value
+    // still in flight would wait for it)
+    uint32_t raw = 0;
+    if constexpr (SI == 1) {
+        const Rsrc r_idx = make_rsrc(sg.idx, valid ? (uint32_t)sg.Kv * 4u : 0u);
+        const int ioff = (int)(cvalid ? (colBase + lcn.colL) * 4u : kOob);
+        if constexpr (XL) U.xc = __builtin_amdgcn_raw_buffer_load_b32(r_idx, ioff, 0, 0);
+        else raw = __builtin_amdgcn_raw_buffer_load_b32(r_idx, ioff, 0, 0);
+    }
+    const uint32_t acBase = ((uint32_t)sk * (uint32_t)sg.Kv + colBase) * 4u;
+    U.ac = buf_f32(make_rsrc(sg.alpha_c, valid ? (uint32_t)sg.nb * (uint32_t)sg.Kv * 4u : 0u),
+                   cvalid ? acBase + lcn.colL * 4u : kOob);
+    if constexpr (SI == 0) {
+#pragma unroll
+        for (int b = 0; b < BMAX; ++b)
+            buf_x(r_x, cvalid ? ((uint32_t)b * ldx + colBase) * xs + lcn.colL * xs : kOob, U.xv[b]);
+    } else if constexpr (XL) {
+        U.xb = buf_u128(r_x, 16u * (uint32_t)tid);  // before the weights, like x in the main segment
+        U.cv = cvalid;
+    }
+    // lookup role: item 2 q + h for tile row rho
+    const bool lval = 2 * cu.q + (int)lcn.hsel < nitems;
+    const uint32_t slab = (uint32_t)nitems * kTileWords * 4u;  // one row tile: all slices and bases
+    const uint32_t woff = lval ? (uint32_t)cu.q * (2u * kTileWords * 4u) + lcn.wl : kOob;
+    const uint32_t arBase = (lcn.hsel ? (uint32_t)k1 : (uint32_t)cu.k) * (uint32_t)a.N * 4u;
+    const Rsrc r_ar = make_rsrc(sg.alpha_r, valid ? (uint32_t)sg.nb * (uint32_t)a.N * 4u : 0u);
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
-        const int rt = rt0 + j;
-        U.w[j][0] = U.w[j][1] = make_uint4(0, 0, 0, 0);
-        if (lval && rt < P.NT) {
-            const uint4* tp =
-                reinterpret_cast<const uint4*>(sg.packed + ((int64_t)(rt * KT + lks) * sg.nb + lk) * kTileWords);
-            U.w[j][0] = tp[rho];
-            U.w[j][1] = tp[kTileRows + rho];
-        }
-        const int row = rt * kTileRows + rho;
-        U.ar[j] = (lval && rt < P.NT && row < a.N) ? sg.alpha_r[(int64_t)lk * a.N + row] : 0.f;
+        const int rt = cu.rg * RPL + j;
+        const Rsrc r_w = make_rsrc(sg.packed + (int64_t)rt * nitems * kTileWords, valid && rt < P.NT ? slab : 0u);
+        U.w[j][0] = buf_u128(r_w, woff);
+        U.w[j][1] = buf_u128(r_w, lval ? woff + kTileRows * 16u : kOob);
+        const uint32_t row = (uint32_t)rt * kTileRows + lcn.rho;
+        U.ar[j] = buf_f32(r_ar, lval && row < (uint32_t)a.N ? arBase + row * 4u : kOob);
     }
-    U.ac = cvalid ? sg.alpha_c[(int64_t)sk * sg.Kv + col] : 0.f;
-    const XT* xp = reinterpret_cast<const XT*>(a.x);
+    if constexpr (SI == 1 && !XL) {
+        const uint32_t xc = raw < ldx ? raw : ldx - 1u;  // in range by contract
 #pragma unroll
-    for (int b = 0; b < BMAX; ++b) U.xv[b] = (b < a.batch && cvalid) ? xp[(int64_t)b * a.ldx + xcol] : XT(0.f);
+        for (int b = 0; b < BMAX; ++b) buf_x(r_x, cvalid ? ((uint32_t)b * ldx + xc) * xs : kOob, U.xv[b]);
+    }
 }
 
-// First unit of workgroup g's range, and the workgroup whose range holds unit x (the largest g
-// with start(g) <= x). 32-bit: the host guarantees U * G < 2^32.
+// First unit of workgroup g's range: the first R workgroups take Q + 1 units, the rest Q.
 __device__ __forceinline__ uint32_t range_start(const StepParams& P, uint32_t g) {
-    return g * (uint32_t)P.U / (uint32_t)P.G;
-}
-__device__ __forceinline__ int owner_of(const StepParams& P, uint32_t x) {
-    return (int)(((x + 1) * (uint32_t)P.G - 1) / (uint32_t)P.U);
+    return g * (uint32_t)P.Q + (g < (uint32_t)P.R ? g : (uint32_t)P.R);
 }
 
-template <typename XT, int RPL, int BMAX>
+// Occupancy: the second argument is a minimum of waves per SIMD (2 lets the compiler use up to
+// 256 VGPRs); two workgroups per CU need at most 128, which the instances with one or two row
+// tiles and batch up to 4 stay within. (Asking for 4 waves per SIMD instead makes the compiler
+// issue the table lookups in smaller batches, which costs more than it gains.)
+template <typename XT, int RPL, int BMAX, bool XL>
 __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(StepParams P) {
     // Batches above 2 keep their per-row accumulators in thread-private LDS slots (registers
     // indexed by a runtime batch index would go to scratch).
@@ -456,6 +578,13 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
     lds_f32* sacc = (lds_f32*)s_acc;
     lds_cchar* tb = (lds_cchar*)s_tab;
     const StepArgs& a = P.a;
+    // The parameter block spans four 64-byte lines of the scalar cache, and every fetch of a
+    // missing line costs a full trip to where the runtime keeps kernel arguments. Asking for one
+    // word of each line here puts all four fetches in one batch instead of letting them
+    // trickle in as first used (one wait instead of several).
+    static_assert(sizeof(StepParams) <= 256, "parameter block grew: touch its new lines");
+    static_assert(offsetof(StepParams, dNb) >= 192, "one touched word per 64-byte line");
+    asm volatile("" ::"s"(P.a.seg[0].nb), "s"(P.a.N), "s"(P.NRG), "s"(P.dNb[1].sh));
 
     const int tid = threadIdx.x;
     const int wv = tid >> 6, L = tid & 63;
@@ -465,49 +594,62 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
     const int p0 = 32 * wv;                       // table entries this lane builds
     uint32_t lc[8];
     lane_columns(l, lc);
+    LaneC lcn;
+    lcn.sd = (uint32_t)__builtin_amdgcn_readfirstlane(tid >> 8);
+    lcn.colL = (uint32_t)(tid & 255);
+    lcn.hsel = (uint32_t)h;
+    lcn.wl = (uint32_t)h * (kTileWords * 4u) + 16u * (uint32_t)rho;
+    lcn.rho = (uint32_t)rho;
 #pragma unroll
     for (int i = 0; i < 8; ++i) lc[i] += 0x80808080u * (uint32_t)h;  // half h's tables: +128 bytes
 
     const int g = blockIdx.x;
-    const int x0 = (int)range_start(P, g);
-    const int x1 = (int)range_start(P, g + 1);
-    Cursor lcur{x0 / P.Urg, x0 % P.Urg};  // next unit to load
-    Cursor pcur = lcur;                     // next unit to process
+    const uint32_t x0 = range_start(P, g);
+    const uint32_t x1 = range_start(P, g + 1);
+    const uint32_t Um = (uint32_t)P.NRG * (uint32_t)P.US[0];  // units of segment 0
 
-    // The first units' weights, scales and activations are requested before anything waits.
-    Unit<XT, RPL, BMAX> s0, s1, s2;
-    if (x0 < x1) { load_unit(s0, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
-    if (x0 + 1 < x1) { load_unit(s1, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
-    if (x0 + 2 < x1) { load_unit(s2, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
-
+    // y = result in one launch: workgroup g zeroes the rows of the row groups rg = g, g + G, ...
+    // with atomic exchanges and raises their flags once every exchange has been performed. It
+    // does so right after requesting its first unit's data, so the wait for the exchanges
+    // overlaps that request and covers nothing else.
     const bool first_mode = P.mode == kModeFirst;
-    if (first_mode) {
-        // zero the rows of the row groups this workgroup owns and raise their flags
-        for (int rg = g; rg < P.NRG; rg += P.G) {
-            uint32_t* cnt = a.ws + kWsHeaderWords + kWsRowGroupWords * rg;
-            float sink = 0.f;
-            uint32_t gen = 0;
-            if (tid == 0) gen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> kArrBits;
-            if (tid < kTileRows) {
+    // Row group rg is zeroed by workgroup (rg + off) mod G. With off = NRG (when G >= 2 NRG) the
+    // zeroing workgroups are not the first ones, which the device places on CUs that also receive
+    // the workgroups beyond one per CU.
+    const int zoff = 2 * P.NRG <= P.G ? P.NRG : 0;
+    const int zrg0 = g >= zoff ? g - zoff : g - zoff + P.G;  // first row group this workgroup zeroes
+    bool zpend = first_mode && zrg0 < P.NRG;
+    auto rg_word = [&](int rg) { return a.ws + kWsHeaderWords + kWsRowGroupWords * rg; };
+    auto zero_owned = [&]() {
+        zpend = false;
+        for (int rg = zrg0; rg < P.NRG; rg += P.G) {
+            float zr[RPL][BMAX];
 #pragma unroll
-                for (int j = 0; j < RPL; ++j) {
-                    const int rt = rg * RPL + j;
-                    const int row = rt * kTileRows + tid;
-                    if (rt >= P.NT || row >= a.N) continue;
-                    for (int b = 0; b < a.batch; ++b)
-                        sink += __hip_atomic_exchange(a.y + (int64_t)b * a.N + row, 0.f, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
+            for (int j = 0; j < RPL; ++j) {
+                const int rt = rg * RPL + j;
+                const int row = rt * kTileRows + tid;
+                const bool rv = tid < kTileRows && rt < P.NT && row < a.N;
+#pragma unroll
+                for (int b = 0; b < BMAX; ++b) {
+                    zr[j][b] = 0.f;
+                    if (rv && b < a.batch)
+                        zr[j][b] = __hip_atomic_exchange(a.y + (int64_t)b * a.N + row, 0.f, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
-            // depend on every returned value (so each exchange has been performed before the
-            // barrier); the store itself is harmless scratch in an unused workspace word
-            if (sink == 1.5e38f) a.ws[1] = 1u;
+            // wait for every returned value (each exchange has then been performed)
+#pragma unroll
+            for (int j = 0; j < RPL; ++j)
+#pragma unroll
+                for (int b = 0; b < BMAX; ++b) asm volatile("" ::"v"(zr[j][b]));
             __syncthreads();
+            // A flag counts the launches that have zeroed its row group, as the arrival
+            // counter's generation field counts the launches whose units have all arrived:
+            // between launches the two are equal, so the increment makes the flag generation + 1.
             if (tid == 0)
-                __hip_atomic_exchange(cnt + kWsFlagOffset, (gen + 1) & kGenMask, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(rg_word(rg) + kWsFlagOffset, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-    }
+    };
 
     float acc[RPL][kAccLds ? 1 : BMAX];
     auto clear_acc = [&]() {
@@ -522,29 +664,48 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
     };
     clear_acc();
 
-    // Row-group bookkeeping (thread 0): arrival counter value and the flag as last read.
-    int cur_rg = -1;
-    uint32_t arrived = 0, seen = 0;
+    // Row-group bookkeeping (thread 0): the arrival counter's value returned on entry, the units
+    // this workgroup adds to it, the flag as read on entry and, if that read did not find it
+    // raised, as read again before the last lookups of the run (kept apart so that a flush
+    // after a successful first read does not wait for the loads issued after it).
+    uint32_t arrived = 0, units_in = 0, seen = 0, seen_late = 0;
+    bool late = false;
+    auto want = [&]() { return ((arrived >> kArrBits) + 1) & kGenMask; };
+    // Entering row group rg with n of its units to process: add n to its counter's arrival
+    // field and take a first look at its flag. Both are requested before the loads that follow,
+    // so using their values never waits for those. Over a launch the arrivals of a row group
+    // add up to its unit count Urg; the flush that completes them resets the field.
+    auto enter = [&](int rg, uint32_t n) {
+        if (first_mode && tid == 0) {
+            units_in = n;
+            arrived = atomicAdd(rg_word(rg), n);
+            seen = __hip_atomic_load(rg_word(rg) + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
 
     // Add this workgroup's partial sums of row group rg into y.
     auto flush = [&](int rg) {
-        uint32_t* cnt = a.ws + kWsHeaderWords + kWsRowGroupWords * rg;
         if (first_mode) {
             if (tid == 0) {
-                const uint32_t want = ((arrived >> kArrBits) + 1) & kGenMask;
+                const uint32_t wnt = want();
+                uint32_t cur = seen;
+                if (late) {
+                    asm volatile("");  // keeps this a branch: only this path waits for seen_late
+                    cur = seen_late;
+                }
                 int n = 0;
-                while (seen != want) {
-                    __builtin_amdgcn_s_sleep(2);
-                    seen = __hip_atomic_load(cnt + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                while ((cur & kGenMask) != wnt) {
                     if (++n > kSpinLimit) {  // cannot happen while the owner runs; never hang
                         atomicOr(a.ws, 1u);
                         break;
                     }
+                    __builtin_amdgcn_s_sleep(2);
+                    cur = __hip_atomic_load(rg_word(rg) + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                // contributors of rg: the workgroups whose ranges meet rg's units
-                const int cg = owner_of(P, (uint32_t)(rg + 1) * P.Urg - 1) - owner_of(P, (uint32_t)rg * P.Urg) + 1;
-                if ((arrived & kArrMask) + 1 == (uint32_t)cg)  // last to arrive: arrivals 0, next generation
-                    atomicAdd(cnt, (1u << kArrBits) - (uint32_t)cg);
+                late = false;
+                const uint32_t total = (uint32_t)P.Urg;
+                if ((arrived & kArrMask) + units_in == total)  // completes it: arrivals 0, next generation
+                    atomicAdd(rg_word(rg), (1u << kArrBits) - total);
             }
             __syncthreads();
         }
@@ -563,7 +724,6 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
                 if (h == 0 && rv) {
                     float* dst = a.y + (int64_t)b * a.N + row;
                     if (P.mode == kModeStore) *dst = total;
-                    else if (P.mode == kModeAdd) *dst += total;
                     else atomicAdd(dst, total);
                 }
             }
@@ -571,7 +731,7 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
     };
 
     // One activation row of one unit: build the tables, barrier, look up.
-    auto row_pass = [&](const Unit<XT, RPL, BMAX>& U, bool mine, bool poll, int rg, int b, float S[RPL]) {
+    auto row_pass = [&](const Unit<XT, RPL, BMAX, XL>& U, bool mine, bool last, int rg, int b, float S[RPL]) {
         if (mine) {
             float v[8];
 #pragma unroll
@@ -582,37 +742,45 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
             for (int pp = 0; pp < 32; ++pp) tab[(p0 + pp) * 64 + 32 * h + l] = lut8_entry(lo, hi0, hi1, pp);
         }
         __syncthreads();
-        // look at the row group's flag while the last lookups before a flush run
-        if (poll && tid == 0 && b == 0)
-            seen = __hip_atomic_load(a.ws + kWsHeaderWords + kWsRowGroupWords * rg + kWsFlagOffset, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+        // before the lookups that end a row group, look at its flag again if the look on entry
+        // did not find it raised (the read then overlaps the lookups)
+        if (first_mode && last && tid == 0 && b == 0 && (seen & kGenMask) != want()) {
+            seen_late = __hip_atomic_load(rg_word(rg) + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            late = true;
+        }
 #pragma unroll
         for (int j = 0; j < RPL; ++j) S[j] = mine ? U.ar[j] * lookup_row(tb, U.w[j][0], U.w[j][1], lc, c) : 0.f;
     };
 
-    // One unit of the list (the one at pcur, which it then advances).
-    auto process = [&](const Unit<XT, RPL, BMAX>& U, int x) {
-        const UnitPos up = unit_pos(P, pcur);
-        if (up.rg != cur_rg) {  // entering a row group: arrive on its counter
-            cur_rg = up.rg;
-            if (first_mode && tid == 0)
-                arrived = atomicAdd(a.ws + kWsHeaderWords + kWsRowGroupWords * up.rg, 1u);
-        }
-        const int nitems = P.KT[up.si] * a.seg[up.si].nb;
-        const bool mine = 2 * up.pair + h < nitems;  // this half has an item in this unit
-        const bool last_of_rg = x + 1 == x1 || pcur.q + 1 == P.Urg;
-        advance(pcur, P.Urg);
+    // One unit: stage, then one table build + lookup pass per activation row; flush if it is
+    // the last unit of its row group in this run.
+    auto process = [&](const Unit<XT, RPL, BMAX, XL>& U, int nitems, Cursor cu, bool last, auto si_c) {
+        constexpr int SI = decltype(si_c)::value;
+        const bool mine = 2 * cu.q + h < nitems;  // this half has an item in this unit
         // scaled activations of both items: v = alpha_c * x (LUT-BSF folds alpha_c here)
+        if constexpr (SI == 1 && XL) {
+            // the activation block into the table area (free until the build below), then the
+            // gather through idx from there
+            lds_u32x4* blk = (lds_u32x4*)(tab + 4 * tid);
+            *blk = u32x4{U.xb.x, U.xb.y, U.xb.z, U.xb.w};
+            __syncthreads();
+            const uint32_t ldx = (uint32_t)a.ldx;
+            const uint32_t xc = U.xc < ldx ? U.xc : ldx - 1u;  // in range by contract
 #pragma unroll
-        for (int b = 0; b < BMAX; ++b)
-            if (b < a.batch) sv[b * 512 + tid] = U.ac * to_f32(U.xv[b]);
+            for (int b = 0; b < BMAX; ++b)
+                if (b < a.batch) sv[b * 512 + tid] = U.cv ? U.ac * lds_x<XT>(tb, (uint32_t)b * ldx + xc) : 0.f;
+        } else {
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b)
+                if (b < a.batch) sv[b * 512 + tid] = U.ac * to_f32(U.xv[b]);
+        }
         __syncthreads();
         if constexpr (!kAccLds) {
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
                 if (b < a.batch) {
                     float S[RPL];
-                    row_pass(U, mine, first_mode && last_of_rg, up.rg, b, S);
+                    row_pass(U, mine, last, cu.rg, b, S);
 #pragma unroll
                     for (int j = 0; j < RPL; ++j) acc[j][kAccLds ? 0 : b] += S[j];
                     __syncthreads();
@@ -621,32 +789,68 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
         } else {
             for (int b = 0; b < a.batch; ++b) {
                 float S[RPL];
-                row_pass(U, mine, first_mode && last_of_rg, up.rg, b, S);
+                row_pass(U, mine, last, cu.rg, b, S);
 #pragma unroll
                 for (int j = 0; j < RPL; ++j) sacc[(j * BMAX + b) * kStepThreads + tid] += S[j];
                 __syncthreads();
             }
         }
-        if (last_of_rg) {
-            flush(up.rg);
+        if (last) {
+            flush(cu.rg);
             clear_acc();
         }
     };
 
-    // Three register slots, each reloaded in place three units ahead (no copies between
-    // slots, which would wait on loads still in flight).
-    for (int x = x0; x < x1; x += 3) {
-        process(s0, x);
-        if (x + 3 < x1) { load_unit(s0, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
-        if (x + 1 < x1) {
-            process(s1, x + 1);
-            if (x + 4 < x1) { load_unit(s1, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
+    // The run of segment SI's units in [x0, x1). Three register slots, each reloaded in place
+    // three units ahead (no copies between slots, which would wait on loads still in flight);
+    // loads past the run are issued with valid = false and read nothing, so every path issues
+    // the same loads. An owner zeroes its row groups right after requesting its first unit.
+    auto run = [&](auto si_c) {
+        constexpr int SI = decltype(si_c)::value;
+        const uint32_t base = SI ? Um : 0u;
+        const uint32_t lo = SI ? (x0 > Um ? x0 : Um) : x0;
+        const uint32_t hi = SI ? x1 : (x1 < Um ? x1 : Um);
+        if (lo >= hi) return;
+        const int US = P.US[SI];
+        const int nb = a.seg[SI].nb;
+        const int nitems = P.KT[SI] * nb;
+        Cursor lcur = cursor_at(lo - base, US, P.dUS[SI], nb, P.dNb[SI]);
+        Cursor pcur = lcur;
+        // units of the run in the row group entered at unit x with cursor cu
+        auto run_units = [&](uint32_t x, const Cursor& cu) {
+            const uint32_t left = (uint32_t)(US - cu.q);
+            return hi - x < left ? hi - x : left;
+        };
+        Unit<XT, RPL, BMAX, XL> s0, s1, s2;
+        load_unit<SI, XL>(s0, P, lcur, true, lcn, tid);
+        advance(lcur, US, nb);
+        if (zpend) zero_owned();
+        enter(pcur.rg, run_units(lo, pcur));
+        load_unit<SI, XL>(s1, P, lcur, lo + 1 < hi, lcn, tid);
+        advance(lcur, US, nb);
+        load_unit<SI, XL>(s2, P, lcur, lo + 2 < hi, lcn, tid);
+        advance(lcur, US, nb);
+        auto step = [&](const Unit<XT, RPL, BMAX, XL>& U, uint32_t x) {
+            const bool last = x + 1 == hi || pcur.q + 1 == US;
+            process(U, nitems, pcur, last, si_c);
+            advance(pcur, US, nb);
+            if (last && x + 1 < hi) enter(pcur.rg, run_units(x + 1, pcur));
+        };
+        for (uint32_t x = lo; x < hi; x += 3) {
+            step(s0, x);
+            load_unit<SI, XL>(s0, P, lcur, x + 3 < hi, lcn, tid);
+            advance(lcur, US, nb);
+            if (x + 1 < hi) step(s1, x + 1);
+            load_unit<SI, XL>(s1, P, lcur, x + 4 < hi, lcn, tid);
+            advance(lcur, US, nb);
+            if (x + 2 < hi) step(s2, x + 2);
+            load_unit<SI, XL>(s2, P, lcur, x + 5 < hi, lcn, tid);
+            advance(lcur, US, nb);
         }
-        if (x + 2 < x1) {
-            process(s2, x + 2);
-            if (x + 5 < x1) { load_unit(s2, P, lcur, h, rho, tid); advance(lcur, P.Urg); }
-        }
-    }
+    };
+    run(std::integral_constant<int, 0>{});
+    if (P.US[1] > 0) run(std::integral_constant<int, 1>{});
+    if (zpend) zero_owned();  // a workgroup without units (the host never launches one)
 }
 
 // ---------------------------------------------------------------------------------------
@@ -728,14 +932,14 @@ hipError_t launch_extract(const uint32_t* packed, int nb, int N, int K, int g, u
 }
 
 // Workgroups of this instance that the device can hold at once (occupancy x CUs), cached.
-template <typename XT, int RPL, int BMAX>
+template <typename XT, int RPL, int BMAX, bool XL>
 static int64_t resident_capacity() {
     static int64_t cap = -1;  // benign race: every thread computes the same value
     if (cap < 0) {
         int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv8<XT, RPL, BMAX>, kStepThreads, 0) !=
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv8<XT, RPL, BMAX, XL>, kStepThreads, 0) !=
                 hipSuccess)
             return 0;
         cap = (int64_t)cus * per_cu;
@@ -745,27 +949,28 @@ static int64_t resident_capacity() {
 
 static inline bool a_ws_missing(const StepParams& P) { return P.a.ws == nullptr; }
 
-template <typename XT, int RPL, int BMAX>
+template <typename XT, int RPL, int BMAX, bool XL>
 static hipError_t launch_step_t(StepParams P, hipStream_t s) {
-    const int64_t cap = resident_capacity<XT, RPL, BMAX>();
+    const int64_t cap = resident_capacity<XT, RPL, BMAX, XL>();
     if (cap <= 0) return hipErrorInvalidConfiguration;
     // Never more workgroups than the device holds at once: the flag waits rely on it.
     int64_t G = P.a.workgroups > 0 ? P.a.workgroups : cap;
     G = G < cap ? G : cap;
     G = G < P.U ? G : P.U;
     P.G = (int)G;
-    if ((uint64_t)P.U * (uint64_t)P.G >= (1ull << 32)) return hipErrorInvalidValue;  // 32-bit range math
-    if (P.mode == kModeFirst && P.G == P.NRG) {
-        P.mode = kModeStore;  // every workgroup holds exactly one whole row group: plain stores
-    }
-    // the arrival field counts contributors of a row group: at most Urg + 1 workgroups
+    P.Q = P.U / P.G;
+    P.R = P.U - P.Q * P.G;
+    // every workgroup holds exactly one whole row group (one segment only: a refinement
+    // segment's units of a row group sit in another part of the list): plain stores
+    const bool whole_rows = P.G == P.NRG && P.US[1] == 0;
+    if (P.mode == kModeFirst && whole_rows) P.mode = kModeStore;
+    // the arrival field counts a row group's units (Urg) and must not overflow into the generation
     if (P.mode == kModeFirst && (a_ws_missing(P) || P.Urg + 1 > (int)kArrMask)) {
         hipError_t e = launch_fill_zero(P.a.y, (int64_t)P.a.batch * P.a.N, s);
         if (e != hipSuccess) return e;
         P.mode = kModeAtomic;
     }
-    if (P.mode == kModeAdd && P.G != P.NRG) P.mode = kModeAtomic;
-    hipLaunchKernelGGL((k_gemv8<XT, RPL, BMAX>), dim3((unsigned)P.G), dim3(kStepThreads), 0, s, P);
+    hipLaunchKernelGGL((k_gemv8<XT, RPL, BMAX, XL>), dim3((unsigned)P.G), dim3(kStepThreads), 0, s, P);
     return hipGetLastError();
 }
 
@@ -774,21 +979,41 @@ static hipError_t launch_step_t(StepParams P, hipStream_t s) {
 template <typename XT>
 static hipError_t launch_step_x(const StepParams& P, int rpl, hipStream_t s) {
     const int batch = P.a.batch;
+    // the gather of a refinement segment goes through LDS when the activation block fits (in
+    // whole 16-byte pieces, so that no load straddles the end of x)
+    const uint64_t xbytes = (uint64_t)batch * (uint64_t)P.a.ldx * sizeof(XT);
+    const bool xl = P.US[1] > 0 && xbytes <= kXlBytes && xbytes % 16 == 0;
     if (batch <= 1) {
-        if (rpl >= 4) return launch_step_t<XT, 4, 1>(P, s);
-        if (rpl >= 2) return launch_step_t<XT, 2, 1>(P, s);
-        return launch_step_t<XT, 1, 1>(P, s);
+        if (xl) {
+            if (rpl >= 4) return launch_step_t<XT, 4, 1, true>(P, s);
+            if (rpl >= 2) return launch_step_t<XT, 2, 1, true>(P, s);
+            return launch_step_t<XT, 1, 1, true>(P, s);
+        }
+        if (rpl >= 4) return launch_step_t<XT, 4, 1, false>(P, s);
+        if (rpl >= 2) return launch_step_t<XT, 2, 1, false>(P, s);
+        return launch_step_t<XT, 1, 1, false>(P, s);
     }
-    if (batch <= 2) {
-        if (rpl >= 2) return launch_step_t<XT, 2, 2>(P, s);
-        return launch_step_t<XT, 1, 2>(P, s);
-    }
-    if (batch <= 4) return launch_step_t<XT, 1, 4>(P, s);
-    if (batch <= 8) return launch_step_t<XT, 1, 8>(P, s);
-    return launch_step_t<XT, 1, 16>(P, s);
+    if (batch <= 2) return launch_step_t<XT, 1, 2, false>(P, s);
+    if (batch <= 4) return launch_step_t<XT, 1, 4, false>(P, s);
+    if (batch <= 8) return launch_step_t<XT, 1, 8, false>(P, s);
+    return launch_step_t<XT, 1, 16, false>(P, s);
 }
 
-int max_rows_per_group(int batch) { return batch <= 1 ? 4 : (batch <= 2 ? 2 : 1); }
+int max_rows_per_group(int batch) { return batch <= 1 ? 4 : 1; }
+
+// The step reads every buffer through 32-bit buffer offsets below 2^31 (kOob is out of range).
+bool step_buffers_fit(const StepArgs& a) {
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t xs = a.x_dtype == UBW_F16 ? 2 : 4;
+    if ((int64_t)a.batch * a.ldx * xs >= lim) return false;
+    for (int i = 0; i < a.nseg; ++i) {
+        const Segment& sg = a.seg[i];
+        const int64_t KT = ceil_div(sg.Kv, kSliceCols);
+        if ((int64_t)sg.nb * a.N * 4 >= lim || (int64_t)sg.nb * sg.Kv * 4 >= lim) return false;
+        if ((int64_t)sg.Kv * 4 >= lim || KT * sg.nb * kTileWords * 4 >= lim) return false;
+    }
+    return true;
+}
 
 hipError_t launch_step(const StepArgs& a, hipStream_t s) {
     StepParams P{};
@@ -808,8 +1033,16 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s) {
         P.Urg += P.US[i];
     }
     if ((int64_t)P.NRG * P.Urg > INT32_MAX / 1024) return hipErrorInvalidValue;
+    for (int i = 0; i < 2; ++i) {
+        P.dUS[i] = fast_div(P.US[i] > 0 ? (uint32_t)P.US[i] : 1u);
+        P.dNb[i] = fast_div(i < a.nseg && a.seg[i].nb > 0 ? (uint32_t)a.seg[i].nb : 1u);
+    }
+    if (!step_buffers_fit(a)) return hipErrorInvalidValue;
+    // the kernel gathers through idx in seg[1] only
+    if (a.seg[0].idx != nullptr || (a.nseg == 2 && a.seg[1].idx == nullptr)) return hipErrorInvalidValue;
+    if (P.Urg == 0) return hipErrorInvalidValue;
     P.U = P.NRG * P.Urg;
-    P.mode = a.accumulate ? kModeAdd : kModeFirst;
+    P.mode = a.accumulate ? kModeAtomic : kModeFirst;
     if (a.x_dtype == UBW_F16) return launch_step_x<__half>(P, rpl, s);
     return launch_step_x<float>(P, rpl, s);
 }

@@ -41,10 +41,11 @@ struct Segment {
     int Kv;                 // columns of this matrix: K, or s
 };
 
-// One launch: up to two segments accumulated into the same y.
+// One launch: up to two segments accumulated into the same y. seg[0] is the main matrix
+// (idx == nullptr, may be empty: nb = Kv = 0), seg[1] the refinement (idx != nullptr).
 struct StepArgs {
     Segment seg[2];
-    int nseg;               // 1 or 2
+    int nseg;               // 1 (seg[0] only) or 2
     int N;
     const void* x;          // [batch][ldx]
     int x_dtype;            // UBW_F32 / UBW_F16
@@ -73,8 +74,10 @@ hipError_t launch_build_lut(const void* x, int x_dtype, int batch, const float* 
                             int g, float* lut, hipStream_t s);
 hipError_t launch_extract(const uint32_t* packed, int nb, int N, int K, int g, uint16_t* out, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, hipStream_t s);
+// Whether every buffer of a step is small enough for the kernel's 32-bit buffer offsets.
+bool step_buffers_fit(const StepArgs& a);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
-// Largest rows_per_group the GEMV instances support for this batch (4, 2 or 1).
+// Largest rows_per_group the GEMV instances support for this batch (4 for batch 1, else 1).
 int max_rows_per_group(int batch);
 
 }  // namespace ubw
