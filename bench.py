@@ -271,15 +271,39 @@ def config_sweep(torch, ubw, dev):
             ubw.lut_gemv_refined(d["packed"], d["ar"], d["ac"], d["idx"], d["packed_s"], d["ar_s"], d["ac_s"],
                                  d["x"][:b], g.n, g.k, y=y, workspace=d["ws"])
 
-        for gis, name in [(list(range(len(wl.gemvs))), "layer")] + [([i], g.name) for i, g in enumerate(wl.gemvs)]:
+        def call_group(ds, gs, b, ys):
+            # GEMVs that read the same x in one launch (the first one's x serves all)
+            ubw.lut_gemv_multi([dict(packed=d["packed"], alpha_r=d["ar"], alpha_c=d["ac"], n=g.n, y=y, idx=d["idx"],
+                                     packed_s=d["packed_s"], alpha_r_s=d["ar_s"], alpha_c_s=d["ac_s"],
+                                     workspace=d["ws"]) for d, g, y in zip(ds, gs, ys)], ds[0]["x"][:b], gs[0].k)
+
+        names = [g.name for g in wl.gemvs]
+        runs = [(list(range(len(wl.gemvs))), "layer", None)]
+        # groups of GEMVs on one input: q/k/v and gate/up
+        groups = [[names.index(m) for m in grp] for grp in (("q", "k", "v"), ("gate", "up")) if set(grp) <= set(names)]
+        if groups:
+            parts = groups + [[i] for i in range(len(names)) if not any(i in grp for grp in groups)]
+            runs.append((list(range(len(wl.gemvs))), "layer_grouped", parts))
+            runs += [(grp, "+".join(names[i] for i in grp) + "_grouped", [list(grp)]) for grp in groups]
+        runs += [([i], g.name, None) for i, g in enumerate(wl.gemvs)]
+        for gis, name, parts in runs:
             C = copies_of(gis)
             for b in wl.batches:
                 ys = [torch.zeros((b, wl.gemvs[i].n), device=dev) for i in gis]
+                pos = {i: j for j, i in enumerate(gis)}
 
                 def launch(k):
                     c = C[k % len(C)]
-                    for j, i in enumerate(gis):
-                        call(c[j], wl.gemvs[i], b, ys[j])
+                    if parts is None:
+                        for j, i in enumerate(gis):
+                            call(c[j], wl.gemvs[i], b, ys[j])
+                        return
+                    for grp in parts:
+                        if len(grp) == 1:
+                            call(c[pos[grp[0]]], wl.gemvs[grp[0]], b, ys[pos[grp[0]]])
+                        else:
+                            call_group([c[pos[i]] for i in grp], [wl.gemvs[i] for i in grp], b,
+                                       [ys[pos[i]] for i in grp])
 
                 for k in range(len(C)):
                     launch(k)

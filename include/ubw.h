@@ -61,6 +61,8 @@ enum { UBW_SRC_CANON_BITS = 0, UBW_SRC_INT8_SIGNS = 1 };  /* ubw_pack_bases sour
 
 /* Largest batch one GEMV call accepts. */
 #define UBW_MAX_BATCH 16
+/* most GEMVs one ubw_lut_gemv_multi call takes */
+#define UBW_MAX_GROUP 8
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* ubw_status_str(int status);
@@ -182,6 +184,42 @@ int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const flo
                          const float* alpha_r_s, const float* alpha_c_s, int ns, int64_t N,
                          int64_t K, int g, const void* x, int x_dtype, int batch, float* y,
                          int accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * One GEMV of a grouped call: its own bases, scales, optional refinement, output and workspace.
+ * All pointers are device pointers except as noted; the struct array itself is host memory.
+ */
+typedef struct ubw_gemv_desc {
+    const uint32_t* packed;     /* main bases from ubw_pack_bases(nb, N, K, g=8) */
+    const float* alpha_r;       /* [nb][N] */
+    const float* alpha_c;       /* [nb][K] */
+    int nb;
+    const int32_t* idx;         /* [s] salient columns, or NULL: no refinement (the next five ignored) */
+    int64_t s;
+    const uint32_t* packed_s;   /* from ubw_pack_bases(ns, N, s, g=8) */
+    const float* alpha_r_s;     /* [ns][N] */
+    const float* alpha_c_s;     /* [ns][s] */
+    int ns;
+    int64_t N;
+    float* y;                   /* [batch][N] */
+    void* workspace;            /* ubw_workspace_bytes(nb, N, K, 8, batch) bytes, or NULL (see there) */
+    size_t ws_bytes;
+} ubw_gemv_desc;
+
+/*
+ * Several steps that read the same activations (e.g. the q, k, v projections, or gate and up)
+ * in ONE launch: for each desc, what ubw_lut_gemv_refined (idx != NULL) or ubw_lut_gemv
+ * (idx == NULL) computes. The device's workgroups are shared out in proportion to each GEMV's
+ * work; each GEMV's outputs and workspace are its own. The GEMVs of a call must not write
+ * overlapping outputs. Section "2. Kernel innovation" (unified kernel execution) carried over
+ * to GEMVs that share x.
+ *   descs        HOST array of count descriptors, 1 <= count <= UBW_MAX_GROUP
+ *   K, g, x, x_dtype, batch, accumulate   shared by all, as ubw_lut_gemv
+ * Errors: UBW_EINVAL (count out of range, null descs, or any desc invalid as in the single
+ *         calls), otherwise as ubw_lut_gemv.
+ */
+int ubw_lut_gemv_multi(const ubw_gemv_desc* descs, int count, int64_t K, int g, const void* x,
+                       int x_dtype, int batch, int accumulate, void* stream);
 
 /*
  * Host-side check of a salient index list: every idx[q] in [0, K) and strictly ascending.

@@ -125,6 +125,65 @@ def test_refined_rejects():
         assert L.ubw_lut_gemv_refined(*a.values()) == status, kw
 
 
+def multi_desc(**kw):
+    d = ubw.GemvDesc()
+    vals = dict(packed=FAKE.value, alpha_r=FAKE.value, alpha_c=FAKE.value, nb=2, idx=None, s=0, packed_s=None,
+                alpha_r_s=None, alpha_c_s=None, ns=0, N=64, y=FAKE.value, workspace=None, ws_bytes=0)
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(d, k, v)
+    return d
+
+
+def multi_call(descs, K=64, g=8, x=FAKE, x_dtype=1, batch=1):
+    arr = (ubw.GemvDesc * max(1, len(descs)))(*descs)
+    return ubw.lib().ubw_lut_gemv_multi(arr, len(descs), K, g, x, x_dtype, batch, 0, None)
+
+
+def test_multi_rejects():
+    L = ubw.lib()
+    ok = multi_desc()
+    assert L.ubw_lut_gemv_multi(None, 1, 64, 8, FAKE, 1, 1, 0, None) == EINVAL       # null descs
+    assert multi_call([]) == EINVAL                                                   # count 0
+    assert multi_call([multi_desc(y=0x10000 + 256 * i) for i in range(9)]) == EINVAL   # count > UBW_MAX_GROUP
+    assert multi_call([ok], g=4) == EUNSUP
+    assert multi_call([ok], K=0) == EINVAL
+    assert multi_call([ok], x=None) == EINVAL
+    assert multi_call([ok], x_dtype=7) == EUNSUP
+    assert multi_call([ok], batch=17) == EINVAL
+    assert multi_call([ok, multi_desc()]) == EINVAL                                   # same y twice
+    ws = 0x20000
+    assert multi_call([multi_desc(workspace=ws, ws_bytes=4096),
+                       multi_desc(y=0x30000, workspace=ws, ws_bytes=4096)]) == EINVAL  # shared workspace
+    # the second desc is the bad one: every desc is checked before anything is enqueued
+    for kw, status in [(dict(packed=None), EINVAL), (dict(nb=0), EINVAL), (dict(N=0), EINVAL),
+                       (dict(packed=MISALIGNED.value), EALIGN), (dict(workspace=FAKE.value, ws_bytes=8), ESIZE),
+                       (dict(workspace=MISALIGNED.value, ws_bytes=4096), EALIGN),
+                       (dict(idx=FAKE.value, s=0, packed_s=FAKE.value, alpha_r_s=FAKE.value,
+                             alpha_c_s=FAKE.value, ns=2), EINVAL),
+                       (dict(idx=FAKE.value, s=10, packed_s=None, alpha_r_s=FAKE.value,
+                             alpha_c_s=FAKE.value, ns=2), EINVAL),
+                       (dict(idx=FAKE.value, s=10, packed_s=MISALIGNED.value, alpha_r_s=FAKE.value,
+                             alpha_c_s=FAKE.value, ns=2), EALIGN),
+                       (dict(idx=FAKE.value, s=10, packed_s=FAKE.value, alpha_r_s=FAKE.value,
+                             alpha_c_s=FAKE.value, ns=0), EINVAL)]:
+        bad = multi_desc(y=0x30000, **kw)
+        assert multi_call([ok, bad]) == status, kw
+
+
+def test_gemv_desc_layout():
+    # the binding's struct mirrors ubw_gemv_desc field for field (LP64 layout)
+    offs = [(f, getattr(ubw.GemvDesc, f).offset) for f, _ in ubw.GemvDesc._fields_]
+    assert offs == [("packed", 0), ("alpha_r", 8), ("alpha_c", 16), ("nb", 24), ("idx", 32), ("s", 40),
+                    ("packed_s", 48), ("alpha_r_s", 56), ("alpha_c_s", 64), ("ns", 72), ("N", 80), ("y", 88),
+                    ("workspace", 96), ("ws_bytes", 104)]
+    assert ctypes.sizeof(ubw.GemvDesc) == 112
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct ubw_gemv_desc \{(.*?)\} ubw_gemv_desc;", text, re.S).group(1)
+    names = re.findall(r"(\w+);", body)
+    assert names == [f for f, _ in ubw.GemvDesc._fields_]
+
+
 def test_other_entry_points_reject():
     L = ubw.lib()
     assert L.ubw_pack_bases(None, 0, 1, 8, 8, 8, FAKE, None) == EINVAL

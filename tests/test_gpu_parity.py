@@ -427,3 +427,98 @@ def test_config5_full_sampled():
             y = gpu_gemv(gb)[:, rows]
             r = oracle_gemv(sampled_rows(gb, rows))
             assert max_rel_err(y, r) <= TOL, (g.name, b)
+
+
+# ------------------------------------------------------------------------------------------
+# grouped launches: several GEMVs on one x in one launch
+
+def multi_entry(g, ws=True, y=None):
+    e = dict(packed=pack(g.bits, g.k), alpha_r=dev(g.alpha_r), alpha_c=dev(g.alpha_c), n=g.n,
+             y=torch.full((g.batch, g.n), float("nan"), device=DEV) if y is None else y)
+    if g.s:
+        e.update(idx=dev(g.idx), packed_s=pack(g.bits_s, g.s), alpha_r_s=dev(g.alpha_r_s),
+                 alpha_c_s=dev(g.alpha_c_s))
+    if ws:
+        e["workspace"] = ubw.workspace(g.n, DEV)
+    return e
+
+
+def shared_x(gs, x):
+    for g in gs:
+        g.x = x
+    return gs
+
+
+@pytest.mark.parametrize("batch", [1, 3, 16])
+def test_multi_integer_exact(batch):
+    """Mixed GEMVs (row counts from 5 to 1100, 1 to 3 bases, with and without refinement) on one
+    x: every output exact, written over NaN or added to, with and without workspaces."""
+    rng = np.random.default_rng(300 + batch)
+    k = 1504   # fp16 x of 3008 bytes: the refinement gather goes through LDS at batch 1
+    gs = [make_integer_gemv(rng, 700, k, 2, s=70, ns=1, batch=batch),
+          make_integer_gemv(rng, 300, k, 1, batch=batch),
+          make_integer_gemv(rng, 1100, k, 3, s=150, ns=2, batch=batch),
+          make_integer_gemv(rng, 5, k, 2, s=3, ns=1, batch=batch)]
+    shared_x(gs, rng.integers(-8, 9, size=(batch, k)).astype(np.float16))
+    ref = [oracle_gemv(g) for g in gs]
+    x = dev(gs[0].x)
+    for ws in (True, False):
+        es = [multi_entry(g, ws=ws) for g in gs]
+        outs = ubw.lut_gemv_multi(es, x, k)
+        for i, (o, r) in enumerate(zip(outs, ref)):
+            assert np.array_equal(host(o).astype(np.float64), r), (i, ws)
+        for e in es:
+            if ws:
+                assert host(e["workspace"])[0] == 0
+        y0 = [rng.integers(-50, 50, (batch, g.n)).astype(np.float32) for g in gs]
+        for e, a in zip(es, y0):
+            e["y"] = dev(a)
+        outs = ubw.lut_gemv_multi(es, x, k, accumulate=True)
+        for i, (o, r, a) in enumerate(zip(outs, ref, y0)):
+            assert np.array_equal(host(o).astype(np.float64), r + a), (i, ws, "accumulate")
+
+
+def test_multi_eight_gemvs_and_workspace_reuse():
+    """UBW_MAX_GROUP GEMVs in one call, then the same workspaces in single calls and a second
+    grouped call: the row-group counters stay consistent across calls of both kinds."""
+    rng = np.random.default_rng(17)
+    k = 777
+    gs = [make_integer_gemv(rng, n, k, 1 + i % 3, s=(40 if i % 2 else 0), ns=(1 + i % 2 if i % 2 else 0))
+          for i, n in enumerate((64, 1, 513, 256, 257, 900, 33, 1300))]
+    shared_x(gs, rng.integers(-8, 9, size=(1, k)).astype(np.float16))
+    ref = [oracle_gemv(g) for g in gs]
+    x = dev(gs[0].x)
+    es = [multi_entry(g) for g in gs]
+    for rep in range(3):
+        outs = ubw.lut_gemv_multi(es, x, k)
+        for i, (o, r) in enumerate(zip(outs, ref)):
+            assert np.array_equal(host(o).astype(np.float64), r), (rep, i)
+        for g, e in zip(gs, es):   # single calls on the same workspaces in between
+            assert np.array_equal(gpu_gemv(g, packed=e["packed"], ws=e["workspace"]), oracle_gemv(g))
+    for e in es:
+        assert host(e["workspace"])[0] == 0
+
+
+def test_multi_single_gemv_matches_single_call():
+    rng = np.random.default_rng(23)
+    g = make_integer_gemv(rng, 1000, 3000, 3, s=150, ns=2, batch=1)
+    out = ubw.lut_gemv_multi([multi_entry(g)], dev(g.x), g.k)[0]
+    assert np.array_equal(host(out).astype(np.float64), oracle_gemv(g))
+
+
+def test_multi_config5_sampled():
+    """70B-shaped q/k/v and gate/up groups on one shared fp16 x each (batch 1 and 16): sampled
+    rows against the oracle within the float tolerance."""
+    wl = config5()
+    by = {g.name: g for g in wl.gemvs}
+    rng = np.random.default_rng(56)
+    for names in (("q", "k", "v"), ("gate", "up")):
+        gs = shared_x([by[nm] for nm in names], by[names[0]].x)
+        for b in wl.batches:
+            gb = [g.with_batch(b) for g in gs]
+            es = [multi_entry(g) for g in gb]
+            outs = ubw.lut_gemv_multi(es, dev(gb[0].x), gb[0].k)
+            for g, o in zip(gb, outs):
+                rows = np.sort(rng.choice(g.n, size=min(g.n, 256), replace=False))
+                r = oracle_gemv(sampled_rows(g, rows))
+                assert max_rel_err(host(o).astype(np.float64)[:, rows], r) <= TOL, (g.name, b)

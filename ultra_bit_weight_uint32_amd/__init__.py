@@ -21,13 +21,25 @@ UBW_OK = 0
 UBW_F32, UBW_F16 = 0, 1
 UBW_SRC_CANON_BITS, UBW_SRC_INT8_SIGNS = 0, 1
 MAX_BATCH = 16
+MAX_GROUP = 8
 
 # every symbol include/ubw.h declares
 EXPORTS = (
     "ubw_status_str", "ubw_version", "ubw_packed_words", "ubw_pack_bases", "ubw_ternary_encode",
     "ubw_build_lut", "ubw_workspace_bytes", "ubw_lut_gemv", "ubw_vcm_gather_refine", "ubw_lut_gemv_refined",
     "ubw_check_indices", "ubw_extract_patterns", "ubw_lut_gemv_geometry", "ubw_bench_stream_read",
+    "ubw_lut_gemv_multi",
 )
+
+
+class GemvDesc(ctypes.Structure):
+    """Mirror of ubw_gemv_desc (include/ubw.h)."""
+    _fields_ = [
+        ("packed", ctypes.c_void_p), ("alpha_r", ctypes.c_void_p), ("alpha_c", ctypes.c_void_p), ("nb", ctypes.c_int),
+        ("idx", ctypes.c_void_p), ("s", ctypes.c_int64), ("packed_s", ctypes.c_void_p),
+        ("alpha_r_s", ctypes.c_void_p), ("alpha_c_s", ctypes.c_void_p), ("ns", ctypes.c_int), ("N", ctypes.c_int64),
+        ("y", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+    ]
 
 
 class UbwError(RuntimeError):
@@ -63,6 +75,7 @@ def lib():
         "ubw_lut_gemv_refined": ([P, P, P, I, P, I64, P, P, P, I, I64, I64, I, P, I, I, P, I, P, SZ, P], I),
         "ubw_lut_gemv_geometry": ([P, P, P, I, I64, I64, P, I64, P, I, I, P, I, I, I, I, P, SZ, P], I),
         "ubw_bench_stream_read": ([P, I64, P, P], I),
+        "ubw_lut_gemv_multi": ([ctypes.POINTER(GemvDesc), I, I64, I, P, I, I, I, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -285,6 +298,58 @@ def lut_gemv_refined(packed, alpha_r, alpha_c, idx, packed_s, alpha_r_s, alpha_c
                                       _xdtype(x), batch, _dev(y, "y", F32), 1 if accumulate else 0, ws, wsb,
                                       _stream()))
     return y
+
+
+def lut_gemv_multi(gemvs, x, k: int, g: int = 8, accumulate: bool = False):
+    """Several GEMVs on the same x in one launch. `gemvs` is a list of dicts with keys packed,
+    alpha_r, alpha_c, n, y and optionally idx, packed_s, alpha_r_s, alpha_c_s (refinement) and
+    workspace; each y is [batch, n] fp32 (written, or added to with accumulate=True). Returns the
+    list of outputs."""
+    torch = _torch()
+    x = _as_2d(x)
+    batch = x.shape[0]
+    if not 1 <= len(gemvs) <= MAX_GROUP:
+        raise ValueError(f"1 to {MAX_GROUP} GEMVs per call")
+    if x.shape[1] != k:
+        raise ValueError("x must have k columns")
+    F32 = (torch.float32,)
+    descs = (GemvDesc * len(gemvs))()
+    outs = []
+    for d, G in zip(descs, gemvs):
+        n = G["n"]
+        nb = G["alpha_r"].shape[0]
+        if tuple(G["alpha_r"].shape) != (nb, n) or tuple(G["alpha_c"].shape) != (nb, k):
+            raise ValueError("shape mismatch between alpha_r, alpha_c and (n, k)")
+        if G["packed"].numel() < packed_words(nb, n, k, g):
+            raise ValueError("packed buffer smaller than packed_words()")
+        y = G["y"]
+        if tuple(y.shape) != (batch, n):
+            raise ValueError(f"y must be [{batch}, {n}]")
+        d.packed = _dev(G["packed"], "packed", _words_dtypes()).value
+        d.alpha_r = _dev(G["alpha_r"], "alpha_r", F32).value
+        d.alpha_c = _dev(G["alpha_c"], "alpha_c", F32).value
+        d.nb = nb
+        if G.get("idx") is not None:
+            s, ns = G["idx"].shape[0], G["alpha_r_s"].shape[0]
+            if tuple(G["alpha_r_s"].shape) != (ns, n) or tuple(G["alpha_c_s"].shape) != (ns, s):
+                raise ValueError("shape mismatch between idx, alpha_r_s, alpha_c_s and n")
+            if G["packed_s"].numel() < packed_words(ns, n, s, g):
+                raise ValueError("packed_s buffer smaller than packed_words()")
+            d.idx = _dev(G["idx"], "idx", (torch.int32,)).value
+            d.s = s
+            d.packed_s = _dev(G["packed_s"], "packed_s", _words_dtypes()).value
+            d.alpha_r_s = _dev(G["alpha_r_s"], "alpha_r_s", F32).value
+            d.alpha_c_s = _dev(G["alpha_c_s"], "alpha_c_s", F32).value
+            d.ns = ns
+        d.N = n
+        d.y = _dev(y, "y", F32).value
+        w, d.ws_bytes = _ws(G.get("workspace"))
+        d.workspace = w.value if w is not None else None
+        outs.append(y)
+    _check("ubw_lut_gemv_multi",
+           lib().ubw_lut_gemv_multi(descs, len(gemvs), k, g, _dev(x, "x", None), _xdtype(x), batch,
+                                    1 if accumulate else 0, _stream()))
+    return outs
 
 
 def check_indices(idx_host, k: int) -> None:

@@ -11,7 +11,7 @@ using namespace ubw;
 
 namespace {
 
-constexpr int kVersion = 2;
+constexpr int kVersion = 3;
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -201,6 +201,43 @@ int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const flo
     a.seg[1] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
     a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(K, nb) + units_of(s, ns), batch);
     return run_step(a, stream);
+}
+
+int ubw_lut_gemv_multi(const ubw_gemv_desc* descs, int count, int64_t K, int g, const void* x, int x_dtype,
+                       int batch, int accumulate, void* stream) {
+    if (!descs || count < 1 || count > UBW_MAX_GROUP || !fits_int(K)) return UBW_EINVAL;
+    if (g != 8) return UBW_EUNSUPPORTED;
+    StepArgs args[UBW_MAX_GROUP];
+    int64_t units = 0, NTmax = 0;
+    for (int i = 0; i < count; ++i) {
+        const ubw_gemv_desc& d = descs[i];
+        int st = validate_gemv_common(d.packed, d.alpha_r, d.alpha_c, d.nb, d.N, K, x, x_dtype, batch, d.y);
+        if (st != UBW_OK) return st;
+        if (d.idx && (st = validate_gemv_common(d.packed_s, d.alpha_r_s, d.alpha_c_s, d.ns, d.N, d.s, x, x_dtype,
+                                                batch, d.y)) != UBW_OK)
+            return st;
+        uint32_t* ws = nullptr;
+        if ((st = check_workspace(d.workspace, d.ws_bytes, d.N, &ws)) != UBW_OK) return st;
+        for (int j = 0; j < i; ++j)  // one output and one workspace per GEMV
+            if (descs[j].y == d.y || (ws && descs[j].workspace == d.workspace)) return UBW_EINVAL;
+        StepArgs a = make_step(d.N, x, x_dtype, K, batch, d.y, accumulate, ws);
+        a.seg[0] = make_segment(d.packed, d.alpha_r, d.alpha_c, nullptr, d.nb, K);
+        a.nseg = 1;
+        int64_t u = units_of(K, d.nb);
+        if (d.idx) {
+            a.nseg = 2;
+            a.seg[1] = make_segment(d.packed_s, d.alpha_r_s, d.alpha_c_s, d.idx, d.ns, d.s);
+            u += units_of(d.s, d.ns);
+        }
+        if (!step_buffers_fit(a)) return UBW_EUNSUPPORTED;
+        args[i] = a;
+        units += ceil_div(d.N, kTileRows) * u;
+        NTmax = ceil_div(d.N, kTileRows) > NTmax ? ceil_div(d.N, kTileRows) : NTmax;
+    }
+    // one row-tile count for all: as for a single GEMV, over the group's total units per tile row
+    const int rpl = choose_rows(NTmax, (units + NTmax - 1) / NTmax, batch);
+    for (int i = 0; i < count; ++i) args[i].rows_per_group = rpl;
+    return hip_status(launch_step_group(args, count, as_stream(stream)));
 }
 
 int ubw_check_indices(const int32_t* idx_host, int64_t s, int64_t K) {

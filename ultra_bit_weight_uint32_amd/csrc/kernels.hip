@@ -561,12 +561,9 @@ __device__ __forceinline__ uint32_t range_start(const StepParams& P, uint32_t g)
     return g * (uint32_t)P.Q + (g < (uint32_t)P.R ? g : (uint32_t)P.R);
 }
 
-// Occupancy: the second argument is a minimum of waves per SIMD (2 lets the compiler use up to
-// 256 VGPRs); two workgroups per CU need at most 128, which the instances with one or two row
-// tiles and batch up to 4 stay within. (Asking for 4 waves per SIMD instead makes the compiler
-// issue the table lookups in smaller batches, which costs more than it gains.)
+// The body of a step: workgroup g of the P.G that work on the GEMV described by P.
 template <typename XT, int RPL, int BMAX, bool XL>
-__global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(StepParams P) {
+__device__ __forceinline__ void step_body(const StepParams& P, int g) {
     // Batches above 2 keep their per-row accumulators in thread-private LDS slots (registers
     // indexed by a runtime batch index would go to scratch).
     constexpr bool kAccLds = BMAX > 2;
@@ -603,7 +600,6 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
 #pragma unroll
     for (int i = 0; i < 8; ++i) lc[i] += 0x80808080u * (uint32_t)h;  // half h's tables: +128 bytes
 
-    const int g = blockIdx.x;
     const uint32_t x0 = range_start(P, g);
     const uint32_t x1 = range_start(P, g + 1);
     const uint32_t Um = (uint32_t)P.NRG * (uint32_t)P.US[0];  // units of segment 0
@@ -853,6 +849,32 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(Ste
     if (zpend) zero_owned();  // a workgroup without units (the host never launches one)
 }
 
+
+// Occupancy: the second argument is a minimum of waves per SIMD (2 lets the compiler use up to
+// 256 VGPRs); two workgroups per CU need at most 128, which the instances with one or two row
+// tiles and batch up to 4 stay within. (Asking for 4 waves per SIMD instead makes the compiler
+// issue the table lookups in smaller batches, which costs more than it gains.)
+template <typename XT, int RPL, int BMAX, bool XL>
+__global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(StepParams P) {
+    step_body<XT, RPL, BMAX, XL>(P, (int)blockIdx.x);
+}
+
+// Several GEMVs sharing x in one launch: GEMV i gets workgroups [start[i], start[i + 1]) and
+// runs the same body on them.
+struct GroupParams {
+    int count;
+    int start[kMaxGroup + 1];
+    StepParams p[kMaxGroup];
+};
+
+template <typename XT, int RPL, int BMAX, bool XL>
+__global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8_group(GroupParams GP) {
+    const int b = (int)blockIdx.x;
+    int i = 0;
+    while (i + 1 < GP.count && b >= GP.start[i + 1]) ++i;
+    step_body<XT, RPL, BMAX, XL>(GP.p[i], b - GP.start[i]);
+}
+
 // ---------------------------------------------------------------------------------------
 // Streaming read with the GEMV's access shape (measurement helper).
 
@@ -931,23 +953,48 @@ hipError_t launch_extract(const uint32_t* packed, int nb, int N, int K, int g, u
     return hipGetLastError();
 }
 
-// Workgroups of this instance that the device can hold at once (occupancy x CUs), cached.
-template <typename XT, int RPL, int BMAX, bool XL>
-static int64_t resident_capacity() {
-    static int64_t cap = -1;  // benign race: every thread computes the same value
-    if (cap < 0) {
+// Workgroups of a kernel instance that the device can hold at once (occupancy x CUs), cached.
+template <typename Kernel>
+static int64_t capacity_of(Kernel k, int64_t& cache) {
+    if (cache < 0) {  // benign race: every thread computes the same value
         int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv8<XT, RPL, BMAX, XL>, kStepThreads, 0) !=
-                hipSuccess)
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kStepThreads, 0) != hipSuccess)
             return 0;
-        cap = (int64_t)cus * per_cu;
+        cache = (int64_t)cus * per_cu;
     }
-    return cap;
+    return cache;
+}
+template <typename XT, int RPL, int BMAX, bool XL>
+static int64_t resident_capacity() {
+    static int64_t cap = -1;
+    return capacity_of(k_gemv8<XT, RPL, BMAX, XL>, cap);
+}
+template <typename XT, int RPL, int BMAX, bool XL>
+static int64_t resident_capacity_group() {
+    static int64_t cap = -1;
+    return capacity_of(k_gemv8_group<XT, RPL, BMAX, XL>, cap);
 }
 
-static inline bool a_ws_missing(const StepParams& P) { return P.a.ws == nullptr; }
+// Split of P's units over G workgroups and the final output mode; zero-fills y first when the
+// single-launch protocol cannot be used (no workspace, or too many units per row group).
+static hipError_t finish_params(StepParams& P, int64_t G, hipStream_t s) {
+    P.G = (int)G;
+    P.Q = P.U / P.G;
+    P.R = P.U - P.Q * P.G;
+    // every workgroup holds exactly one whole row group (one segment only: a refinement
+    // segment's units of a row group sit in another part of the list): plain stores
+    const bool whole_rows = P.G == P.NRG && P.US[1] == 0;
+    if (P.mode == kModeFirst && whole_rows) P.mode = kModeStore;
+    // the arrival field counts a row group's units (Urg) and must not overflow into the generation
+    if (P.mode == kModeFirst && (P.a.ws == nullptr || P.Urg + 1 > (int)kArrMask)) {
+        hipError_t e = launch_fill_zero(P.a.y, (int64_t)P.a.batch * P.a.N, s);
+        if (e != hipSuccess) return e;
+        P.mode = kModeAtomic;
+    }
+    return hipSuccess;
+}
 
 template <typename XT, int RPL, int BMAX, bool XL>
 static hipError_t launch_step_t(StepParams P, hipStream_t s) {
@@ -957,46 +1004,76 @@ static hipError_t launch_step_t(StepParams P, hipStream_t s) {
     int64_t G = P.a.workgroups > 0 ? P.a.workgroups : cap;
     G = G < cap ? G : cap;
     G = G < P.U ? G : P.U;
-    P.G = (int)G;
-    P.Q = P.U / P.G;
-    P.R = P.U - P.Q * P.G;
-    // every workgroup holds exactly one whole row group (one segment only: a refinement
-    // segment's units of a row group sit in another part of the list): plain stores
-    const bool whole_rows = P.G == P.NRG && P.US[1] == 0;
-    if (P.mode == kModeFirst && whole_rows) P.mode = kModeStore;
-    // the arrival field counts a row group's units (Urg) and must not overflow into the generation
-    if (P.mode == kModeFirst && (a_ws_missing(P) || P.Urg + 1 > (int)kArrMask)) {
-        hipError_t e = launch_fill_zero(P.a.y, (int64_t)P.a.batch * P.a.N, s);
-        if (e != hipSuccess) return e;
-        P.mode = kModeAtomic;
-    }
+    hipError_t e = finish_params(P, G, s);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_gemv8<XT, RPL, BMAX, XL>), dim3((unsigned)P.G), dim3(kStepThreads), 0, s, P);
     return hipGetLastError();
 }
 
-// Instances: (row tiles per workgroup, batch bound) pairs whose registers fit without spills;
-// max_rows_per_group() is the host-side rule that keeps requests inside this set.
-template <typename XT>
-static hipError_t launch_step_x(const StepParams& P, int rpl, hipStream_t s) {
-    const int batch = P.a.batch;
-    // the gather of a refinement segment goes through LDS when the activation block fits (in
-    // whole 16-byte pieces, so that no load straddles the end of x)
-    const uint64_t xbytes = (uint64_t)batch * (uint64_t)P.a.ldx * sizeof(XT);
-    const bool xl = P.US[1] > 0 && xbytes <= kXlBytes && xbytes % 16 == 0;
+// Grouped launch: the workgroups the device holds at once (at most the total units) are shared
+// out in proportion to each GEMV's units, at least one each.
+template <typename XT, int RPL, int BMAX, bool XL>
+static hipError_t launch_group_t(GroupParams GP, hipStream_t s) {
+    const int64_t cap = resident_capacity_group<XT, RPL, BMAX, XL>();
+    if (cap < GP.count) return hipErrorInvalidConfiguration;
+    int64_t Ut = 0;
+    for (int i = 0; i < GP.count; ++i) Ut += GP.p[i].U;
+    const int64_t Gt = Ut < cap ? Ut : cap;
+    int64_t Gi[kMaxGroup], sum = 0;
+    for (int i = 0; i < GP.count; ++i) {
+        Gi[i] = Gt * GP.p[i].U / Ut;
+        Gi[i] = Gi[i] < 1 ? 1 : (Gi[i] > GP.p[i].U ? GP.p[i].U : Gi[i]);
+        sum += Gi[i];
+    }
+    while (sum > Gt) {  // the minimum of one each can overshoot: take from the largest share
+        int j = 0;
+        for (int i = 1; i < GP.count; ++i) j = Gi[i] > Gi[j] ? i : j;
+        --Gi[j];
+        --sum;
+    }
+    for (int i = 0; i < GP.count && sum < Gt; ++i) {  // hand out what rounding left over
+        const int64_t add = Gt - sum < GP.p[i].U - Gi[i] ? Gt - sum : GP.p[i].U - Gi[i];
+        Gi[i] += add;
+        sum += add;
+    }
+    GP.start[0] = 0;
+    for (int i = 0; i < GP.count; ++i) {
+        hipError_t e = finish_params(GP.p[i], Gi[i], s);
+        if (e != hipSuccess) return e;
+        GP.start[i + 1] = GP.start[i] + (int)Gi[i];
+    }
+    hipLaunchKernelGGL((k_gemv8_group<XT, RPL, BMAX, XL>), dim3((unsigned)GP.start[GP.count]), dim3(kStepThreads), 0,
+                       s, GP);
+    return hipGetLastError();
+}
+
+// Instances: (row tiles per workgroup, batch bound, refinement gather through LDS) choices whose
+// registers fit without spills; max_rows_per_group() is the host-side rule that keeps requests
+// inside this set. f(XT, RPL, BMAX, XL) is called with the chosen instance's parameters.
+template <typename XT, typename F>
+static hipError_t dispatch_instance(int batch, int rpl, bool xl, F f) {
+    using std::integral_constant;
     if (batch <= 1) {
         if (xl) {
-            if (rpl >= 4) return launch_step_t<XT, 4, 1, true>(P, s);
-            if (rpl >= 2) return launch_step_t<XT, 2, 1, true>(P, s);
-            return launch_step_t<XT, 1, 1, true>(P, s);
+            if (rpl >= 4) return f(XT{}, integral_constant<int, 4>{}, integral_constant<int, 1>{}, std::true_type{});
+            if (rpl >= 2) return f(XT{}, integral_constant<int, 2>{}, integral_constant<int, 1>{}, std::true_type{});
+            return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 1>{}, std::true_type{});
         }
-        if (rpl >= 4) return launch_step_t<XT, 4, 1, false>(P, s);
-        if (rpl >= 2) return launch_step_t<XT, 2, 1, false>(P, s);
-        return launch_step_t<XT, 1, 1, false>(P, s);
+        if (rpl >= 4) return f(XT{}, integral_constant<int, 4>{}, integral_constant<int, 1>{}, std::false_type{});
+        if (rpl >= 2) return f(XT{}, integral_constant<int, 2>{}, integral_constant<int, 1>{}, std::false_type{});
+        return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 1>{}, std::false_type{});
     }
-    if (batch <= 2) return launch_step_t<XT, 1, 2, false>(P, s);
-    if (batch <= 4) return launch_step_t<XT, 1, 4, false>(P, s);
-    if (batch <= 8) return launch_step_t<XT, 1, 8, false>(P, s);
-    return launch_step_t<XT, 1, 16, false>(P, s);
+    if (batch <= 2) return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 2>{}, std::false_type{});
+    if (batch <= 4) return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 4>{}, std::false_type{});
+    if (batch <= 8) return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 8>{}, std::false_type{});
+    return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 16>{}, std::false_type{});
+}
+
+// The gather of a refinement segment goes through LDS when the activation block fits (in whole
+// 16-byte pieces, so that no load straddles the end of x).
+static bool gather_in_lds(const StepArgs& a) {
+    const uint64_t xbytes = (uint64_t)a.batch * (uint64_t)a.ldx * (a.x_dtype == UBW_F16 ? 2u : 4u);
+    return xbytes <= kXlBytes && xbytes % 16 == 0;
 }
 
 int max_rows_per_group(int batch) { return batch <= 1 ? 4 : 1; }
@@ -1015,8 +1092,9 @@ bool step_buffers_fit(const StepArgs& a) {
     return true;
 }
 
-hipError_t launch_step(const StepArgs& a, hipStream_t s) {
-    StepParams P{};
+// Everything of a GEMV's parameters except its workgroup split and final mode.
+static hipError_t make_params(const StepArgs& a, StepParams& P) {
+    P = StepParams{};
     P.a = a;
     const int rpl = a.rows_per_group;
     P.NT = (int)ceil_div(a.N, kTileRows);
@@ -1043,8 +1121,42 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s) {
     if (P.Urg == 0) return hipErrorInvalidValue;
     P.U = P.NRG * P.Urg;
     P.mode = a.accumulate ? kModeAtomic : kModeFirst;
-    if (a.x_dtype == UBW_F16) return launch_step_x<__half>(P, rpl, s);
-    return launch_step_x<float>(P, rpl, s);
+    return hipSuccess;
+}
+
+hipError_t launch_step(const StepArgs& a, hipStream_t s) {
+    StepParams P;
+    hipError_t e = make_params(a, P);
+    if (e != hipSuccess) return e;
+    const bool xl = P.US[1] > 0 && gather_in_lds(a);
+    auto go = [&](auto xt, auto rpl_c, auto bmax_c, auto xl_c) {
+        return launch_step_t<decltype(xt), decltype(rpl_c)::value, decltype(bmax_c)::value, decltype(xl_c)::value>(P, s);
+    };
+    if (a.x_dtype == UBW_F16) return dispatch_instance<__half>(a.batch, a.rows_per_group, xl, go);
+    return dispatch_instance<float>(a.batch, a.rows_per_group, xl, go);
+}
+
+// Several GEMVs that share x, batch, dtype and rows_per_group, in one launch.
+hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
+    GroupParams GP{};
+    GP.count = count;
+    bool any_refine = false, lds_ok = true;
+    for (int i = 0; i < count; ++i) {
+        if (a[i].x != a[0].x || a[i].batch != a[0].batch || a[i].x_dtype != a[0].x_dtype ||
+            a[i].ldx != a[0].ldx || a[i].rows_per_group != a[0].rows_per_group)
+            return hipErrorInvalidValue;
+        hipError_t e = make_params(a[i], GP.p[i]);
+        if (e != hipSuccess) return e;
+        any_refine = any_refine || GP.p[i].US[1] > 0;
+        lds_ok = lds_ok && gather_in_lds(a[i]);
+    }
+    const bool xl = any_refine && lds_ok;
+    auto go = [&](auto xt, auto rpl_c, auto bmax_c, auto xl_c) {
+        return launch_group_t<decltype(xt), decltype(rpl_c)::value, decltype(bmax_c)::value, decltype(xl_c)::value>(GP, s);
+    };
+    if (a[0].x_dtype == UBW_F16) return dispatch_instance<__half>(a[0].batch, a[0].rows_per_group, xl, go);
+    return dispatch_instance<float>(a[0].batch, a[0].rows_per_group, xl, go);
 }
 
 }  // namespace ubw

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/ubw.h"
+
 namespace ubw {
 
 constexpr int kTileRows = 256;
@@ -27,6 +29,7 @@ constexpr int kSliceWords = 8;
 constexpr int kSliceCols = 256;
 constexpr int kTileWords = kTileRows * kSliceWords;  // 2048 words = 8 KiB per base per tile
 constexpr int kThreads = 256;
+constexpr int kMaxGroup = UBW_MAX_GROUP;  // GEMVs per grouped launch
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -74,6 +77,8 @@ hipError_t launch_build_lut(const void* x, int x_dtype, int batch, const float* 
                             int g, float* lut, hipStream_t s);
 hipError_t launch_extract(const uint32_t* packed, int nb, int N, int K, int g, uint16_t* out, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, hipStream_t s);
+// Several steps sharing x (same x, batch, dtype, rows_per_group) in one launch.
+hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s);
 // Whether every buffer of a step is small enough for the kernel's 32-bit buffer offsets.
 bool step_buffers_fit(const StepArgs& a);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
