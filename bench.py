@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs", action="store_true",
                     help="instead of the headline line: time every GEMV and layer of the 7B MLP (config 4) and the "
-                         "70B layer (config 5) at their batches, same protocol, one JSON line each")
+                         "70B layer (config 5) at their batches, and the group-scale variant, same protocol, one JSON line each")
     ap.add_argument("--profile-run", action="store_true",
                     help="for hardware-counter runs: a 64 MiB device copy (known bytes, to scale the counters) "
                          "then --steps cold steps; prints one line, no timing")
@@ -83,6 +83,7 @@ def main():
     torch.cuda.set_device(dev)
     if args.configs:
         config_sweep(torch, ubw, dev)
+        gs_sweep(torch, ubw, dev)
         return
     wl = config3(seed=0)
     g = wl.gemvs[0]
@@ -317,6 +318,52 @@ def config_sweep(torch, ubw, dev):
             del C
             torch.cuda.empty_cache()
         del base
+        torch.cuda.empty_cache()
+
+
+def gs_sweep(torch, ubw, dev):
+    """The group-scale variant (one fp16 row scale per 128 columns) on the 7B attention
+    projection (with its refinement) and the 7B MLP up projection, batch 1, cold, one JSON line
+    each, next to the per-row call on the same data."""
+    from workloads import algorithmic_bytes, config3, config4
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a).to(dev)
+
+    rng = np.random.default_rng(5)
+    for label, g in (("7B attention projection (config 3)", config3(seed=0).gemvs[0]),
+                     ("7B MLP up (config 4)", config4(seed=0).gemvs[0].with_batch(1))):
+        cols = ubw.group_scale_cols(g.k)
+        arg = rng.uniform(0.05, 0.5, size=(g.nb, g.n, cols)).astype(np.float16)
+        base = dict(packed=ubw.pack_bases(t(g.bits), g.nb, g.n, g.k), arg=t(ubw.arrange_group_scales(arg)),
+                    ar=t(g.alpha_r), ac=t(g.alpha_c),
+                    x=t(g.x), packed_s=ubw.pack_bases(t(g.bits_s), g.ns, g.n, g.s), ar_s=t(g.alpha_r_s),
+                    ac_s=t(g.alpha_c_s), idx=t(g.idx), ws=ubw.workspace(g.n, dev))
+        size = sum(v.numel() * v.element_size() for v in base.values())
+        C = [{k: v.clone() for k, v in base.items()} for _ in range(max(2, -(-COLD_BYTES // size)))]
+        y = torch.zeros((1, g.n), device=dev)
+        per_row = algorithmic_bytes(g.n, g.k, g.nb, 1, 2, g.s, g.ns)
+        grouped = per_row - g.nb * g.n * 4 + g.nb * g.n * cols * 2   # fp16 block scales instead of fp32 per row
+
+        def launch_gs(k):
+            c = C[k % len(C)]
+            ubw.lut_gemv_gs(c["packed"], c["arg"], c["ac"], c["x"], g.n, g.k, idx=c["idx"], packed_s=c["packed_s"],
+                            alpha_r_s=c["ar_s"], alpha_c_s=c["ac_s"], y=y, workspace=c["ws"])
+
+        def launch_row(k):
+            c = C[k % len(C)]
+            ubw.lut_gemv_refined(c["packed"], c["ar"], c["ac"], c["idx"], c["packed_s"], c["ar_s"], c["ac_s"], c["x"],
+                                 g.n, g.k, y=y, workspace=c["ws"])
+
+        for name, fn, by in (("group scales (g128, fp16)", launch_gs, grouped), ("per-row scales", launch_row, per_row)):
+            for k in range(len(C)):
+                fn(k)
+            us = run_queued(torch, fn, 200) * 1e3 / 200
+            print(json.dumps({"sweep": label, "gemv": name, "batch": 1, "us": round(us, 2),
+                              "GBps": round(by / us / 1e3, 1), "pct_of_peak": round(by / us / 1e3 / PEAK_GBS * 100, 2),
+                              "algorithmic_bytes": by, "cold_copies": len(C)}), flush=True)
+        del C
         torch.cuda.empty_cache()
 
 

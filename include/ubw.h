@@ -61,6 +61,8 @@ enum { UBW_SRC_CANON_BITS = 0, UBW_SRC_INT8_SIGNS = 1 };  /* ubw_pack_bases sour
 
 /* Largest batch one GEMV call accepts. */
 #define UBW_MAX_BATCH 16
+/* columns per row scale in ubw_lut_gemv_gs */
+#define UBW_GROUP_COLS 128
 /* most GEMVs one ubw_lut_gemv_multi call takes */
 #define UBW_MAX_GROUP 8
 
@@ -186,6 +188,30 @@ int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const flo
                          int accumulate, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Group-scale variant: the row scale of the main bases varies along the row, one value per
+ * 128-column block. The technical summary's "Experimental results" (accuracy) names a
+ * "2b-s16-g128" setting without defining its fields; read here as 2 bases, 16-bit scales,
+ * groups of 128 columns:
+ * y[b][r] (+)= sum_{k<nb} sum_j alpha_rg[k][r][j / 128] * B^(k)[r][j] * alpha_c^(k)[j] * x[b][j]
+ *              + the refinement of ubw_lut_gemv_refined when idx != NULL (its row scales stay
+ *              one fp32 per row; with idx == NULL the refinement arguments are ignored).
+ *   alpha_rg     fp16 [nb][ceil(K / 256)][N][2]: element [k][t][r][h] is the scale of base k,
+ *                row r, columns 256 t + 128 h ... 256 t + 128 h + 127 (block 2 t + h), so that
+ *                the rows of one 256-column slice are contiguous. A block wholly past column K
+ *                (h = 1 of the last slice when K mod 256 is in 1..128) is padding and never used
+ *                (any value, NaN included). 4-byte aligned.
+ *   gsize        must be UBW_GROUP_COLS
+ * Everything else as ubw_lut_gemv_refined (main bases, alpha_c, x, y, accumulate, workspace).
+ * Errors: as ubw_lut_gemv_refined; gsize other than 128 is UBW_EUNSUPPORTED, an alpha_rg not
+ *         4-byte aligned UBW_EALIGN.
+ */
+int ubw_lut_gemv_gs(const uint32_t* packed, const uint16_t* alpha_rg, const float* alpha_c, int nb,
+                    int gsize, const int32_t* idx, int64_t s, const uint32_t* packed_s,
+                    const float* alpha_r_s, const float* alpha_c_s, int ns, int64_t N, int64_t K,
+                    int g, const void* x, int x_dtype, int batch, float* y, int accumulate,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * One GEMV of a grouped call: its own bases, scales, optional refinement, output and workspace.
  * All pointers are device pointers except as noted; the struct array itself is host memory.
  */
@@ -236,19 +262,20 @@ int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, i
                          uint16_t* out, void* stream);
 
 /*
- * Test and tuning export: ubw_lut_gemv (vcm = 0) or ubw_vcm_gather_refine (vcm = 1) with an
+ * Test and tuning export: ubw_lut_gemv (mode = 0), ubw_vcm_gather_refine (mode = 1) or the
+ * main bases of ubw_lut_gemv_gs (mode = 2: alpha_r is then its fp16 alpha_rg) with an
  * explicit launch geometry. The kernel walks a list of units (a unit: rows_per_group tiles of
  * 256 rows x two (256-column slice, base) items) split into equal contiguous ranges over
  * `workgroups` persistent workgroups (0 = as many as the device holds at once; larger values
  * are capped to that). rows_per_group is 1, 2 or 4 for batch 1 and 1 above (UBW_ERANGE
  * otherwise). Results equal the default geometry's up to fp32 summation
- * order. For vcm = 0, idx is ignored and Kv = K; for vcm = 1, Kv = s. workspace as
- * ubw_lut_gemv.
+ * order. For modes 0 and 2, idx is ignored and Kv = K; for mode 1, Kv = s. workspace as
+ * ubw_lut_gemv. A mode outside 0..2 is UBW_ERANGE.
  */
-int ubw_lut_gemv_geometry(const uint32_t* packed, const float* alpha_r, const float* alpha_c,
+int ubw_lut_gemv_geometry(const uint32_t* packed, const void* alpha_r, const float* alpha_c,
                           int nb, int64_t N, int64_t Kv, const int32_t* idx, int64_t K,
                           const void* x, int x_dtype, int batch, float* y, int accumulate,
-                          int vcm, int rows_per_group, int workgroups, void* workspace,
+                          int mode, int rows_per_group, int workgroups, void* workspace,
                           size_t ws_bytes, void* stream);
 
 /*

@@ -38,6 +38,8 @@ def _load():
     I = ctypes.c_int
     lib.oracle_gemv.argtypes = [P, P, P, I, I64, I64, P, I64, P, P, P, I, P, I, P]
     lib.oracle_gemv.restype = None
+    lib.oracle_gemv_gs.argtypes = [P, P, I64, I, P, I, I64, I64, P, I64, P, P, P, I, P, I, P]
+    lib.oracle_gemv_gs.restype = None
     lib.oracle_lut_gemv.argtypes = [P, P, P, I, I64, I64, P, I64, P, P, P, I, P, I, I, P]
     lib.oracle_lut_gemv.restype = None
     lib.oracle_patterns.argtypes = [P, I, I64, I64, I, P]
@@ -121,6 +123,31 @@ def gemv(bits, alpha_r, alpha_c, x, idx=None, bits_s=None, alpha_r_s=None, alpha
     _load().oracle_gemv(_ptr(bits), _ptr(alpha_r), _ptr(alpha_c), nb, n, k,
                         _ptr(idx), s, _ptr(bits_s), _ptr(alpha_r_s), _ptr(alpha_c_s), ns,
                         _ptr(x), batch, _ptr(y))
+    return y
+
+
+def gemv_gs(bits, alpha_rg, alpha_c, x, gsize=128, idx=None, bits_s=None, alpha_r_s=None, alpha_c_s=None):
+    """Group-scale variant of gemv: alpha_rg [nb, N, G] (G >= ceil(K / gsize)) holds one row
+    scale per block of gsize columns; fp16 scales are passed as their exact fp32 values.
+    Returns float64 [batch, N]."""
+    bits = _c(bits, np.uint32)
+    alpha_rg = _c(np.asarray(alpha_rg).astype(np.float32), np.float32)
+    alpha_c = _c(alpha_c, np.float32)
+    nb, n, _ = bits.shape
+    k = alpha_c.shape[1]
+    gcols = alpha_rg.shape[2]
+    assert bits.shape[2] == words_per_row(k) and alpha_c.shape == (nb, k)
+    assert alpha_rg.shape[:2] == (nb, n) and gcols >= -(-k // gsize)
+    x = _x64(x)
+    assert x.shape[1] == k
+    batch = x.shape[0]
+    idx, s, bits_s, alpha_r_s, alpha_c_s, ns = _refine_args(idx, bits_s, alpha_r_s, alpha_c_s, n)
+    if s:
+        assert idx.min() >= 0 and idx.max() < k
+    y = np.empty((batch, n), dtype=np.float64)
+    _load().oracle_gemv_gs(_ptr(bits), _ptr(alpha_rg), gcols, int(gsize), _ptr(alpha_c), nb, n, k,
+                           _ptr(idx), s, _ptr(bits_s), _ptr(alpha_r_s), _ptr(alpha_c_s), ns,
+                           _ptr(x), batch, _ptr(y))
     return y
 
 

@@ -107,6 +107,55 @@ void oracle_gemv(const uint32_t* bits, const float* alpha_r, const float* alpha_
     }
 }
 
+
+/*
+ * Group-scale variant of the same definition: the row scale of a main base varies along the
+ * row, one value per block of gsize columns (the technical summary's "Experimental results"
+ * name a "2b-s16-g128" setting; read as 2 bases, 16-bit scales, 128-column groups):
+ *
+ * W_hat[r][j] = sum_{k<nb} alpha_rg[k][r][j / gsize] * alpha_c[k][j] * B^(k)[r][j]
+ *             + the salient refinement exactly as in oracle_gemv
+ * y[b][r]     = sum_{j<K} W_hat[r][j] * x[b][j]
+ *
+ * alpha_rg: [nb][N][gcols], gcols >= ceil(K / gsize) (entries past that are not read).
+ * Other arguments as oracle_gemv.
+ */
+void oracle_gemv_gs(const uint32_t* bits, const float* alpha_rg, int64_t gcols, int gsize,
+                    const float* alpha_c, int nb, int64_t N, int64_t K,
+                    const int32_t* idx, int64_t s, const uint32_t* bits_s,
+                    const float* alpha_r_s, const float* alpha_c_s, int ns,
+                    const double* x, int batch, double* y) {
+    const int64_t kw = words_per_row(K);
+    const int64_t sw = words_per_row(s);
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < N; ++r) {
+            for (int64_t j = 0; j < K; ++j) w[j] = 0.0;
+            for (int k = 0; k < nb; ++k) {
+                const uint32_t* row = bits + ((int64_t)k * N + r) * kw;
+                const float* ar = alpha_rg + ((int64_t)k * N + r) * gcols;
+                for (int64_t j = 0; j < K; ++j)
+                    w[j] += (double)ar[j / gsize] * (double)alpha_c[(int64_t)k * K + j] * sign_at(row, j);
+            }
+            for (int k = 0; k < ns && s > 0; ++k) {
+                const uint32_t* row = bits_s + ((int64_t)k * N + r) * sw;
+                const double ar = (double)alpha_r_s[(int64_t)k * N + r];
+                for (int64_t q = 0; q < s; ++q)
+                    w[idx[q]] += ar * (double)alpha_c_s[(int64_t)k * s + q] * sign_at(row, q);
+            }
+            for (int b = 0; b < batch; ++b) {
+                const double* xb = x + (int64_t)b * K;
+                double acc = 0.0;
+                for (int64_t j = 0; j < K; ++j) acc += w[j] * xb[j];
+                y[(int64_t)b * N + r] = acc;
+            }
+        }
+        free(w);
+    }
+}
+
 /*
  * Pattern indices: for base k, row r and group gi (columns gi*g .. gi*g+g-1), the g-bit
  * number whose bit i is the sign bit of column gi*g+i. Columns >= K read as 0.

@@ -184,6 +184,28 @@ def test_gemv_desc_layout():
     assert names == [f for f, _ in ubw.GemvDesc._fields_]
 
 
+def test_gs_rejects():
+    L = ubw.lib()
+    args = dict(packed=FAKE, arg=FAKE, ac=FAKE, nb=2, gsize=128, idx=None, s=0, packed_s=None, ar_s=None, ac_s=None,
+                ns=0, N=64, K=300, g=8, x=FAKE, x_dtype=1, batch=1, y=FAKE, acc=0, ws=None, wsb=0, stream=None)
+    ref = dict(idx=FAKE, s=10, packed_s=FAKE, ar_s=FAKE, ac_s=FAKE, ns=2)
+    for kw, status in [(dict(arg=None), EINVAL), (dict(gsize=64), EUNSUP), (dict(gsize=0), EUNSUP),
+                       (dict(arg=ctypes.c_void_p(0x10002)), EALIGN), (dict(g=4), EUNSUP), (dict(nb=0), EINVAL),
+                       (dict(batch=17), EINVAL), (dict(ws=FAKE, wsb=4), ESIZE), (dict(packed=MISALIGNED), EALIGN),
+                       (dict(ref, s=0), EINVAL), (dict(ref, packed_s=None), EINVAL), (dict(ref, ns=0), EINVAL),
+                       (dict(ref, packed_s=MISALIGNED), EALIGN)]:
+        a = dict(args)
+        a.update(kw)
+        assert L.ubw_lut_gemv_gs(*a.values()) == status, kw
+    base = [FAKE, FAKE, FAKE, 2, 64, 64, None, 64, FAKE, 1, 1, FAKE, 0]
+    tail = [1, 1, None, 0, None]
+    assert L.ubw_lut_gemv_geometry(*base, 3, *tail) == ERANGE                     # mode outside 0..2
+    assert L.ubw_lut_gemv_geometry(*base, -1, *tail) == ERANGE
+    b2 = list(base)
+    b2[1] = ctypes.c_void_p(0x10002)
+    assert L.ubw_lut_gemv_geometry(*b2, 2, *tail) == EALIGN                       # group scales: 4-byte aligned
+
+
 def test_other_entry_points_reject():
     L = ubw.lib()
     assert L.ubw_pack_bases(None, 0, 1, 8, 8, 8, FAKE, None) == EINVAL
@@ -205,3 +227,18 @@ def test_check_indices_host():
         with pytest.raises(ubw.UbwError) as e:
             ubw.check_indices(np.array(bad, np.int32), 10)
         assert e.value.status == ERANGE
+
+
+def test_arrange_group_scales_layout():
+    rng = np.random.default_rng(3)
+    a = rng.uniform(0, 1, size=(2, 5, 6)).astype(np.float16)
+    d = ubw.arrange_group_scales(a)
+    assert d.shape == (2, 3, 5, 2) and d.dtype == np.float16 and d.flags.c_contiguous
+    for k in range(2):
+        for t in range(3):
+            for r in range(5):
+                for h in range(2):
+                    assert d[k, t, r, h] == a[k, r, 2 * t + h]
+    with pytest.raises(ValueError):
+        ubw.arrange_group_scales(a[:, :, :5])
+    assert [ubw.group_scale_cols(k) for k in (1, 128, 129, 256, 257, 700)] == [2, 2, 2, 2, 4, 6]

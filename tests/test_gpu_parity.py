@@ -522,3 +522,96 @@ def test_multi_config5_sampled():
                 rows = np.sort(rng.choice(g.n, size=min(g.n, 256), replace=False))
                 r = oracle_gemv(sampled_rows(g, rows))
                 assert max_rel_err(host(o).astype(np.float64)[:, rows], r) <= TOL, (g.name, b)
+
+
+# ------------------------------------------------------------------------------------------
+# group-scale variant: one fp16 row scale per 128 columns
+
+def gs_scales(rng, g, integer=True, pad_nan=True):
+    """[nb, n, 2 ceil(k/256)] fp16 block scales; padding entries (blocks past column k) NaN,
+    which the kernel must never read."""
+    cols = ubw.group_scale_cols(g.k)
+    if integer:
+        a = rng.integers(1, 4, size=(g.nb, g.n, cols)).astype(np.float16)
+    else:
+        a = rng.uniform(0.05, 0.5, size=(g.nb, g.n, cols)).astype(np.float16)
+    used = -(-g.k // 128)
+    if pad_nan and used < cols:
+        a[:, :, used:] = np.float16("nan")
+    return a
+
+
+def gpu_gs(g, arg, refine=True, y=None, accumulate=False, ws=True):
+    kw = {}
+    if refine and g.s:
+        kw = dict(idx=dev(g.idx), packed_s=pack(g.bits_s, g.s), alpha_r_s=dev(g.alpha_r_s),
+                  alpha_c_s=dev(g.alpha_c_s))
+    w = ubw.workspace(g.n, DEV) if ws else None
+    out = ubw.lut_gemv_gs(pack(g.bits, g.k), dev(ubw.arrange_group_scales(arg)), dev(g.alpha_c), dev(g.x), g.n,
+                          g.k, y=y,
+                          accumulate=accumulate, workspace=w, **kw)
+    res = host(out).astype(np.float64)
+    if w is not None:
+        assert host(w)[0] == 0
+    return res
+
+
+def oracle_gs(g, arg, refine=True):
+    kw = g.refine_kwargs() if refine else {}
+    return oracle.gemv_gs(g.bits, arg, g.alpha_c, g.x, **kw)
+
+
+GS_SHAPES = [(300, 700, 2, 0), (513, 1000, 3, 50), (256, 384, 1, 0), (100, 129, 2, 7), (1, 33, 1, 0),
+             (700, 1500, 2, 70)]
+
+
+@pytest.mark.parametrize("n,k,nb,s", GS_SHAPES)
+@pytest.mark.parametrize("batch", [1, 3, 16])
+def test_gs_integer_exact(n, k, nb, s, batch):
+    rng = np.random.default_rng(n + 3 * k + 11 * nb + batch)
+    g = make_integer_gemv(rng, n, k, nb, s=s, ns=(2 if s else 0), batch=batch)
+    arg = gs_scales(rng, g)
+    ref = oracle_gs(g, arg)
+    for ws in (True, False):
+        y = torch.full((batch, n), float("nan"), device=DEV)
+        assert np.array_equal(gpu_gs(g, arg, y=y, ws=ws), ref), ws
+    y0 = rng.integers(-50, 50, (batch, n)).astype(np.float32)
+    assert np.array_equal(gpu_gs(g, arg, y=dev(y0), accumulate=True), ref + y0)
+
+
+@pytest.mark.parametrize("rpg", [1, 2, 4])
+def test_gs_geometries_integer_exact(rpg):
+    rng = np.random.default_rng(40 + rpg)
+    n, k = 4 * 256 + 100, 6 * 256 + 77
+    for nb in (1, 2, 3):
+        g = make_integer_gemv(rng, n, k, nb, batch=1)
+        arg = gs_scales(rng, g)
+        ref = oracle_gs(g, arg)
+        for wgs in (1, 3, 7, 0):
+            y = torch.full((1, n), float("nan"), device=DEV)
+            ubw.lut_gemv_geometry(pack(g.bits, k), dev(ubw.arrange_group_scales(arg)), dev(g.alpha_c), dev(g.x), n,
+                                  k, y, rows_per_group=rpg,
+                                  workgroups=wgs, workspace=ubw.workspace(n, DEV), group_scales=True)
+            assert np.array_equal(host(y).astype(np.float64), ref), (nb, wgs)
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gs_float_tolerance(batch):
+    """7B attention projection shape with 128-column fp16 group scales and the salient
+    refinement, float scales and fp16 x, within the float tolerance."""
+    rng = np.random.default_rng(90 + batch)
+    g = make_gemv(rng, "gs", 4096, 4096, 2, s=205, ns=2, batch=batch)
+    arg = gs_scales(rng, g, integer=False)
+    assert max_rel_err(gpu_gs(g, arg), oracle_gs(g, arg)) <= TOL
+
+
+def test_gs_equal_blocks_match_plain_gemv():
+    """Equal block scales along each row: the same product as the per-row call (float)."""
+    rng = np.random.default_rng(91)
+    g = make_gemv(rng, "gs", 1000, 3000, 2, s=150, ns=1, batch=2)
+    arg = np.repeat(g.alpha_r.astype(np.float16)[:, :, None], ubw.group_scale_cols(g.k), axis=2)
+    g16 = make_gemv(rng, "gs", 1000, 3000, 2, s=150, ns=1, batch=2)
+    g16.bits, g16.alpha_c, g16.x, g16.idx = g.bits, g.alpha_c, g.x, g.idx
+    g16.bits_s, g16.alpha_r_s, g16.alpha_c_s = g.bits_s, g.alpha_r_s, g.alpha_c_s
+    g16.alpha_r = g.alpha_r.astype(np.float16).astype(np.float32)
+    assert max_rel_err(gpu_gs(g, arg), gpu_gemv(g16)) <= TOL

@@ -272,3 +272,67 @@ def test_refinement_invariants():
     x0[:, g.idx] = 0.0
     assert np.allclose(oracle.gemv(g.bits, g.alpha_r, g.alpha_c, x0, **g.refine_kwargs()),
                        oracle.gemv(g.bits, g.alpha_r, g.alpha_c, x0), rtol=1e-14, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------------
+# group-scale variant: one row scale per 128-column block
+
+def _gs_problem(rng, n, k, nb, integer):
+    gcols = 2 * ((k + 255) // 256)
+    if integer:
+        g = make_integer_gemv(rng, n, k, nb, batch=2)
+        arg = rng.integers(1, 4, size=(nb, n, gcols)).astype(np.float16)
+    else:
+        g = make_gemv(rng, "gs", n, k, nb, batch=2)
+        arg = rng.uniform(0.05, 0.5, size=(nb, n, gcols)).astype(np.float16)
+    return g, arg
+
+
+@pytest.mark.parametrize("k", [77, 128, 200, 256, 300, 700])
+def test_gs_constant_blocks_equal_plain(k):
+    """Equal scales in every block of a row reduce to the per-row definition, value for value."""
+    rng = np.random.default_rng(k)
+    g, _ = _gs_problem(rng, 21, k, 2, integer=False)
+    arg = np.repeat(g.alpha_r[:, :, None], 2 * ((k + 255) // 256), axis=2)
+    assert np.array_equal(oracle.gemv_gs(g.bits, arg, g.alpha_c, g.x), oracle.gemv(g.bits, g.alpha_r, g.alpha_c, g.x))
+
+
+@pytest.mark.parametrize("integer", [True, False])
+@pytest.mark.parametrize("k", [129, 256, 300, 700])
+def test_gs_sum_of_block_restricted_products(integer, k):
+    """The product splits over column blocks: block q alone is the per-row definition with
+    alpha_r = the block's scales and alpha_c zero outside the block. A wrong block index, a
+    dropped block or a block read from the wrong row fails this."""
+    rng = np.random.default_rng(1000 + k + integer)
+    g, arg = _gs_problem(rng, 17, k, 3, integer)
+    y = oracle.gemv_gs(g.bits, arg, g.alpha_c, g.x)
+    parts = np.zeros_like(y)
+    for q in range(-(-k // 128)):
+        ac = np.zeros_like(g.alpha_c)
+        ac[:, 128 * q:128 * (q + 1)] = g.alpha_c[:, 128 * q:128 * (q + 1)]
+        parts += oracle.gemv(g.bits, arg[:, :, q].astype(np.float32), ac, g.x)
+    if integer:
+        assert np.array_equal(y, parts)
+    else:
+        assert np.allclose(y, parts, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+
+
+def test_gs_integer_matvec_equals_numpy():
+    rng = np.random.default_rng(77)
+    k = 300
+    g, arg = _gs_problem(rng, 40, k, 2, integer=True)
+    signs = dense_signs(g.bits, k)
+    scale = np.repeat(arg.astype(np.int64), 128, axis=2)[:, :, :k]   # block scale of every column
+    w = (signs * scale).sum(axis=0)
+    assert np.array_equal(oracle.gemv_gs(g.bits, arg, g.alpha_c, g.x), (g.x.astype(np.int64) @ w.T).astype(np.float64))
+
+
+def test_gs_refinement_adds_the_same_branch():
+    rng = np.random.default_rng(78)
+    g = make_integer_gemv(rng, 30, 500, 2, s=40, ns=2, batch=2)
+    arg = rng.integers(1, 4, size=(2, 30, 4)).astype(np.float16)
+    with_ref = oracle.gemv_gs(g.bits, arg, g.alpha_c, g.x, **g.refine_kwargs())
+    without = oracle.gemv_gs(g.bits, arg, g.alpha_c, g.x)
+    branch = oracle.gemv(g.bits, g.alpha_r, g.alpha_c, g.x, **g.refine_kwargs()) - oracle.gemv(
+        g.bits, g.alpha_r, g.alpha_c, g.x)
+    assert np.array_equal(with_ref, without + branch)

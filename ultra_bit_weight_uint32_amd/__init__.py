@@ -28,7 +28,7 @@ EXPORTS = (
     "ubw_status_str", "ubw_version", "ubw_packed_words", "ubw_pack_bases", "ubw_ternary_encode",
     "ubw_build_lut", "ubw_workspace_bytes", "ubw_lut_gemv", "ubw_vcm_gather_refine", "ubw_lut_gemv_refined",
     "ubw_check_indices", "ubw_extract_patterns", "ubw_lut_gemv_geometry", "ubw_bench_stream_read",
-    "ubw_lut_gemv_multi",
+    "ubw_lut_gemv_multi", "ubw_lut_gemv_gs",
 )
 
 
@@ -76,6 +76,7 @@ def lib():
         "ubw_lut_gemv_geometry": ([P, P, P, I, I64, I64, P, I64, P, I, I, P, I, I, I, I, P, SZ, P], I),
         "ubw_bench_stream_read": ([P, I64, P, P], I),
         "ubw_lut_gemv_multi": ([ctypes.POINTER(GemvDesc), I, I64, I, P, I, I, I, P], I),
+        "ubw_lut_gemv_gs": ([P, P, P, I, I, P, I64, P, P, P, I, I64, I64, I, P, I, I, P, I, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -300,6 +301,63 @@ def lut_gemv_refined(packed, alpha_r, alpha_c, idx, packed_s, alpha_r_s, alpha_c
     return y
 
 
+GROUP_COLS = 128
+
+
+def group_scale_cols(k: int) -> int:
+    """Blocks of 128 columns per row, padded to an even count (2 * ceil(k / 256))."""
+    return 2 * ((int(k) + 255) // 256)
+
+
+def arrange_group_scales(a):
+    """Host-side layout of block scales for lut_gemv_gs: numpy [nb, n, group_scale_cols(k)]
+    (block q of row r at [k, r, q]) -> fp16 [nb, ceil(k/256), n, 2], slice-major."""
+    import numpy as np
+    a = np.asarray(a, dtype=np.float16)
+    nb, n, cols = a.shape
+    if cols % 2:
+        raise ValueError("pad the block count to an even number (group_scale_cols)")
+    return np.ascontiguousarray(a.reshape(nb, n, cols // 2, 2).transpose(0, 2, 1, 3))
+
+
+def lut_gemv_gs(packed, alpha_rg, alpha_c, x, n: int, k: int, g: int = 8, idx=None, packed_s=None, alpha_r_s=None,
+                alpha_c_s=None, y=None, accumulate: bool = False, workspace=None):
+    """Group-scale variant: alpha_rg fp16 [nb, ceil(k/256), n, 2] (arrange_group_scales) holds
+    one row scale per 128 columns; optional refinement (idx, packed_s, alpha_r_s, alpha_c_s) as
+    lut_gemv_refined. Returns y [batch, N]."""
+    torch = _torch()
+    x = _as_2d(x)
+    batch = x.shape[0]
+    nb = alpha_rg.shape[0]
+    if x.shape[1] != k or tuple(alpha_rg.shape) != (nb, (k + 255) // 256, n, 2) or tuple(alpha_c.shape) != (nb, k):
+        raise ValueError("shape mismatch between x, alpha_rg, alpha_c and (n, k)")
+    if packed.numel() < packed_words(nb, n, k, g):
+        raise ValueError("packed buffer smaller than packed_words()")
+    F32 = (torch.float32,)
+    ref = (None, 0, None, None, None, 0)
+    if idx is not None:
+        ns, s = alpha_r_s.shape[0], idx.shape[0]
+        if tuple(alpha_r_s.shape) != (ns, n) or tuple(alpha_c_s.shape) != (ns, s):
+            raise ValueError("shape mismatch between idx, alpha_r_s, alpha_c_s and n")
+        if packed_s.numel() < packed_words(ns, n, s, g):
+            raise ValueError("packed_s buffer smaller than packed_words()")
+        ref = (_dev(idx, "idx", (torch.int32,)), s, _dev(packed_s, "packed_s", _words_dtypes()),
+               _dev(alpha_r_s, "alpha_r_s", F32), _dev(alpha_c_s, "alpha_c_s", F32), ns)
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs y")
+        y = torch.empty((batch, n), dtype=torch.float32, device=x.device)
+    if tuple(y.shape) != (batch, n):
+        raise ValueError(f"y must be [{batch}, {n}]")
+    ws, wsb = _ws(workspace)
+    _check("ubw_lut_gemv_gs",
+           lib().ubw_lut_gemv_gs(_dev(packed, "packed", _words_dtypes()),
+                                 _dev(alpha_rg, "alpha_rg", (torch.float16, torch.int16)),
+                                 _dev(alpha_c, "alpha_c", F32), nb, GROUP_COLS, *ref, n, k, g, _dev(x, "x", None),
+                                 _xdtype(x), batch, _dev(y, "y", F32), 1 if accumulate else 0, ws, wsb, _stream()))
+    return y
+
+
 def lut_gemv_multi(gemvs, x, k: int, g: int = 8, accumulate: bool = False):
     """Several GEMVs on the same x in one launch. `gemvs` is a list of dicts with keys packed,
     alpha_r, alpha_c, n, y and optionally idx, packed_s, alpha_r_s, alpha_c_s (refinement) and
@@ -370,20 +428,25 @@ def extract_patterns(packed, nb: int, n: int, k: int, g: int = 8):
 
 
 def lut_gemv_geometry(packed, alpha_r, alpha_c, x, n: int, kv: int, y, *, idx=None, k=None, accumulate=False,
-                      rows_per_group=1, workgroups=0, workspace=None):
+                      rows_per_group=1, workgroups=0, workspace=None, group_scales=False):
     """Main (idx None) or refinement (idx given, k = x's row length) GEMV with an explicit
-    launch geometry; for tests and tuning."""
+    launch geometry; for tests and tuning. group_scales=True: main bases with alpha_r the fp16
+    group-scale array of lut_gemv_gs."""
     torch = _torch()
     x = _as_2d(x)
     batch = x.shape[0]
     nb = alpha_r.shape[0]
     vcm = idx is not None
+    if group_scales and (vcm or tuple(alpha_r.shape) != (nb, (kv + 255) // 256, n, 2)):
+        raise ValueError("group scales: main bases only, alpha_r [nb, ceil(k/256), n, 2] fp16")
+    mode = 1 if vcm else (2 if group_scales else 0)
+    ar_types = (torch.float16, torch.int16) if group_scales else (torch.float32,)
     _check("ubw_lut_gemv_geometry",
-           lib().ubw_lut_gemv_geometry(_dev(packed, "packed", _words_dtypes()), _dev(alpha_r, "alpha_r", (torch.float32,)),
+           lib().ubw_lut_gemv_geometry(_dev(packed, "packed", _words_dtypes()), _dev(alpha_r, "alpha_r", ar_types),
                                        _dev(alpha_c, "alpha_c", (torch.float32,)), nb, n, kv,
                                        _dev(idx, "idx", (torch.int32,)) if vcm else None, k if vcm else kv,
                                        _dev(x, "x", None), _xdtype(x), batch, _dev(y, "y", (torch.float32,)),
-                                       1 if accumulate else 0, 1 if vcm else 0, rows_per_group, workgroups,
+                                       1 if accumulate else 0, mode, rows_per_group, workgroups,
                                        *_ws(workspace), _stream()))
     return y
 

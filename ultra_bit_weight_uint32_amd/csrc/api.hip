@@ -11,7 +11,7 @@ using namespace ubw;
 
 namespace {
 
-constexpr int kVersion = 3;
+constexpr int kVersion = 4;
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -35,7 +35,7 @@ int choose_rows(int64_t NT, int64_t units_per_tile_row_group, int batch) {
 
 int64_t units_of(int64_t Kv, int nb) { return ceil_div(ceil_div(Kv, kSliceCols) * nb, 2); }
 
-int validate_gemv_common(const void* packed, const float* ar, const float* ac, int nb, int64_t N, int64_t Kv,
+int validate_gemv_common(const void* packed, const void* ar, const float* ac, int nb, int64_t N, int64_t Kv,
                          const void* x, int x_dtype, int batch, const float* y) {
     if (!packed || !ar || !ac || !x || !y) return UBW_EINVAL;
     if (nb < 1 || nb > 64 || !fits_int(N) || !fits_int(Kv)) return UBW_EINVAL;
@@ -56,7 +56,7 @@ int check_workspace(void* ws, size_t ws_bytes, int64_t N, uint32_t** out) {
     return UBW_OK;
 }
 
-Segment make_segment(const uint32_t* packed, const float* ar, const float* ac, const int32_t* idx, int nb,
+Segment make_segment(const uint32_t* packed, const void* ar, const float* ac, const int32_t* idx, int nb,
                      int64_t Kv) {
     Segment g{};
     g.packed = packed;
@@ -203,6 +203,32 @@ int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const flo
     return run_step(a, stream);
 }
 
+int ubw_lut_gemv_gs(const uint32_t* packed, const uint16_t* alpha_rg, const float* alpha_c, int nb, int gsize,
+                    const int32_t* idx, int64_t s, const uint32_t* packed_s, const float* alpha_r_s,
+                    const float* alpha_c_s, int ns, int64_t N, int64_t K, int g, const void* x, int x_dtype,
+                    int batch, float* y, int accumulate, void* workspace, size_t ws_bytes, void* stream) {
+    int st = validate_gemv_common(packed, alpha_rg, alpha_c, nb, N, K, x, x_dtype, batch, y);
+    if (st != UBW_OK) return st;
+    if (idx && (st = validate_gemv_common(packed_s, alpha_r_s, alpha_c_s, ns, N, s, x, x_dtype, batch, y)) != UBW_OK)
+        return st;
+    if (g != 8 || gsize != UBW_GROUP_COLS) return UBW_EUNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(alpha_rg) & 3u) != 0) return UBW_EALIGN;
+    uint32_t* ws = nullptr;
+    if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
+    StepArgs a = make_step(N, x, x_dtype, K, batch, y, accumulate, ws);
+    a.gs = 1;
+    a.nseg = 1;
+    a.seg[0] = make_segment(packed, alpha_rg, alpha_c, nullptr, nb, K);
+    int64_t units = units_of(K, nb);
+    if (idx) {
+        a.nseg = 2;
+        a.seg[1] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
+        units += units_of(s, ns);
+    }
+    a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units, batch);
+    return run_step(a, stream);
+}
+
 int ubw_lut_gemv_multi(const ubw_gemv_desc* descs, int count, int64_t K, int g, const void* x, int x_dtype,
                        int batch, int accumulate, void* stream) {
     if (!descs || count < 1 || count > UBW_MAX_GROUP || !fits_int(K)) return UBW_EINVAL;
@@ -257,12 +283,15 @@ int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, i
     return hip_status(launch_extract(packed, nb, (int)N, (int)K, g, out, as_stream(stream)));
 }
 
-int ubw_lut_gemv_geometry(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb, int64_t N,
+int ubw_lut_gemv_geometry(const uint32_t* packed, const void* alpha_r, const float* alpha_c, int nb, int64_t N,
                           int64_t Kv, const int32_t* idx, int64_t K, const void* x, int x_dtype, int batch,
-                          float* y, int accumulate, int vcm, int rows_per_group, int workgroups,
+                          float* y, int accumulate, int mode, int rows_per_group, int workgroups,
                           void* workspace, size_t ws_bytes, void* stream) {
     int st = validate_gemv_common(packed, alpha_r, alpha_c, nb, N, Kv, x, x_dtype, batch, y);
     if (st != UBW_OK) return st;
+    if (mode < 0 || mode > 2) return UBW_ERANGE;
+    const bool vcm = mode == 1;
+    if (mode == 2 && (reinterpret_cast<uintptr_t>(alpha_r) & 3u) != 0) return UBW_EALIGN;
     if (rows_per_group != 1 && rows_per_group != 2 && rows_per_group != 4) return UBW_ERANGE;
     if (rows_per_group > max_rows_per_group(batch)) return UBW_ERANGE;
     if (workgroups < 0) return UBW_ERANGE;
@@ -270,6 +299,7 @@ int ubw_lut_gemv_geometry(const uint32_t* packed, const float* alpha_r, const fl
     uint32_t* ws = nullptr;
     if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
     StepArgs a = make_step(N, x, x_dtype, vcm ? K : Kv, batch, y, accumulate, ws);
+    a.gs = mode == 2 ? 1 : 0;
     if (vcm) {
         a.nseg = 2;
         a.seg[1] = make_segment(packed, alpha_r, alpha_c, idx, nb, Kv);

@@ -57,33 +57,35 @@ __device__ __forceinline__ float lds_x<__half>(lds_cchar* base, uint32_t i) {
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(__half v) { return __half2float(v); }
 
-// Rotation of the lane that owns tile row rho: word rotation a and byte rotation c.
-__device__ __forceinline__ int rot_words(int rho) { return (rho & 31) >> 2; }
-__device__ __forceinline__ int rot_bytes(int rho) { return rho & 3; }
+// Order of the lane that owns tile row rho: slot s holds word s ^ a, byte jj of a slot holds
+// byte jj ^ c of that word.
+__device__ __forceinline__ int xor_words(int rho) { return (rho & 31) >> 2; }
+__device__ __forceinline__ int xor_bytes(int rho) { return rho & 3; }
+
+// Bytes of a canonical word in the order of the row that owns it: byte jj = byte jj ^ c.
+__device__ __forceinline__ uint32_t bytes_for_row(uint32_t v, int c) {
+    const uint32_t sel = 0x03020100u ^ (0x01010101u * (uint32_t)c);
+    return __builtin_amdgcn_perm(0u, v, sel);
+}
 
 // Per-lane column offsets of the 32 steps, four per register: byte jj of lc[i] is
-// 4 * ((l + 4 i + jj) mod 32), the byte offset of the group the lane reads at step 4 i + jj.
+// 4 * ((4 i + jj) ^ l), the byte offset of the group the lane reads at step 4 i + jj.
 __device__ __forceinline__ void lane_columns(int l, uint32_t lc[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         uint32_t v = 0;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) v |= (uint32_t)(4 * ((l + 4 * i + jj) & 31)) << (8 * jj);
+        for (int jj = 0; jj < 4; ++jj) v |= (uint32_t)(4 * ((4 * i + jj) ^ l)) << (8 * jj);
         lc[i] = v;
     }
 }
 
 // Address of the step 4 i + jj lookup: byte 0 = the lane's column offset for that step (byte
-// jj of lc), byte 1 = the pattern (byte jj of the aligned word A), bytes 2-3 zero. So the
-// result is 256 * pattern + 4 * group.
+// jj of lc), byte 1 = the pattern (byte jj of slot i), bytes 2-3 zero. So the result is
+// 256 * pattern + 4 * group.
 template <int JJ>
 __device__ __forceinline__ uint32_t perm_addr(uint32_t A, uint32_t lc) {
     return __builtin_amdgcn_perm(A, lc, 0x0C0C0000u | ((4u + JJ) << 8) | (uint32_t)JJ);
-}
-
-// The four patterns of steps 4i .. 4i+3 start at byte c of the slot pair (W[i], W[i+1]).
-__device__ __forceinline__ uint32_t aligned_pair(uint32_t lo, uint32_t hi, uint32_t c) {
-    return __builtin_amdgcn_alignbyte(hi, lo, c);
 }
 
 // LUT-BSF for one group of 8 columns with scaled activations v[0..7]:
@@ -126,20 +128,43 @@ __device__ __forceinline__ void lut4_table(const float v[4], float T[16]) {
     for (int q = 0; q < 8; ++q) T[8 + q] = T[q] + u3;
 }
 
-// Sum over the 32 groups of one row's slice for one base: the lane's 8 slots hold words
-// (s + a) mod 8; step t reads the table of group (t + l) mod 32 at that group's pattern.
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
+    return __half2float(__ushort_as_half((unsigned short)h));
+}
+
+// Sums over the 32 groups of one row's slice for one base: step t = 4 i + jj reads the table
+// of group t ^ l at the pattern in byte jj of slot i. lo gets steps 0..15 (groups of the
+// 128-column half (l >> 4) of the slice), hi steps 16..31 (the other half).
 // tb points at the base's half of the table block.
-__device__ __forceinline__ float lookup_row(lds_cchar* tb, const uint4& w0, const uint4& w1, const uint32_t lc[8],
-                                            uint32_t c) {
-    const uint32_t W[9] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w0.x};
+__device__ __forceinline__ void lookup_halves(lds_cchar* tb, const uint4& w0, const uint4& w1, const uint32_t lc[8],
+                                              float& lo, float& hi) {
+    const uint32_t W[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float s[2][4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        s[half][0] = s[half][1] = s[half][2] = s[half][3] = 0.f;
+#pragma unroll
+        for (int i = 4 * half; i < 4 * half + 4; ++i) {
+            s[half][0] += *(const lds_f32*)(tb + perm_addr<0>(W[i], lc[i]));
+            s[half][1] += *(const lds_f32*)(tb + perm_addr<1>(W[i], lc[i]));
+            s[half][2] += *(const lds_f32*)(tb + perm_addr<2>(W[i], lc[i]));
+            s[half][3] += *(const lds_f32*)(tb + perm_addr<3>(W[i], lc[i]));
+        }
+    }
+    lo = (s[0][0] + s[0][1]) + (s[0][2] + s[0][3]);
+    hi = (s[1][0] + s[1][1]) + (s[1][2] + s[1][3]);
+}
+
+// The whole slice: one sum over the 32 groups.
+__device__ __forceinline__ float lookup_row(lds_cchar* tb, const uint4& w0, const uint4& w1, const uint32_t lc[8]) {
+    const uint32_t W[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t A = aligned_pair(W[i], W[i + 1], c);
-        s0 += *(const lds_f32*)(tb + perm_addr<0>(A, lc[i]));
-        s1 += *(const lds_f32*)(tb + perm_addr<1>(A, lc[i]));
-        s2 += *(const lds_f32*)(tb + perm_addr<2>(A, lc[i]));
-        s3 += *(const lds_f32*)(tb + perm_addr<3>(A, lc[i]));
+        s0 += *(const lds_f32*)(tb + perm_addr<0>(W[i], lc[i]));
+        s1 += *(const lds_f32*)(tb + perm_addr<1>(W[i], lc[i]));
+        s2 += *(const lds_f32*)(tb + perm_addr<2>(W[i], lc[i]));
+        s3 += *(const lds_f32*)(tb + perm_addr<3>(W[i], lc[i]));
     }
     return (s0 + s1) + (s2 + s3);
 }
@@ -159,6 +184,7 @@ __global__ void k_fill_zero(float* __restrict__ y, int64_t n) {
 
 struct PackPos {
     int k, row, wcol;  // base, matrix row, canonical word column
+    int c;             // byte order of the row (bytes_for_row)
 };
 
 __device__ __forceinline__ PackPos pack_pos(int64_t o, int nb, int KT) {
@@ -171,8 +197,8 @@ __device__ __forceinline__ PackPos pack_pos(int64_t o, int nb, int KT) {
     const int ks = (int)(tile % KT);
     const int rt = (int)(tile / KT);
     const int s = 4 * q + e;
-    const int wi = (s + rot_words(rho)) & 7;
-    return PackPos{k, rt * kTileRows + rho, ks * kSliceWords + wi};
+    const int wi = s ^ xor_words(rho);
+    return PackPos{k, rt * kTileRows + rho, ks * kSliceWords + wi, xor_bytes(rho)};
 }
 
 __global__ void k_pack_canon(const uint32_t* __restrict__ src, int nb, int N, int K, int KT,
@@ -187,7 +213,7 @@ __global__ void k_pack_canon(const uint32_t* __restrict__ src, int nb, int N, in
         const int rem = K - p.wcol * 32;
         if (rem < 32) val &= (1u << rem) - 1u;
     }
-    dst[o] = val;
+    dst[o] = bytes_for_row(val, p.c);
 }
 
 __global__ void k_pack_int8(const int8_t* __restrict__ src, int nb, int N, int K, int KT, int64_t total,
@@ -203,7 +229,7 @@ __global__ void k_pack_int8(const int8_t* __restrict__ src, int nb, int N, int K
             if (col < K && r[col] > 0) val |= 1u << b;
         }
     }
-    dst[o] = val;
+    dst[o] = bytes_for_row(val, p.c);
 }
 
 // Ternary weights as two half-scale bases: base 0 bit = (w >= 0), base 1 bit = (w > 0), so
@@ -224,7 +250,7 @@ __global__ void k_ternary_bits(const int8_t* __restrict__ w, int N, int K, int K
             }
         }
     }
-    dst[o] = val;
+    dst[o] = bytes_for_row(val, p.c);
 }
 
 __global__ void k_ternary_scales(const float* __restrict__ scale, int N, int K, float* __restrict__ alpha_r,
@@ -292,15 +318,14 @@ __global__ void k_extract8(const uint32_t* __restrict__ packed, int nb, int N, i
     if (rt >= NT || row >= N) return;
     const uint4* tp = reinterpret_cast<const uint4*>(packed + blk * kTileWords);
     const uint4 w0 = tp[rho], w1 = tp[kTileRows + rho];
-    const uint32_t W[9] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w0.x};
-    const uint32_t c = rot_bytes(rho);
+    const uint32_t W[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     uint32_t lc[8];
     lane_columns(rho & 31, lc);
     const int ng = (K + 7) / 8;
     uint16_t* o = out + ((int64_t)k * N + row) * ng;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t A = aligned_pair(W[i], W[i + 1], c);
+        const uint32_t A = W[i];
         const uint32_t ad[4] = {perm_addr<0>(A, lc[i]), perm_addr<1>(A, lc[i]), perm_addr<2>(A, lc[i]),
                                 perm_addr<3>(A, lc[i])};
 #pragma unroll
@@ -323,16 +348,16 @@ __global__ void k_extract4(const uint32_t* __restrict__ packed, int nb, int N, i
     const uint4* tp = reinterpret_cast<const uint4*>(packed + blk * kTileWords);
     const uint4 w0 = tp[rho], w1 = tp[kTileRows + rho];
     const uint32_t S[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    const int a = rot_words(rho);
+    const int a = xor_words(rho), c = xor_bytes(rho);
     const int ng = (K + 3) / 4;
     uint16_t* o = out + ((int64_t)k * N + row) * ng;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const int wi = (s + a) & 7;
+        const int wi = s ^ a;
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
+        for (int n = 0; n < 8; ++n) {  // nibble n of the word: nibble n & 1 of stored byte (n >> 1) ^ c
             const int gi = ks * 64 + wi * 8 + n;
-            if (gi < ng) o[gi] = (uint16_t)((S[s] >> (4 * n)) & 15u);
+            if (gi < ng) o[gi] = (uint16_t)((S[s] >> (8 * ((n >> 1) ^ c) + 4 * (n & 1))) & 15u);
         }
     }
 }
@@ -406,7 +431,8 @@ constexpr uint32_t kXlBytes = 16 * kStepThreads;
 template <typename XT, int RPL, int BMAX, bool XL>
 struct Unit {
     uint4 w[RPL][2];   // this lane's item: its rows' 8 words (two 16-byte halves of the slice)
-    float ar[RPL];     // alpha_r of the item's base at the lane's rows
+    float ar[RPL];     // alpha_r of the item's base at the lane's rows (with group scales: the two
+                       // fp16 scales of the item's slice at those rows, low half first)
     float ac;          // staging: alpha_c of the staged item's base at the staged column
     XT xv[BMAX];       // staging: activations of the staged column (0 for rows >= batch)
     uint4 xb;          // XL: this thread's 16 bytes of the activation block
@@ -497,7 +523,7 @@ struct LaneC {
     uint32_t rho;     // tile row
 };
 
-template <int SI, bool XL, typename XT, int RPL, int BMAX>
+template <int SI, bool XL, bool GS, typename XT, int RPL, int BMAX>
 __device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const StepParams& P, Cursor cu, bool valid,
                                           const LaneC& lcn, int tid) {
     const StepArgs& a = P.a;
@@ -538,8 +564,14 @@ __device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const Step
     const bool lval = 2 * cu.q + (int)lcn.hsel < nitems;
     const uint32_t slab = (uint32_t)nitems * kTileWords * 4u;  // one row tile: all slices and bases
     const uint32_t woff = lval ? (uint32_t)cu.q * (2u * kTileWords * 4u) + lcn.wl : kOob;
-    const uint32_t arBase = (lcn.hsel ? (uint32_t)k1 : (uint32_t)cu.k) * (uint32_t)a.N * 4u;
-    const Rsrc r_ar = make_rsrc(sg.alpha_r, valid ? (uint32_t)sg.nb * (uint32_t)a.N * 4u : 0u);
+    // alpha_r: one fp32 per row, or (group scales) the two fp16 scales of the item's slice,
+    // stored [nb][KT][N][2] so that consecutive rows (lanes) read consecutive 4-byte words
+    constexpr bool gsc = SI == 0 && GS;
+    const uint32_t kh = lcn.hsel ? (uint32_t)k1 : (uint32_t)cu.k;
+    const uint32_t arRow = gsc ? kh * (uint32_t)P.KT[0] + (uint32_t)(lcn.hsel ? ks1 : cu.ks) : kh;
+    const uint32_t arBase = arRow * (uint32_t)a.N * 4u;
+    const Rsrc r_ar =
+        make_rsrc(sg.alpha_r, valid ? (uint32_t)sg.nb * (gsc ? (uint32_t)P.KT[0] : 1u) * (uint32_t)a.N * 4u : 0u);
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
         const int rt = cu.rg * RPL + j;
@@ -562,7 +594,7 @@ __device__ __forceinline__ uint32_t range_start(const StepParams& P, uint32_t g)
 }
 
 // The body of a step: workgroup g of the P.G that work on the GEMV described by P.
-template <typename XT, int RPL, int BMAX, bool XL>
+template <typename XT, int RPL, int BMAX, bool XL, bool GS>
 __device__ __forceinline__ void step_body(const StepParams& P, int g) {
     // Batches above 2 keep their per-row accumulators in thread-private LDS slots (registers
     // indexed by a runtime batch index would go to scratch).
@@ -587,7 +619,7 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
     const int wv = tid >> 6, L = tid & 63;
     const int h = L >> 5, l = L & 31;
     const int rho = 32 * wv + l;                  // tile row of this lane
-    const uint32_t c = (uint32_t)rot_bytes(rho);
+    const bool l_hi = (l & 16) != 0;              // its first 16 lookup steps are the slice's upper half
     const int p0 = 32 * wv;                       // table entries this lane builds
     uint32_t lc[8];
     lane_columns(l, lc);
@@ -727,7 +759,8 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
     };
 
     // One activation row of one unit: build the tables, barrier, look up.
-    auto row_pass = [&](const Unit<XT, RPL, BMAX, XL>& U, bool mine, bool last, int rg, int b, float S[RPL]) {
+    auto row_pass = [&](const Unit<XT, RPL, BMAX, XL>& U, bool mine, bool last, int rg, int b, auto gs_c,
+                        float S[RPL]) {
         if (mine) {
             float v[8];
 #pragma unroll
@@ -744,8 +777,24 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             seen_late = __hip_atomic_load(rg_word(rg) + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             late = true;
         }
+        if constexpr (decltype(gs_c)::value) {
+            // group scales: the first 16 steps of a lane cover the 128-column half (l >> 4) of the
+            // slice, the last 16 the other half
 #pragma unroll
-        for (int j = 0; j < RPL; ++j) S[j] = mine ? U.ar[j] * lookup_row(tb, U.w[j][0], U.w[j][1], lc, c) : 0.f;
+            for (int j = 0; j < RPL; ++j) {
+                float lo, hi;
+                lookup_halves(tb, U.w[j][0], U.w[j][1], lc, lo, hi);
+                const uint32_t pr = __float_as_uint(U.ar[j]);
+                const float a0 = half_bits_to_f32(pr & 0xFFFFu), a1 = half_bits_to_f32(pr >> 16);
+                // a half past column K sums to exactly 0 and its scale (padding) is not read
+                const float pa = lo != 0.f ? (l_hi ? a1 : a0) * lo : 0.f;
+                const float pb = hi != 0.f ? (l_hi ? a0 : a1) * hi : 0.f;
+                S[j] = mine ? pa + pb : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < RPL; ++j) S[j] = mine ? U.ar[j] * lookup_row(tb, U.w[j][0], U.w[j][1], lc) : 0.f;
+        }
     };
 
     // One unit: stage, then one table build + lookup pass per activation row; flush if it is
@@ -776,7 +825,7 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             for (int b = 0; b < BMAX; ++b) {
                 if (b < a.batch) {
                     float S[RPL];
-                    row_pass(U, mine, last, cu.rg, b, S);
+                    row_pass(U, mine, last, cu.rg, b, std::integral_constant<bool, SI == 0 && GS>{}, S);
 #pragma unroll
                     for (int j = 0; j < RPL; ++j) acc[j][kAccLds ? 0 : b] += S[j];
                     __syncthreads();
@@ -785,7 +834,7 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         } else {
             for (int b = 0; b < a.batch; ++b) {
                 float S[RPL];
-                row_pass(U, mine, last, cu.rg, b, S);
+                row_pass(U, mine, last, cu.rg, b, std::integral_constant<bool, SI == 0 && GS>{}, S);
 #pragma unroll
                 for (int j = 0; j < RPL; ++j) sacc[(j * BMAX + b) * kStepThreads + tid] += S[j];
                 __syncthreads();
@@ -818,13 +867,13 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             return hi - x < left ? hi - x : left;
         };
         Unit<XT, RPL, BMAX, XL> s0, s1, s2;
-        load_unit<SI, XL>(s0, P, lcur, true, lcn, tid);
+        load_unit<SI, XL, GS>(s0, P, lcur, true, lcn, tid);
         advance(lcur, US, nb);
         if (zpend) zero_owned();
         enter(pcur.rg, run_units(lo, pcur));
-        load_unit<SI, XL>(s1, P, lcur, lo + 1 < hi, lcn, tid);
+        load_unit<SI, XL, GS>(s1, P, lcur, lo + 1 < hi, lcn, tid);
         advance(lcur, US, nb);
-        load_unit<SI, XL>(s2, P, lcur, lo + 2 < hi, lcn, tid);
+        load_unit<SI, XL, GS>(s2, P, lcur, lo + 2 < hi, lcn, tid);
         advance(lcur, US, nb);
         auto step = [&](const Unit<XT, RPL, BMAX, XL>& U, uint32_t x) {
             const bool last = x + 1 == hi || pcur.q + 1 == US;
@@ -834,13 +883,13 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         };
         for (uint32_t x = lo; x < hi; x += 3) {
             step(s0, x);
-            load_unit<SI, XL>(s0, P, lcur, x + 3 < hi, lcn, tid);
+            load_unit<SI, XL, GS>(s0, P, lcur, x + 3 < hi, lcn, tid);
             advance(lcur, US, nb);
             if (x + 1 < hi) step(s1, x + 1);
-            load_unit<SI, XL>(s1, P, lcur, x + 4 < hi, lcn, tid);
+            load_unit<SI, XL, GS>(s1, P, lcur, x + 4 < hi, lcn, tid);
             advance(lcur, US, nb);
             if (x + 2 < hi) step(s2, x + 2);
-            load_unit<SI, XL>(s2, P, lcur, x + 5 < hi, lcn, tid);
+            load_unit<SI, XL, GS>(s2, P, lcur, x + 5 < hi, lcn, tid);
             advance(lcur, US, nb);
         }
     };
@@ -854,9 +903,9 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
 // 256 VGPRs); two workgroups per CU need at most 128, which the instances with one or two row
 // tiles and batch up to 4 stay within. (Asking for 4 waves per SIMD instead makes the compiler
 // issue the table lookups in smaller batches, which costs more than it gains.)
-template <typename XT, int RPL, int BMAX, bool XL>
+template <typename XT, int RPL, int BMAX, bool XL, bool GS>
 __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(StepParams P) {
-    step_body<XT, RPL, BMAX, XL>(P, (int)blockIdx.x);
+    step_body<XT, RPL, BMAX, XL, GS>(P, (int)blockIdx.x);
 }
 
 // Several GEMVs sharing x in one launch: GEMV i gets workgroups [start[i], start[i + 1]) and
@@ -872,7 +921,7 @@ __global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8_gro
     const int b = (int)blockIdx.x;
     int i = 0;
     while (i + 1 < GP.count && b >= GP.start[i + 1]) ++i;
-    step_body<XT, RPL, BMAX, XL>(GP.p[i], b - GP.start[i]);
+    step_body<XT, RPL, BMAX, XL, false>(GP.p[i], b - GP.start[i]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -966,10 +1015,10 @@ static int64_t capacity_of(Kernel k, int64_t& cache) {
     }
     return cache;
 }
-template <typename XT, int RPL, int BMAX, bool XL>
+template <typename XT, int RPL, int BMAX, bool XL, bool GS>
 static int64_t resident_capacity() {
     static int64_t cap = -1;
-    return capacity_of(k_gemv8<XT, RPL, BMAX, XL>, cap);
+    return capacity_of(k_gemv8<XT, RPL, BMAX, XL, GS>, cap);
 }
 template <typename XT, int RPL, int BMAX, bool XL>
 static int64_t resident_capacity_group() {
@@ -996,9 +1045,9 @@ static hipError_t finish_params(StepParams& P, int64_t G, hipStream_t s) {
     return hipSuccess;
 }
 
-template <typename XT, int RPL, int BMAX, bool XL>
+template <typename XT, int RPL, int BMAX, bool XL, bool GS>
 static hipError_t launch_step_t(StepParams P, hipStream_t s) {
-    const int64_t cap = resident_capacity<XT, RPL, BMAX, XL>();
+    const int64_t cap = resident_capacity<XT, RPL, BMAX, XL, GS>();
     if (cap <= 0) return hipErrorInvalidConfiguration;
     // Never more workgroups than the device holds at once: the flag waits rely on it.
     int64_t G = P.a.workgroups > 0 ? P.a.workgroups : cap;
@@ -1006,7 +1055,7 @@ static hipError_t launch_step_t(StepParams P, hipStream_t s) {
     G = G < P.U ? G : P.U;
     hipError_t e = finish_params(P, G, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemv8<XT, RPL, BMAX, XL>), dim3((unsigned)P.G), dim3(kStepThreads), 0, s, P);
+    hipLaunchKernelGGL((k_gemv8<XT, RPL, BMAX, XL, GS>), dim3((unsigned)P.G), dim3(kStepThreads), 0, s, P);
     return hipGetLastError();
 }
 
@@ -1086,7 +1135,8 @@ bool step_buffers_fit(const StepArgs& a) {
     for (int i = 0; i < a.nseg; ++i) {
         const Segment& sg = a.seg[i];
         const int64_t KT = ceil_div(sg.Kv, kSliceCols);
-        if ((int64_t)sg.nb * a.N * 4 >= lim || (int64_t)sg.nb * sg.Kv * 4 >= lim) return false;
+        const int64_t arows = (i == 0 && a.gs) ? KT : 1;  // alpha_r: [nb][N] fp32 or [nb][KT][N][2] fp16
+        if ((int64_t)sg.nb * arows * a.N * 4 >= lim || (int64_t)sg.nb * sg.Kv * 4 >= lim) return false;
         if ((int64_t)sg.Kv * 4 >= lim || KT * sg.nb * kTileWords * 4 >= lim) return false;
     }
     return true;
@@ -1129,9 +1179,19 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s) {
     hipError_t e = make_params(a, P);
     if (e != hipSuccess) return e;
     const bool xl = P.US[1] > 0 && gather_in_lds(a);
+    // group scales are a separate set of instances: the per-row kernels carry no code for them
     auto go = [&](auto xt, auto rpl_c, auto bmax_c, auto xl_c) {
-        return launch_step_t<decltype(xt), decltype(rpl_c)::value, decltype(bmax_c)::value, decltype(xl_c)::value>(P, s);
+        return launch_step_t<decltype(xt), decltype(rpl_c)::value, decltype(bmax_c)::value, decltype(xl_c)::value,
+                             false>(P, s);
     };
+    auto go_gs = [&](auto xt, auto rpl_c, auto bmax_c, auto xl_c) {
+        return launch_step_t<decltype(xt), decltype(rpl_c)::value, decltype(bmax_c)::value, decltype(xl_c)::value,
+                             true>(P, s);
+    };
+    if (a.gs) {
+        if (a.x_dtype == UBW_F16) return dispatch_instance<__half>(a.batch, a.rows_per_group, xl, go_gs);
+        return dispatch_instance<float>(a.batch, a.rows_per_group, xl, go_gs);
+    }
     if (a.x_dtype == UBW_F16) return dispatch_instance<__half>(a.batch, a.rows_per_group, xl, go);
     return dispatch_instance<float>(a.batch, a.rows_per_group, xl, go);
 }
@@ -1143,7 +1203,7 @@ hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s) {
     GP.count = count;
     bool any_refine = false, lds_ok = true;
     for (int i = 0; i < count; ++i) {
-        if (a[i].x != a[0].x || a[i].batch != a[0].batch || a[i].x_dtype != a[0].x_dtype ||
+        if (a[i].gs || a[i].x != a[0].x || a[i].batch != a[0].batch || a[i].x_dtype != a[0].x_dtype ||
             a[i].ldx != a[0].ldx || a[i].rows_per_group != a[0].rows_per_group)
             return hipErrorInvalidValue;
         hipError_t e = make_params(a[i], GP.p[i]);

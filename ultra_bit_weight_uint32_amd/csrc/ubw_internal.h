@@ -9,12 +9,13 @@
 // row and half-tile, and consecutive rows (= consecutive lanes of a wave) read consecutive
 // vectors.
 //
-// Slot s of row rho holds word (s + a) mod 8 of the row's 256-column slice, where
-// a = (rho mod 32) / 4. That rotation, together with a byte rotation by c = rho mod 4, makes
-// the lane that owns row rho visit the 32 column groups of the slice in the order
-// (t + rho mod 32) mod 32 for t = 0..31, so that the 32 lanes of each half-wave look up 32
-// different tables at every step; the tables are laid out so that each one sits in a single
-// LDS bank, which makes every lookup instruction bank-conflict free.
+// Slot s of row rho holds word s ^ a of the row's 256-column slice, with its bytes permuted:
+// byte jj of the slot is byte jj ^ c of the word, where l = rho mod 32 = 4 a + c. Byte jj of
+// slot i is then the pattern of column group (4 i + jj) ^ l, so the lane that owns row rho
+// visits the 32 groups of the slice in the order t ^ l for t = 0..31: the 32 lanes of each
+// half-wave look up 32 different tables at every step (each table sits in a single LDS bank,
+// which makes every lookup instruction bank-conflict free), and steps 0..15 cover one
+// 128-column half of the slice, steps 16..31 the other.
 // Rows >= N and columns >= K are stored as zero bits.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -37,7 +38,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // bases over the s virtual columns that idx maps onto activation columns.
 struct Segment {
     const uint32_t* packed;
-    const float* alpha_r;   // [nb][N]
+    const void* alpha_r;    // [nb][N] fp32; with StepArgs::gs, fp16 [nb][N][2 * ceil(Kv / 256)]
     const float* alpha_c;   // [nb][Kv]
     const int32_t* idx;     // [Kv] virtual column -> activation column, or nullptr (identity)
     int nb;
@@ -52,6 +53,7 @@ struct StepArgs {
     int N;
     const void* x;          // [batch][ldx]
     int x_dtype;            // UBW_F32 / UBW_F16
+    int gs;                 // 1: seg[0] has one fp16 row scale per 128 columns (see Segment)
     int64_t ldx;            // activation row length K
     int batch;
     float* y;               // [batch][N]
