@@ -40,6 +40,8 @@ def _load():
     lib.oracle_gemv.restype = None
     lib.oracle_gemv_gs.argtypes = [P, P, I64, I, P, I, I64, I64, P, I64, P, P, P, I, P, I, P]
     lib.oracle_gemv_gs.restype = None
+    lib.oracle_fit.argtypes = [P, I64, I64, I, I, P, P, P, P]
+    lib.oracle_fit.restype = None
     lib.oracle_lut_gemv.argtypes = [P, P, P, I, I64, I64, P, I64, P, P, P, I, P, I, I, P]
     lib.oracle_lut_gemv.restype = None
     lib.oracle_patterns.argtypes = [P, I, I64, I64, I, P]
@@ -212,3 +214,18 @@ def ternary_encode(w, zero_first_plus=True):
     out = np.empty((2, n, words_per_row(k)), dtype=np.uint32)
     _load().oracle_ternary_encode(_ptr(w), n, k, 1 if zero_first_plus else 0, _ptr(out))
     return out
+
+
+def fit(w, nb, iters):
+    """Offline fit of nb bases to a dense w [N, K] (fp32 values): residual sign binarization
+    with `iters` alternating least-squares rounds for (alpha_r, alpha_c) per base. Returns
+    (bits [nb, N, ceil(K/32)] uint32, alpha_r [nb, N], alpha_c [nb, K], residual [N, K]), the
+    scales and residual in float64."""
+    w = _c(np.asarray(w).astype(np.float32), np.float32)
+    n, k = w.shape
+    bits = np.empty((nb, n, words_per_row(k)), dtype=np.uint32)
+    ar = np.empty((nb, n), dtype=np.float64)
+    ac = np.empty((nb, k), dtype=np.float64)
+    res = np.empty((n, k), dtype=np.float64)
+    _load().oracle_fit(_ptr(w), n, k, int(nb), int(iters), _ptr(bits), _ptr(ar), _ptr(ac), _ptr(res))
+    return bits, ar, ac, res

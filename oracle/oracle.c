@@ -29,6 +29,7 @@
  */
 #include <stdint.h>
 #include <stdlib.h>
+#include <math.h>
 #include <string.h>
 #include <omp.h>
 
@@ -311,5 +312,69 @@ void oracle_ternary_encode(const int8_t* w, int64_t N, int64_t K, int zero_first
             out[(0 * N + r) * kw + j / 32] |= b1 << (j % 32);
             out[(1 * N + r) * kw + j / 32] |= b2 << (j % 32);
         }
+    }
+}
+
+/*
+ * Offline fit of the decomposition from a dense matrix: residual binarization with
+ * alternating least squares for the two scale vectors. The page ("1. Algorithm innovation")
+ * gives only the form W ~ sum_k (alpha_r^(k) alpha_c^(k)^T) (.) B^(k); the steps below are
+ * the plainest fit of that form, written out:
+ *
+ *   R = W
+ *   for each base k:
+ *     B = sign(R)  (+1 where R >= 0), so that R (.) B = |R| =: A
+ *     alpha_r[r] = mean_j A[r][j], alpha_c = 1                      (per-row binarization)
+ *     repeat iters times (each half step is the exact least-squares solution of
+ *     min ||A - alpha_r alpha_c^T||_F for one vector with the other fixed):
+ *       alpha_c[j] = sum_r A[r][j] alpha_r[r] / sum_r alpha_r[r]^2   (0 if the sum is 0)
+ *       alpha_r[r] = sum_j A[r][j] alpha_c[j] / sum_j alpha_c[j]^2   (0 if the sum is 0)
+ *     R = R - (alpha_r alpha_c^T) (.) B
+ *
+ * w [N][K] (fp32 values), bits [nb][N][ceil(K/32)] canonical (columns >= K zero),
+ * alpha_r [nb][N], alpha_c [nb][K], residual [N][K] (the final R). All arithmetic fp64.
+ */
+void oracle_fit(const float* w, int64_t N, int64_t K, int nb, int iters, uint32_t* bits,
+                double* alpha_r, double* alpha_c, double* residual) {
+    const int64_t kw = words_per_row(K);
+    double* R = residual;
+    for (int64_t i = 0; i < N * K; ++i) R[i] = (double)w[i];
+    memset(bits, 0, sizeof(uint32_t) * (size_t)(nb * N * kw));
+    for (int k = 0; k < nb; ++k) {
+        uint32_t* bk = bits + (int64_t)k * N * kw;
+        double* ar = alpha_r + (int64_t)k * N;
+        double* ac = alpha_c + (int64_t)k * K;
+        for (int64_t r = 0; r < N; ++r) {
+            double s = 0.0;
+            for (int64_t j = 0; j < K; ++j) {
+                const double v = R[r * K + j];
+                if (v >= 0.0) bk[r * kw + j / 32] |= 1u << (j % 32);
+                s += fabs(v);
+            }
+            ar[r] = s / (double)K;
+        }
+        for (int64_t j = 0; j < K; ++j) ac[j] = 1.0;
+        for (int it = 0; it < iters; ++it) {
+            double sr = 0.0;
+            for (int64_t r = 0; r < N; ++r) sr += ar[r] * ar[r];
+            for (int64_t j = 0; j < K; ++j) ac[j] = 0.0;
+            for (int64_t r = 0; r < N; ++r)
+                for (int64_t j = 0; j < K; ++j) ac[j] += fabs(R[r * K + j]) * ar[r];
+            for (int64_t j = 0; j < K; ++j) ac[j] = sr > 0.0 ? ac[j] / sr : 0.0;
+            double sc = 0.0;
+            for (int64_t j = 0; j < K; ++j) sc += ac[j] * ac[j];
+#pragma omp parallel for schedule(static)
+            for (int64_t r = 0; r < N; ++r) {
+                double s = 0.0;
+                for (int64_t j = 0; j < K; ++j) s += fabs(R[r * K + j]) * ac[j];
+                ar[r] = sc > 0.0 ? s / sc : 0.0;
+            }
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < N; ++r)
+            for (int64_t j = 0; j < K; ++j) {
+                const double b = ((bk[r * kw + j / 32] >> (j % 32)) & 1u) ? 1.0 : -1.0;
+                R[r * K + j] -= ar[r] * ac[j] * b;
+            }
     }
 }

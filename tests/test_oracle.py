@@ -336,3 +336,79 @@ def test_gs_refinement_adds_the_same_branch():
     branch = oracle.gemv(g.bits, g.alpha_r, g.alpha_c, g.x, **g.refine_kwargs()) - oracle.gemv(
         g.bits, g.alpha_r, g.alpha_c, g.x)
     assert np.array_equal(with_ref, without + branch)
+
+
+# ---------------------------------------------------------------------------------------------
+# offline fit: residual sign binarization + alternating least squares for (alpha_r, alpha_c)
+
+def _sign_bits(m):
+    """Canonical words of sign(m) (+1 where m >= 0) via numpy packbits."""
+    n, k = m.shape
+    b = np.zeros((n, words_per_row(k) * 32), np.uint8)
+    b[:, :k] = (m >= 0)
+    return np.packbits(b, axis=1, bitorder="little").view(np.uint32).reshape(n, words_per_row(k))
+
+
+def test_fit_gaussian_one_base_closed_form():
+    """N(0,1) entries, one base, no ALS round: alpha = mean|w| ~ sqrt(2/pi) and the residual
+    keeps 1 - 2/pi of the energy."""
+    rng = np.random.default_rng(200)
+    w = rng.standard_normal((512, 2048)).astype(np.float32)
+    bits, ar, ac, res = oracle.fit(w, 1, 0)
+    assert np.allclose(ar[0], np.abs(w.astype(np.float64)).mean(axis=1), rtol=1e-12)
+    assert np.all(ac == 1.0)
+    assert abs(ar[0].mean() - np.sqrt(2 / np.pi)) < 5e-3
+    assert abs((res ** 2).sum() / (w.astype(np.float64) ** 2).sum() - (1 - 2 / np.pi)) < 5e-3
+
+
+def test_fit_recovers_an_exact_decomposition():
+    """W = (a b^T) (.) B with positive a, b: one base and one ALS round give B exactly and a
+    zero residual (|W| has rank one)."""
+    rng = np.random.default_rng(201)
+    n, k = 70, 333
+    a = rng.integers(1, 9, n).astype(np.float64)     # small integers: a b^T is exact in fp32
+    b = rng.integers(1, 9, k).astype(np.float64)
+    signs = np.where(rng.random((n, k)) < 0.5, -1.0, 1.0)
+    w = (np.outer(a, b) * signs).astype(np.float32)
+    bits, ar, ac, res = oracle.fit(w, 1, 1)
+    assert np.array_equal(bits[0], _sign_bits(w))
+    assert np.abs(res).max() < 1e-12 * np.abs(w).max()
+    assert np.allclose(np.outer(ar[0], ac[0]), np.abs(w.astype(np.float64)), rtol=1e-12)
+
+
+def test_fit_als_converges_to_leading_singular_pair():
+    """Many ALS rounds are a power iteration on |R|: alpha_r alpha_c^T tends to the best rank-one
+    approximation sigma_1 u_1 v_1^T of |W| (numpy SVD)."""
+    rng = np.random.default_rng(202)
+    w = rng.standard_normal((60, 90)).astype(np.float32)
+    bits, ar, ac, res = oracle.fit(w, 1, 300)
+    u, sv, vt = np.linalg.svd(np.abs(w.astype(np.float64)))
+    best = sv[0] * np.outer(u[:, 0], vt[0])
+    assert np.allclose(np.outer(ar[0], ac[0]), best, rtol=1e-8, atol=1e-10)
+
+
+def test_fit_error_never_increases():
+    rng = np.random.default_rng(203)
+    w = (rng.standard_normal((200, 300)) * rng.uniform(0.2, 3, (200, 1)) * rng.uniform(0.2, 3, (1, 300))
+         ).astype(np.float32)
+    by_bases = [np.linalg.norm(oracle.fit(w, nb, 3)[3]) for nb in range(1, 5)]
+    assert all(b < a for a, b in zip([np.linalg.norm(w)] + by_bases, by_bases))
+    by_rounds = [np.linalg.norm(oracle.fit(w, 1, t)[3]) for t in range(0, 6)]
+    assert all(b <= a * (1 + 1e-14) for a, b in zip(by_rounds, by_rounds[1:]))
+
+
+def test_fit_bases_follow_the_residual():
+    """Base k's bits are the signs of the residual left by the first k bases, the residual is
+    W minus the dequantized bases, and the scaled bases reconstruct W - residual."""
+    rng = np.random.default_rng(204)
+    w = rng.standard_normal((50, 130)).astype(np.float32)
+    w[::7, ::5] = 0.0          # sign(0) reads +1
+    bits, ar, ac, res = oracle.fit(w, 3, 2)
+    assert np.array_equal(bits[0], _sign_bits(w))
+    for k in (1, 2):
+        prev = oracle.fit(w, k, 2)
+        assert np.array_equal(bits[k], _sign_bits(prev[3]))
+        assert np.allclose(prev[1], ar[:k]) and np.allclose(prev[2], ac[:k])
+    signs = dense_signs(bits, 130).astype(np.float64)
+    w_hat = sum(np.outer(ar[k], ac[k]) * signs[k] for k in range(3))
+    assert np.allclose(w.astype(np.float64) - w_hat, res, rtol=0, atol=1e-12)
