@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs", action="store_true",
                     help="instead of the headline line: time every GEMV and layer of the 7B MLP (config 4) and the "
-                         "70B layer (config 5) at their batches, and the group-scale variant, same protocol, one JSON line each")
+                         "70B layer (config 5) at their batches, the group-scale variant and the offline fit, one JSON line each")
     ap.add_argument("--profile-run", action="store_true",
                     help="for hardware-counter runs: a 64 MiB device copy (known bytes, to scale the counters) "
                          "then --steps cold steps; prints one line, no timing")
@@ -84,6 +84,7 @@ def main():
     if args.configs:
         config_sweep(torch, ubw, dev)
         gs_sweep(torch, ubw, dev)
+        fit_sweep(torch, ubw, dev)
         return
     wl = config3(seed=0)
     g = wl.gemvs[0]
@@ -364,6 +365,40 @@ def gs_sweep(torch, ubw, dev):
                               "GBps": round(by / us / 1e3, 1), "pct_of_peak": round(by / us / 1e3 / PEAK_GBS * 100, 2),
                               "algorithmic_bytes": by, "cold_copies": len(C)}), flush=True)
         del C
+        torch.cuda.empty_cache()
+
+
+def fit_bytes(n, k, nb, iters, w_bytes=4):
+    """HBM bytes the fit's passes must move: W read and the residual written once, then per
+    base after the first a residual update (read + write), the sign words, 2 reads of the
+    residual per ALS round, and the final update."""
+    nk = n * k
+    return (w_bytes + 4) * nk + (nb - 1) * 8 * nk + nb * nk // 8 + nb * iters * 8 * nk + 8 * nk
+
+
+def fit_sweep(torch, ubw, dev):
+    """The offline fit (residual binarization + alternating least squares) at the 7B projection
+    and the 70B q/o shapes: one JSON line each, GPU time next to the oracle's on the host."""
+    import oracle
+    rng = np.random.default_rng(6)
+    for n, k, nb, iters in ((4096, 4096, 2, 5), (8192, 8192, 3, 5)):
+        w = (rng.standard_normal((n, k)) * rng.uniform(0.2, 3, (n, 1))).astype(np.float32)
+        wt = torch.from_numpy(w).to(dev)
+        res = torch.empty((n, k), dtype=torch.float32, device=dev)
+        ws = torch.empty(ubw.fit_workspace_bytes(n, k) // 4, dtype=torch.float32, device=dev)
+        for _ in range(2):
+            ubw.fit_bases(wt, nb, iters, residual=res, workspace=ws)
+        reps = 5
+        ms = run_queued(torch, lambda i: ubw.fit_bases(wt, nb, iters, residual=res, workspace=ws), reps) / reps
+        by = fit_bytes(n, k, nb, iters)
+        t0 = time.perf_counter()
+        oracle.fit(w, nb, iters)
+        cpu = time.perf_counter() - t0
+        print(json.dumps({"sweep": "offline fit", "shape": [n, k], "nb": nb, "iters": iters, "ms": round(ms, 3),
+                          "GBps": round(by / ms / 1e6, 1), "pct_of_peak": round(by / ms / 1e6 / PEAK_GBS * 100, 2),
+                          "algorithmic_bytes": by, "oracle_s": round(cpu, 3), "oracle_cores": oracle.max_threads()}),
+              flush=True)
+        del wt, res, ws
         torch.cuda.empty_cache()
 
 

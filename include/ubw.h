@@ -248,6 +248,34 @@ int ubw_lut_gemv_multi(const ubw_gemv_desc* descs, int count, int64_t K, int g, 
                        int x_dtype, int batch, int accumulate, void* stream);
 
 /*
+ * Offline fit of the decomposition from a dense matrix (load time; its output feeds
+ * ubw_pack_bases with UBW_SRC_CANON_BITS). Section "1. Algorithm innovation" gives the form
+ * W ~ sum_k (alpha_r^(k) alpha_c^(k)^T) (.) B^(k), B in {-1,+1}, but not how it is fitted; the
+ * fit here is residual binarization with alternating least squares:
+ *   R = W; for k < nb: B^(k) = sign(R) (+1 where R >= 0); A = |R|;
+ *   alpha_r = row means of A, alpha_c = 1; then `iters` rounds of
+ *   alpha_c = A^T alpha_r / ||alpha_r||^2 and alpha_r = A alpha_c / ||alpha_c||^2 (each the
+ *   least-squares optimum for one vector given the other; 0 where the norm is 0);
+ *   R = R - (alpha_r alpha_c^T) (.) B^(k).
+ * The error ||R|| never increases from one base, or one round, to the next.
+ *   w          [N][K] fp32 (UBW_F32) or fp16 (UBW_F16), row-major
+ *   nb         bases, 1..64; iters: ALS rounds per base, 0..10000 (0 = per-row binarization)
+ *   bits       OUT canonical signs [nb][N][ceil(K/32)] uint32 (column j: word j/32, bit j%32;
+ *              bits past column K are 0)
+ *   alpha_r    OUT fp32 [nb][N];  alpha_c OUT fp32 [nb][K]
+ *   residual   OUT fp32 [N][K]: W minus the fitted bases. It may be the same buffer as w when w
+ *              is fp32 (the fit then overwrites W).
+ *   workspace  ubw_fit_workspace_bytes(N, K) bytes of scratch (partial sums), caller-owned
+ * All sums are fp32 in a fixed order (no atomics): the result is deterministic.
+ * Errors: UBW_EINVAL (null, sizes, nb, iters), UBW_EUNSUPPORTED (w_dtype), UBW_EALIGN (a pointer
+ *         not 4-byte aligned), UBW_ERANGE (N above 4,194,240), UBW_ESIZE (workspace), UBW_EHIP.
+ */
+int ubw_fit_workspace_bytes(int64_t N, int64_t K, size_t* out);
+int ubw_fit_bases(const void* w, int w_dtype, int64_t N, int64_t K, int nb, int iters, uint32_t* bits,
+                  float* alpha_r, float* alpha_c, float* residual, void* workspace, size_t ws_bytes,
+                  void* stream);
+
+/*
  * Host-side check of a salient index list: every idx[q] in [0, K) and strictly ascending.
  * idx is a HOST pointer. Returns UBW_OK or UBW_ERANGE (UBW_EINVAL for null / s < 1).
  */

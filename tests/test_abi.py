@@ -206,6 +206,26 @@ def test_gs_rejects():
     assert L.ubw_lut_gemv_geometry(*b2, 2, *tail) == EALIGN                       # group scales: 4-byte aligned
 
 
+def test_fit_rejects():
+    L = ubw.lib()
+    sz = ctypes.c_size_t()
+    assert L.ubw_fit_workspace_bytes(0, 10, ctypes.byref(sz)) == EINVAL
+    assert L.ubw_fit_workspace_bytes(10, 10, None) == EINVAL
+    assert L.ubw_fit_workspace_bytes(100, 300, ctypes.byref(sz)) == 0
+    assert sz.value == 4 * (2 * 300 + 2 + 2)                      # 2 row chunks of 64, 2 column blocks
+    need = sz.value
+    args = dict(w=FAKE, dt=0, N=100, K=300, nb=2, iters=3, bits=FAKE, ar=FAKE, ac=FAKE, res=FAKE, ws=FAKE,
+                wsb=need, stream=None)
+    for kw, status in [(dict(w=None), EINVAL), (dict(bits=None), EINVAL), (dict(res=None), EINVAL),
+                       (dict(ws=None), EINVAL), (dict(N=0), EINVAL), (dict(K=-1), EINVAL), (dict(nb=0), EINVAL),
+                       (dict(nb=65), EINVAL), (dict(iters=-1), EINVAL), (dict(iters=10001), EINVAL),
+                       (dict(dt=5), EUNSUP), (dict(ar=ctypes.c_void_p(0x10002)), EALIGN),
+                       (dict(wsb=need - 4), ESIZE), (dict(N=65535 * 64 + 1, wsb=1 << 40), ERANGE)]:
+        a = dict(args)
+        a.update(kw)
+        assert L.ubw_fit_bases(*a.values()) == status, kw
+
+
 def test_other_entry_points_reject():
     L = ubw.lib()
     assert L.ubw_pack_bases(None, 0, 1, 8, 8, 8, FAKE, None) == EINVAL

@@ -615,3 +615,87 @@ def test_gs_equal_blocks_match_plain_gemv():
     g16.bits_s, g16.alpha_r_s, g16.alpha_c_s = g.bits_s, g.alpha_r_s, g.alpha_c_s
     g16.alpha_r = g.alpha_r.astype(np.float16).astype(np.float32)
     assert max_rel_err(gpu_gs(g, arg), gpu_gemv(g16)) <= TOL
+
+
+# ------------------------------------------------------------------------------------------
+# offline fit (residual sign binarization + alternating least squares)
+
+def fit_matrix(rng, n, k, dtype=np.float32):
+    """Anisotropic dense matrix: N(0,1) entries times per-row and per-column magnitudes."""
+    w = rng.standard_normal((n, k)) * rng.uniform(0.2, 3, (n, 1)) * rng.uniform(0.2, 3, (1, k))
+    return w.astype(dtype)
+
+
+def check_fit(w, nb, iters):
+    wt = dev(w)
+    bits, ar, ac, res = ubw.fit_bases(wt, nb, iters)
+    bits, ar, ac, res = host(bits).view(np.uint32), host(ar), host(ac), host(res)
+    obits, oar, oac, ores = oracle.fit(w, nb, iters)
+    w64 = w.astype(np.float64)
+    scale = np.abs(w64).max()
+    # base 0: the signs of W itself, decided on the same values on both sides
+    assert np.array_equal(bits[0], obits[0])
+    for kk in range(nb):
+        if kk:
+            # later bases: signs of a residual that fp32 and fp64 round differently; a sign may
+            # differ only where that residual is within rounding of zero
+            rk = oracle.fit(w, kk, iters)[3]
+            diff = np.unpackbits((bits[kk] ^ obits[kk]).view(np.uint8), axis=-1, bitorder="little")[:, :w.shape[1]]
+            if diff.any():
+                assert np.abs(rk[diff.astype(bool)]).max() <= 1e-5 * scale, kk
+        assert max_rel_err(ar[kk], oar[kk]) <= 1e-4, ("alpha_r", kk)
+        assert max_rel_err(ac[kk], oac[kk]) <= 1e-4, ("alpha_c", kk)
+    assert np.linalg.norm(res - ores) <= 1e-4 * np.linalg.norm(w64)
+    return res
+
+
+# (a single row is fitted exactly by one base, so its second base would fit rounding noise)
+@pytest.mark.parametrize("n,k,nb,iters", [(300, 700, 3, 5), (1, 33, 1, 2), (257, 64, 1, 0), (65, 300, 2, 1),
+                                          (1000, 2000, 2, 10)])
+def test_fit_matches_oracle(n, k, nb, iters):
+    rng = np.random.default_rng(n + k + nb + iters)
+    check_fit(fit_matrix(rng, n, k), nb, iters)
+
+
+def test_fit_fp16_input_and_zeros():
+    rng = np.random.default_rng(7)
+    w = fit_matrix(rng, 200, 513, np.float16)
+    w[::5, ::3] = 0          # sign(0) reads +1 on both sides
+    check_fit(w, 2, 3)
+
+
+def test_fit_config3_shape():
+    """4096 x 4096 (the 7B projection), 2 bases, 5 rounds: every scale and the residual."""
+    rng = np.random.default_rng(8)
+    res = check_fit(fit_matrix(rng, 4096, 4096), 2, 5)
+    assert np.isfinite(res).all()
+
+
+def test_fit_recovers_exact_decomposition_and_error_falls():
+    rng = np.random.default_rng(9)
+    n, k = 300, 1000
+    a = rng.integers(1, 9, n).astype(np.float64)
+    b = rng.integers(1, 9, k).astype(np.float64)
+    signs = np.where(rng.random((n, k)) < 0.5, -1.0, 1.0)
+    w = (np.outer(a, b) * signs).astype(np.float32)
+    bits, ar, ac, res = ubw.fit_bases(dev(w), 1, 1)
+    words = oracle.fit(w, 1, 0)[0][0]   # the signs of w
+    assert np.array_equal(host(bits)[0].view(np.uint32), words)
+    assert np.abs(host(res)).max() <= 1e-5 * np.abs(w).max()
+    # the residual of a general matrix shrinks with every base
+    w = fit_matrix(rng, 500, 700)
+    norms = [np.linalg.norm(host(ubw.fit_bases(dev(w), nb, 3)[3])) for nb in (1, 2, 3, 4)]
+    assert all(b < a for a, b in zip([np.linalg.norm(w)] + norms, norms))
+
+
+def test_fit_output_drives_the_gemv():
+    """Fitted bases packed and run through the step equal the oracle GEMV of the same bases."""
+    rng = np.random.default_rng(10)
+    n, k = 700, 1500
+    w = fit_matrix(rng, n, k)
+    bits, ar, ac, _ = ubw.fit_bases(dev(w), 2, 3)
+    x = rng.standard_normal((2, k)).astype(np.float16)
+    packed = ubw.pack_bases(bits, 2, n, k)
+    y = ubw.lut_gemv(packed, ar, ac, dev(x), n, k, workspace=ubw.workspace(n, DEV))
+    r = oracle.gemv(host(bits).view(np.uint32), host(ar), host(ac), x)
+    assert max_rel_err(host(y), r) <= TOL

@@ -28,7 +28,7 @@ EXPORTS = (
     "ubw_status_str", "ubw_version", "ubw_packed_words", "ubw_pack_bases", "ubw_ternary_encode",
     "ubw_build_lut", "ubw_workspace_bytes", "ubw_lut_gemv", "ubw_vcm_gather_refine", "ubw_lut_gemv_refined",
     "ubw_check_indices", "ubw_extract_patterns", "ubw_lut_gemv_geometry", "ubw_bench_stream_read",
-    "ubw_lut_gemv_multi", "ubw_lut_gemv_gs",
+    "ubw_lut_gemv_multi", "ubw_lut_gemv_gs", "ubw_fit_workspace_bytes", "ubw_fit_bases",
 )
 
 
@@ -77,6 +77,8 @@ def lib():
         "ubw_bench_stream_read": ([P, I64, P, P], I),
         "ubw_lut_gemv_multi": ([ctypes.POINTER(GemvDesc), I, I64, I, P, I, I, I, P], I),
         "ubw_lut_gemv_gs": ([P, P, P, I, I, P, I64, P, P, P, I, I64, I64, I, P, I, I, P, I, P, SZ, P], I),
+        "ubw_fit_workspace_bytes": ([I64, I64, ctypes.POINTER(SZ)], I),
+        "ubw_fit_bases": ([P, I, I64, I64, I, I, P, P, P, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -408,6 +410,44 @@ def lut_gemv_multi(gemvs, x, k: int, g: int = 8, accumulate: bool = False):
            lib().ubw_lut_gemv_multi(descs, len(gemvs), k, g, _dev(x, "x", None), _xdtype(x), batch,
                                     1 if accumulate else 0, _stream()))
     return outs
+
+
+def fit_workspace_bytes(n: int, k: int) -> int:
+    out = ctypes.c_size_t()
+    _check("ubw_fit_workspace_bytes", lib().ubw_fit_workspace_bytes(n, k, ctypes.byref(out)))
+    return out.value
+
+
+def fit_bases(w, nb: int, iters: int = 5, residual=None, workspace=None):
+    """Fit nb bases to a dense w [N, K] (fp32 or fp16 tensor on the GPU): residual sign
+    binarization with `iters` alternating least-squares rounds per base. Returns
+    (bits [nb, N, ceil(K/32)] int32 canonical words, alpha_r [nb, N], alpha_c [nb, K],
+    residual [N, K] fp32); bits go to pack_bases(..., src is canonical bits)."""
+    torch = _torch()
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    dt = {torch.float32: 0, torch.float16: 1}.get(w.dtype)
+    if dt is None:
+        raise ValueError("w must be float32 or float16")
+    dev = w.device
+    bits = torch.empty((nb, n, (k + 31) // 32), dtype=torch.int32, device=dev)
+    ar = torch.empty((nb, n), dtype=torch.float32, device=dev)
+    ac = torch.empty((nb, k), dtype=torch.float32, device=dev)
+    if residual is None:
+        residual = torch.empty((n, k), dtype=torch.float32, device=dev)
+    if tuple(residual.shape) != (n, k) or residual.dtype != torch.float32:
+        raise ValueError("residual must be float32 [N, K]")
+    need = fit_workspace_bytes(n, k)
+    if workspace is None:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=dev)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace smaller than fit_workspace_bytes()")
+    _check("ubw_fit_bases", lib().ubw_fit_bases(_dev(w, "w", None), dt, n, k, nb, iters, _dev(bits, "bits", None),
+                                                _dev(ar, "alpha_r", None), _dev(ac, "alpha_c", None),
+                                                _dev(residual, "residual", None), _dev(workspace, "workspace", None),
+                                                need, _stream()))
+    return bits, ar, ac, residual
 
 
 def check_indices(idx_host, k: int) -> None:

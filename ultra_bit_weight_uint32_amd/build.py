@@ -10,7 +10,7 @@ import time
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libubw.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "api.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "fit.hip", "api.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -25,18 +25,34 @@ HIPCC_FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel (one hipcc per file), then link."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
     tmp = LIB + ".tmp"
-    cmd = [hipcc] + HIPCC_FLAGS + ["-o", tmp] + SOURCES
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
     t0 = time.time()
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    jobs, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [hipcc] + compile_flags + ["-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+        objs.append(obj)
     # hipcc's host pass does not know the packed-fp32 feature name and says so; that is noise
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
-    if res.returncode != 0:
+    failed, msgs = False, []
+    for p in jobs:
+        out, _ = p.communicate()
+        msgs += [ln for ln in out.splitlines() if noise not in ln and ln.strip()]
+        failed = failed or p.returncode != 0
+    if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    res = subprocess.run(link, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, LIB)

@@ -11,7 +11,8 @@ using namespace ubw;
 
 namespace {
 
-constexpr int kVersion = 4;
+constexpr int kVersion = 5;
+constexpr int kMaxFitIters = 10000;
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -264,6 +265,27 @@ int ubw_lut_gemv_multi(const ubw_gemv_desc* descs, int count, int64_t K, int g, 
     const int rpl = choose_rows(NTmax, (units + NTmax - 1) / NTmax, batch);
     for (int i = 0; i < count; ++i) args[i].rows_per_group = rpl;
     return hip_status(launch_step_group(args, count, as_stream(stream)));
+}
+
+int ubw_fit_workspace_bytes(int64_t N, int64_t K, size_t* out) {
+    if (!out || !fits_int(N) || !fits_int(K)) return UBW_EINVAL;
+    *out = (size_t)fit_workspace_floats(N, K) * 4;
+    return UBW_OK;
+}
+
+int ubw_fit_bases(const void* w, int w_dtype, int64_t N, int64_t K, int nb, int iters, uint32_t* bits,
+                  float* alpha_r, float* alpha_c, float* residual, void* workspace, size_t ws_bytes, void* stream) {
+    if (!w || !bits || !alpha_r || !alpha_c || !residual || !workspace) return UBW_EINVAL;
+    if (!fits_int(N) || !fits_int(K) || nb < 1 || nb > 64 || iters < 0 || iters > kMaxFitIters) return UBW_EINVAL;
+    if (w_dtype != UBW_F16 && w_dtype != UBW_F32) return UBW_EUNSUPPORTED;
+    if (ceil_div(N, 64) > 65535) return UBW_ERANGE;  // column-sum grid height
+    if ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(bits) | reinterpret_cast<uintptr_t>(alpha_r) |
+         reinterpret_cast<uintptr_t>(alpha_c) | reinterpret_cast<uintptr_t>(residual) |
+         reinterpret_cast<uintptr_t>(workspace)) & 3u)
+        return UBW_EALIGN;
+    if (ws_bytes < (size_t)fit_workspace_floats(N, K) * 4) return UBW_ESIZE;
+    return hip_status(launch_fit(w, w_dtype, (int)N, (int)K, nb, iters, bits, alpha_r, alpha_c, residual,
+                                 (float*)workspace, as_stream(stream)));
 }
 
 int ubw_check_indices(const int32_t* idx_host, int64_t s, int64_t K) {

@@ -83,6 +83,11 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s);
 // Whether every buffer of a step is small enough for the kernel's 32-bit buffer offsets.
 bool step_buffers_fit(const StepArgs& a);
+
+// Offline fit (fit.hip): scratch floats for partial sums, and the launch sequence.
+int64_t fit_workspace_floats(int64_t N, int64_t K);
+hipError_t launch_fit(const void* w, int w_dtype, int N, int K, int nb, int iters, uint32_t* bits, float* alpha_r,
+                      float* alpha_c, float* residual, float* ws, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
 // Largest rows_per_group the GEMV instances support for this batch (4 for batch 1, else 1).
 int max_rows_per_group(int batch);
