@@ -229,3 +229,31 @@ def fit(w, nb, iters):
     res = np.empty((n, k), dtype=np.float64)
     _load().oracle_fit(_ptr(w), n, k, int(nb), int(iters), _ptr(bits), _ptr(ar), _ptr(ac), _ptr(res))
     return bits, ar, ac, res
+
+
+def hessian(x):
+    """H = 2 X^T X for calibration activations x [T, K] (the OBQ proxy Hessian of a linear
+    layer's squared output error), fp64."""
+    x = np.asarray(x).astype(np.float64)
+    return 2.0 * (x.T @ x)
+
+
+def saliency(h, w, s, damp=0.01):
+    """Hessian-guided salient-column search ("1. Algorithm innovation", saliency search: OBQ
+    sensitivities through the inverse Hessian; the columns with the highest scores form the
+    mask). Reading: H_d = H + lambda I with lambda = damp * mean(diag H) (1 when that is 0);
+    d_j = [H_d^-1]_jj; the OBQ error of removing weight w_rj is w_rj^2 / d_j, and its
+    second-order sensitivity score is w_rj^2 / d_j^2, summed over the rows of a column:
+    score_j = sum_r w_rj^2 / d_j^2. The s columns with the largest scores (ties: lower index
+    first) are returned ascending. Returns (d, score, idx)."""
+    h = np.array(h, dtype=np.float64)
+    k = h.shape[0]
+    lam = damp * float(np.mean(np.diag(h)))
+    if lam == 0.0:
+        lam = 1.0
+    h[np.diag_indices(k)] += lam
+    d = np.diag(np.linalg.inv(h)).copy()
+    score = (np.asarray(w, dtype=np.float64) ** 2).sum(axis=0) / (d * d)
+    order = np.lexsort((np.arange(k), -score))
+    idx = np.sort(order[:s]).astype(np.int32)
+    return d, score, idx

@@ -412,3 +412,58 @@ def test_fit_bases_follow_the_residual():
     signs = dense_signs(bits, 130).astype(np.float64)
     w_hat = sum(np.outer(ar[k], ac[k]) * signs[k] for k in range(3))
     assert np.allclose(w.astype(np.float64) - w_hat, res, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# Hessian-guided saliency
+
+def test_hessian_integer_gram():
+    rng = np.random.default_rng(300)
+    x = rng.integers(-5, 6, size=(40, 17))
+    h = oracle.hessian(x.astype(np.float16))
+    assert np.array_equal(h, 2.0 * (x.T.astype(np.int64) @ x).astype(np.float64))
+
+
+def test_saliency_orthogonal_columns_closed_form():
+    """Columns of X orthogonal: H = diag(2 c_j), so [H_d^-1]_jj = 1 / (2 c_j + lambda) and the
+    score is sum_r w_rj^2 (2 c_j + lambda)^2."""
+    rng = np.random.default_rng(301)
+    q, _ = np.linalg.qr(rng.standard_normal((64, 16)))
+    c = rng.uniform(0.5, 3, 16)
+    x = q * np.sqrt(c)                       # x^T x = diag(c)
+    w = rng.standard_normal((9, 16))
+    h = oracle.hessian(x)
+    lam = 0.05 * np.mean(2 * c)
+    d, score, idx = oracle.saliency(h, w, 5, damp=0.05)
+    assert np.allclose(d, 1 / (2 * c + lam), rtol=1e-10)
+    expect = (w ** 2).sum(axis=0) * (2 * c + lam) ** 2
+    assert np.allclose(score, expect, rtol=1e-10)
+    assert np.array_equal(idx, np.sort(np.argsort(-expect)[:5]))
+
+
+def test_saliency_two_by_two_by_hand():
+    """H = [[4, 2], [2, 3]], damp 0.5 -> lambda = 0.5 * 3.5 = 1.75, H_d = [[5.75, 2], [2, 4.75]],
+    det = 23.3125, [H_d^-1]_00 = 4.75 / 23.3125, [H_d^-1]_11 = 5.75 / 23.3125."""
+    h = np.array([[4.0, 2.0], [2.0, 3.0]])
+    w = np.array([[1.0, 2.0], [3.0, -1.0]])    # column sums of squares: 10, 5
+    d, score, idx = oracle.saliency(h, w, 1, damp=0.5)
+    det = 5.75 * 4.75 - 4.0
+    assert np.allclose(d, [4.75 / det, 5.75 / det], rtol=1e-14)
+    assert np.allclose(score, [10 / d[0] ** 2, 5 / d[1] ** 2], rtol=1e-14)
+    assert idx.tolist() == [0]
+
+
+def test_saliency_permutation_and_ties():
+    rng = np.random.default_rng(302)
+    x = rng.standard_normal((50, 30))
+    w = rng.standard_normal((8, 30))
+    d, score, idx = oracle.saliency(oracle.hessian(x), w, 7)
+    p = rng.permutation(30)
+    dp, sp, ip = oracle.saliency(oracle.hessian(x[:, p]), w[:, p], 7)
+    assert np.allclose(dp, d[p], rtol=1e-9) and np.allclose(sp, score[p], rtol=1e-9)
+    assert np.array_equal(np.sort(p[ip]), idx)
+    # equal scores: the lower index wins; s = K selects every column
+    h = np.eye(4) * 2.0
+    w = np.ones((3, 4))
+    assert oracle.saliency(h, w, 2)[2].tolist() == [0, 1]
+    assert oracle.saliency(h, w, 4)[2].tolist() == [0, 1, 2, 3]
