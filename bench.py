@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs", action="store_true",
                     help="instead of the headline line: time every GEMV and layer of the 7B MLP (config 4) and the "
-                         "70B layer (config 5) at their batches, the group-scale variant and the offline fit, one JSON line each")
+                         "70B layer (config 5) at their batches, the group-scale variant, the offline fit and the saliency search")
     ap.add_argument("--profile-run", action="store_true",
                     help="for hardware-counter runs: a 64 MiB device copy (known bytes, to scale the counters) "
                          "then --steps cold steps; prints one line, no timing")
@@ -85,6 +85,7 @@ def main():
         config_sweep(torch, ubw, dev)
         gs_sweep(torch, ubw, dev)
         fit_sweep(torch, ubw, dev)
+        saliency_sweep(torch, ubw, dev)
         return
     wl = config3(seed=0)
     g = wl.gemvs[0]
@@ -399,6 +400,39 @@ def fit_sweep(torch, ubw, dev):
                           "algorithmic_bytes": by, "oracle_s": round(cpu, 3), "oracle_cores": oracle.max_threads()}),
               flush=True)
         del wt, res, ws
+        torch.cuda.empty_cache()
+
+
+def saliency_sweep(torch, ubw, dev):
+    """Hessian-guided salient-column search at the 7B projection (K = 4096) and the 70B q/o
+    (K = 8192) shapes, 2048 calibration rows: the Gram matrix on the matrix cores (TFLOP/s
+    against the fp16 dense peak) and the whole search (damped Cholesky, inverse diagonal,
+    scores, selection); the oracle (numpy fp64) is timed beside the first."""
+    import oracle
+    rng = np.random.default_rng(7)
+    for k, n, s in ((4096, 4096, 205), (8192, 8192, 410)):
+        t = 2048
+        x = torch.from_numpy((rng.standard_normal((t, k)) * rng.uniform(0.2, 2, (1, k))).astype(np.float16)).to(dev)
+        w = torch.from_numpy(rng.standard_normal((n, k)).astype(np.float32)).to(dev)
+        h = torch.empty((k, k), dtype=torch.float32, device=dev)
+        ws = torch.empty(ubw.saliency_workspace_bytes(n, k) // 4, dtype=torch.float32, device=dev)
+        ubw.gram(x, out=h)
+        reps = 10
+        gms = run_queued(torch, lambda i: ubw.gram(x, out=h), reps) / reps
+        flops = 2.0 * t * k * k
+        ubw.hessian_saliency(h, w, s, workspace=ws)
+        ms = run_queued(torch, lambda i: (ubw.gram(x, out=h), ubw.hessian_saliency(h, w, s, workspace=ws)), 3) / 3
+        line = {"sweep": "hessian saliency", "K": k, "T": t, "N": n, "s": s, "gram_ms": round(gms, 3),
+                "gram_TFLOPs": round(flops / gms / 1e9, 1), "gram_pct_of_fp16_peak": round(flops / gms / 1e9 / 2500 * 100, 2),
+                "search_ms": round(ms, 3)}
+        if k == 4096:
+            xh = x.cpu().numpy()
+            wh = w.cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.saliency(oracle.hessian(xh), wh, s)
+            line["oracle_s"] = round(time.perf_counter() - t0, 3)
+        print(json.dumps(line), flush=True)
+        del x, w, h, ws
         torch.cuda.empty_cache()
 
 

@@ -276,6 +276,41 @@ int ubw_fit_bases(const void* w, int w_dtype, int64_t N, int64_t K, int nb, int 
                   void* stream);
 
 /*
+ * Gram matrix of calibration activations on the matrix cores: H = scale * X^T X, the proxy
+ * Hessian 2 X^T X of a linear layer's squared output error when scale = 2 (input to
+ * ubw_hessian_saliency).
+ *   x   fp16 [T][K] (UBW_F16 only), row-major;  H  OUT fp32 [K][K], both triangles written
+ * Errors: UBW_EINVAL (null, T or K < 1), UBW_EUNSUPPORTED (x_dtype), UBW_ERANGE (K above
+ *         8,388,480), UBW_EALIGN (x not 2-, H not 4-byte aligned), UBW_EHIP.
+ */
+int ubw_gram(const void* x, int x_dtype, int64_t T, int64_t K, float scale, float* H, void* stream);
+
+/*
+ * Hessian-guided salient-column search. Section "1. Algorithm innovation", saliency search:
+ * weight sensitivities come from the inverse Hessian (Optimal Brain Quantization) and the
+ * highest-scoring columns form the salient mask. The page gives no formula; read as
+ *   H_d = H + lambda I, lambda = damp * mean(diag H) (1 when that mean is not positive)
+ *   d_j = [H_d^-1]_jj,  score_j = sum_r W[r][j]^2 / d_j^2
+ *   idx = the s columns with the highest scores (equal scores: lower index first), ascending
+ * computed by a blocked fp32 Cholesky of H_d and a blocked triangular solve for diag(H_d^-1).
+ *   H          IN symmetric [K][K] fp32 (e.g. from ubw_gram); OUT its lower triangle holds the
+ *              Cholesky factor of H_d (the upper triangle is left partly updated)
+ *   W          fp32 [N][K], the layer's dense weights
+ *   d, score   OUT fp32 [K];  idx OUT int32 [s], 1 <= s <= K
+ *   workspace  ubw_saliency_workspace_bytes(N, K) bytes (about 2 K^2 + N K / 16 bytes:
+ *              the factor's block inverses and the triangular solve's blocks), caller-owned.
+ *              On return its float 0 holds lambda and float 1 an error code: 0 none, 1 a
+ *              pivot was not positive (H_d not positive definite in fp32), 2 the selection
+ *              did not find exactly s columns (NaN scores).
+ * Errors: UBW_EINVAL (null, sizes, s, damp negative or not finite), UBW_ERANGE (N above
+ *         4,194,240), UBW_EALIGN (a pointer not 4-byte aligned), UBW_ESIZE, UBW_EHIP.
+ */
+int ubw_saliency_workspace_bytes(int64_t N, int64_t K, size_t* out);
+int ubw_hessian_saliency(float* H, int64_t K, float damp, const float* W, int64_t N, int64_t s,
+                         float* d, float* score, int32_t* idx, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/*
  * Host-side check of a salient index list: every idx[q] in [0, K) and strictly ascending.
  * idx is a HOST pointer. Returns UBW_OK or UBW_ERANGE (UBW_EINVAL for null / s < 1).
  */

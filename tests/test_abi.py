@@ -226,6 +226,31 @@ def test_fit_rejects():
         assert L.ubw_fit_bases(*a.values()) == status, kw
 
 
+def test_saliency_rejects():
+    L = ubw.lib()
+    assert L.ubw_gram(None, 1, 10, 10, 2.0, FAKE, None) == EINVAL
+    assert L.ubw_gram(FAKE, 1, 0, 10, 2.0, FAKE, None) == EINVAL
+    assert L.ubw_gram(FAKE, 0, 10, 10, 2.0, FAKE, None) == EUNSUP          # fp16 only
+    assert L.ubw_gram(ctypes.c_void_p(0x10001), 1, 10, 10, 2.0, FAKE, None) == EALIGN
+    assert L.ubw_gram(FAKE, 1, 10, 65535 * 128 + 1, 2.0, FAKE, None) == ERANGE
+    sz = ctypes.c_size_t()
+    assert L.ubw_saliency_workspace_bytes(100, 0, ctypes.byref(sz)) == EINVAL
+    assert L.ubw_saliency_workspace_bytes(100, 300, ctypes.byref(sz)) == 0
+    nblk = 5
+    assert sz.value == 4 * (16 + nblk * 4096 + 4096 * nblk * (nblk + 1) // 2 + 2 * 300 + 300)
+    need = sz.value
+    args = dict(H=FAKE, K=300, damp=0.01, W=FAKE, N=100, s=10, d=FAKE, score=FAKE, idx=FAKE, ws=FAKE, wsb=need,
+                stream=None)
+    for kw, status in [(dict(H=None), EINVAL), (dict(idx=None), EINVAL), (dict(ws=None), EINVAL), (dict(s=0), EINVAL),
+                       (dict(s=301), EINVAL), (dict(K=0), EINVAL), (dict(damp=-1.0), EINVAL),
+                       (dict(damp=float("nan")), EINVAL), (dict(damp=float("inf")), EINVAL),
+                       (dict(W=ctypes.c_void_p(0x10002)), EALIGN), (dict(wsb=need - 4), ESIZE),
+                       (dict(N=65535 * 64 + 1, wsb=1 << 45), ERANGE)]:
+        a = dict(args)
+        a.update(kw)
+        assert L.ubw_hessian_saliency(*a.values()) == status, kw
+
+
 def test_other_entry_points_reject():
     L = ubw.lib()
     assert L.ubw_pack_bases(None, 0, 1, 8, 8, 8, FAKE, None) == EINVAL

@@ -699,3 +699,78 @@ def test_fit_output_drives_the_gemv():
     y = ubw.lut_gemv(packed, ar, ac, dev(x), n, k, workspace=ubw.workspace(n, DEV))
     r = oracle.gemv(host(bits).view(np.uint32), host(ar), host(ac), x)
     assert max_rel_err(host(y), r) <= TOL
+
+
+# ------------------------------------------------------------------------------------------
+# Hessian-guided saliency: Gram matrix on the matrix cores, blocked Cholesky, selection
+
+@pytest.mark.parametrize("t,k", [(300, 200), (1, 129), (32, 128), (2048, 512), (77, 1000)])
+def test_gram_integer_exact(t, k):
+    """Integer activations: every product and partial sum is an integer below 2^24, so the
+    matrix-core result is exact (pins the operand and result lane layouts)."""
+    rng = np.random.default_rng(t + k)
+    x = rng.integers(-4, 5, size=(t, k)).astype(np.float16)
+    h = host(ubw.gram(dev(x)))
+    assert np.array_equal(h.astype(np.float64), oracle.hessian(x))
+
+
+def test_gram_float():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((1024, 1000)).astype(np.float16)
+    h = host(ubw.gram(dev(x))).astype(np.float64)
+    r = oracle.hessian(x)
+    assert np.abs(h - r).max() <= 1e-5 * np.abs(r).max()
+
+
+def check_saliency(x, w, s, damp=0.01):
+    hd = ubw.gram(dev(x))
+    h_in = host(hd).astype(np.float64)
+    d, score, idx, ws = ubw.hessian_saliency(hd, dev(w), s, damp=damp)
+    d, score, idx, ws, L = host(d), host(score), host(idx), host(ws), np.tril(host(hd).astype(np.float64))
+    assert ws[1] == 0
+    od, oscore, oidx = oracle.saliency(h_in, w, s, damp=damp)
+    k = len(d)
+    lam = damp * np.mean(np.diag(h_in))
+    assert abs(ws[0] - lam) <= 1e-5 * lam
+    # the factor: L L^T = H + lambda I
+    hd64 = h_in + lam * np.eye(k)
+    assert np.abs(L @ L.T - hd64).max() <= 2e-7 * max(k, 500) * np.abs(hd64).max()
+    assert max_rel_err(d, od) <= 1e-3
+    assert max_rel_err(score, oscore) <= 2e-3
+    # the selection is exactly the top s of the GPU's own scores (ties: lower index)...
+    own = np.sort(np.lexsort((np.arange(k), -score.astype(np.float64)))[:s])
+    assert np.array_equal(idx, own)
+    # ...and differs from the oracle's only at scores within rounding of the boundary
+    bound = np.sort(oscore)[::-1][s - 1]
+    for j in set(idx.tolist()) ^ set(oidx.tolist()):
+        assert abs(oscore[j] - bound) <= 4e-3 * bound, j
+    return idx
+
+
+@pytest.mark.parametrize("t,k,n,s", [(500, 64, 40, 5), (300, 300, 100, 31), (2000, 1000, 300, 50), (100, 700, 50, 70),
+                                     (1000, 1, 3, 1)])
+def test_saliency_matches_oracle(t, k, n, s):
+    rng = np.random.default_rng(t + k + n)
+    x = (rng.standard_normal((t, k)) * rng.uniform(0.2, 2, (1, k))).astype(np.float16)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    check_saliency(x, w, s)
+
+
+def test_saliency_7b_projection_shape():
+    """K = 4096 with 2048 synthetic calibration rows (fewer than K: H is singular and only the
+    damping makes it definite), a dense 4096 x 4096 W, 205 salient columns (5%)."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((2048, 4096)) * rng.uniform(0.2, 2, (1, 4096))).astype(np.float16)
+    w = rng.standard_normal((4096, 4096)).astype(np.float32)
+    idx = check_saliency(x, w, 205)
+    ubw.check_indices(idx, 4096)
+
+
+def test_saliency_flags_a_matrix_that_is_not_definite():
+    """-2 I: the mean of the diagonal is negative, so lambda = 1 and H_d = -I has no Cholesky
+    factor: the error code is set (the kernels still finish)."""
+    k = 100
+    h = torch.from_numpy(-2.0 * np.eye(k, dtype=np.float32)).to(DEV)
+    w = torch.ones((4, k), device=DEV)
+    _, _, _, ws = ubw.hessian_saliency(h, w, 10)
+    assert host(ws)[1] != 0

@@ -29,6 +29,7 @@ EXPORTS = (
     "ubw_build_lut", "ubw_workspace_bytes", "ubw_lut_gemv", "ubw_vcm_gather_refine", "ubw_lut_gemv_refined",
     "ubw_check_indices", "ubw_extract_patterns", "ubw_lut_gemv_geometry", "ubw_bench_stream_read",
     "ubw_lut_gemv_multi", "ubw_lut_gemv_gs", "ubw_fit_workspace_bytes", "ubw_fit_bases",
+    "ubw_gram", "ubw_saliency_workspace_bytes", "ubw_hessian_saliency",
 )
 
 
@@ -79,6 +80,9 @@ def lib():
         "ubw_lut_gemv_gs": ([P, P, P, I, I, P, I64, P, P, P, I, I64, I64, I, P, I, I, P, I, P, SZ, P], I),
         "ubw_fit_workspace_bytes": ([I64, I64, ctypes.POINTER(SZ)], I),
         "ubw_fit_bases": ([P, I, I64, I64, I, I, P, P, P, P, P, SZ, P], I),
+        "ubw_gram": ([P, I, I64, I64, ctypes.c_float, P, P], I),
+        "ubw_saliency_workspace_bytes": ([I64, I64, ctypes.POINTER(SZ)], I),
+        "ubw_hessian_saliency": ([P, I64, ctypes.c_float, P, I64, I64, P, P, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -448,6 +452,53 @@ def fit_bases(w, nb: int, iters: int = 5, residual=None, workspace=None):
                                                 _dev(residual, "residual", None), _dev(workspace, "workspace", None),
                                                 need, _stream()))
     return bits, ar, ac, residual
+
+
+def gram(x, scale: float = 2.0, out=None):
+    """H = scale * x^T x on the matrix cores; x fp16 [T, K] on the GPU. Returns H fp32 [K, K]."""
+    torch = _torch()
+    if x.dim() != 2 or x.dtype != torch.float16:
+        raise ValueError("x must be float16 [T, K]")
+    t, k = x.shape
+    if out is None:
+        out = torch.empty((k, k), dtype=torch.float32, device=x.device)
+    if tuple(out.shape) != (k, k) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [K, K]")
+    _check("ubw_gram", lib().ubw_gram(_dev(x, "x", None), 1, t, k, float(scale), _dev(out, "H", None), _stream()))
+    return out
+
+
+def saliency_workspace_bytes(n: int, k: int) -> int:
+    out = ctypes.c_size_t()
+    _check("ubw_saliency_workspace_bytes", lib().ubw_saliency_workspace_bytes(n, k, ctypes.byref(out)))
+    return out.value
+
+
+def hessian_saliency(h, w, s: int, damp: float = 0.01, workspace=None):
+    """Salient columns from the Hessian h [K, K] fp32 (overwritten: its lower triangle becomes
+    the damped Cholesky factor) and the dense weights w [N, K] fp32. Returns (d [K] = diag of
+    the damped inverse, score [K], idx [s] int32 ascending, workspace); workspace[0] holds the
+    damping lambda and workspace[1] an error code (0 = none)."""
+    torch = _torch()
+    k = h.shape[0]
+    if tuple(h.shape) != (k, k) or h.dtype != torch.float32:
+        raise ValueError("h must be float32 [K, K]")
+    if w.dim() != 2 or w.shape[1] != k or w.dtype != torch.float32:
+        raise ValueError("w must be float32 [N, K]")
+    n = w.shape[0]
+    need = saliency_workspace_bytes(n, k)
+    if workspace is None:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=h.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace smaller than saliency_workspace_bytes()")
+    d = torch.empty(k, dtype=torch.float32, device=h.device)
+    score = torch.empty(k, dtype=torch.float32, device=h.device)
+    idx = torch.empty(s, dtype=torch.int32, device=h.device)
+    _check("ubw_hessian_saliency",
+           lib().ubw_hessian_saliency(_dev(h, "h", None), k, float(damp), _dev(w, "w", None), n, s, _dev(d, "d", None),
+                                      _dev(score, "score", None), _dev(idx, "idx", None),
+                                      _dev(workspace, "workspace", None), need, _stream()))
+    return d, score, idx, workspace
 
 
 def check_indices(idx_host, k: int) -> None:

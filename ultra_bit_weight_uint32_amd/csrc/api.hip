@@ -11,7 +11,7 @@ using namespace ubw;
 
 namespace {
 
-constexpr int kVersion = 5;
+constexpr int kVersion = 6;
 constexpr int kMaxFitIters = 10000;
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -286,6 +286,35 @@ int ubw_fit_bases(const void* w, int w_dtype, int64_t N, int64_t K, int nb, int 
     if (ws_bytes < (size_t)fit_workspace_floats(N, K) * 4) return UBW_ESIZE;
     return hip_status(launch_fit(w, w_dtype, (int)N, (int)K, nb, iters, bits, alpha_r, alpha_c, residual,
                                  (float*)workspace, as_stream(stream)));
+}
+
+int ubw_gram(const void* x, int x_dtype, int64_t T, int64_t K, float scale, float* H, void* stream) {
+    if (!x || !H || !fits_int(T) || !fits_int(K)) return UBW_EINVAL;
+    if (x_dtype != UBW_F16) return UBW_EUNSUPPORTED;
+    if (ceil_div(K, 128) > 65535) return UBW_ERANGE;
+    if ((reinterpret_cast<uintptr_t>(x) & 1u) || (reinterpret_cast<uintptr_t>(H) & 3u)) return UBW_EALIGN;
+    return hip_status(launch_gram(x, (int)T, (int)K, scale, H, as_stream(stream)));
+}
+
+int ubw_saliency_workspace_bytes(int64_t N, int64_t K, size_t* out) {
+    if (!out || !fits_int(N) || !fits_int(K)) return UBW_EINVAL;
+    *out = (size_t)saliency_workspace_floats(N, K) * 4;
+    return UBW_OK;
+}
+
+int ubw_hessian_saliency(float* H, int64_t K, float damp, const float* W, int64_t N, int64_t s, float* d,
+                         float* score, int32_t* idx, void* workspace, size_t ws_bytes, void* stream) {
+    if (!H || !W || !d || !score || !idx || !workspace) return UBW_EINVAL;
+    if (!fits_int(K) || !fits_int(N) || s < 1 || s > K) return UBW_EINVAL;
+    if (!(damp >= 0.f) || !(damp < 1e30f)) return UBW_EINVAL;
+    if (ceil_div(N, 64) > 65535) return UBW_ERANGE;
+    if ((reinterpret_cast<uintptr_t>(H) | reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(d) |
+         reinterpret_cast<uintptr_t>(score) | reinterpret_cast<uintptr_t>(idx) |
+         reinterpret_cast<uintptr_t>(workspace)) & 3u)
+        return UBW_EALIGN;
+    if (ws_bytes < (size_t)saliency_workspace_floats(N, K) * 4) return UBW_ESIZE;
+    return hip_status(launch_saliency(H, (int)K, damp, W, (int)N, (int)s, d, score, idx, (float*)workspace,
+                                      as_stream(stream)));
 }
 
 int ubw_check_indices(const int32_t* idx_host, int64_t s, int64_t K) {

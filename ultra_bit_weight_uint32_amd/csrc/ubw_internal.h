@@ -84,6 +84,12 @@ hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s);
 // Whether every buffer of a step is small enough for the kernel's 32-bit buffer offsets.
 bool step_buffers_fit(const StepArgs& a);
 
+// Hessian-guided saliency (saliency.hip).
+hipError_t launch_gram(const void* x, int T, int K, float scale, float* H, hipStream_t s);
+int64_t saliency_workspace_floats(int64_t N, int64_t K);
+hipError_t launch_saliency(float* H, int K, float damp, const float* W, int N, int s, float* d, float* score,
+                           int32_t* idx, float* ws, hipStream_t st);
+
 // Offline fit (fit.hip): scratch floats for partial sums, and the launch sequence.
 int64_t fit_workspace_floats(int64_t N, int64_t K);
 hipError_t launch_fit(const void* w, int w_dtype, int N, int K, int nb, int iters, uint32_t* bits, float* alpha_r,
