@@ -59,7 +59,8 @@ typedef enum {
 enum { UBW_F32 = 0, UBW_F16 = 1 };                       /* activation dtypes */
 enum { UBW_SRC_CANON_BITS = 0, UBW_SRC_INT8_SIGNS = 1 };  /* ubw_pack_bases sources */
 
-/* Largest batch one GEMV call accepts. */
+/* Largest batch one GEMV call accepts. Batches above 4 rows are processed as consecutive
+ * launches of 4 activation rows each on the call's stream. */
 #define UBW_MAX_BATCH 16
 /* columns per row scale in ubw_lut_gemv_gs */
 #define UBW_GROUP_COLS 128

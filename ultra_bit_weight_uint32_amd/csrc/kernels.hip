@@ -596,15 +596,14 @@ __device__ __forceinline__ uint32_t range_start(const StepParams& P, uint32_t g)
 // The body of a step: workgroup g of the P.G that work on the GEMV described by P.
 template <typename XT, int RPL, int BMAX, bool XL, bool GS>
 __device__ __forceinline__ void step_body(const StepParams& P, int g) {
-    // Batches above 2 keep their per-row accumulators in thread-private LDS slots (registers
-    // indexed by a runtime batch index would go to scratch).
-    constexpr bool kAccLds = BMAX > 2;
+    // Per-row partial sums live in registers, one per (row tile, activation row): the batch
+    // loops below are unrolled over BMAX (at most kBatchChunk) with a runtime bound, so every
+    // index is a constant.
+    static_assert(BMAX <= kBatchChunk, "larger batches run as chunks");
     __shared__ __align__(16) float s_tab[256 * 64];       // one unit's 64 tables: 64 KiB
     __shared__ __align__(16) float s_v[BMAX * 2 * 256];   // scaled activations [b][item][column]
-    __shared__ __align__(16) float s_acc[kAccLds ? RPL * BMAX * kStepThreads : 1];
     lds_f32* tab = (lds_f32*)s_tab;
     lds_f32* sv = (lds_f32*)s_v;
-    lds_f32* sacc = (lds_f32*)s_acc;
     lds_cchar* tb = (lds_cchar*)s_tab;
     const StepArgs& a = P.a;
     // The parameter block spans four 64-byte lines of the scalar cache, and every fetch of a
@@ -679,16 +678,12 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         }
     };
 
-    float acc[RPL][kAccLds ? 1 : BMAX];
+    float acc[RPL][BMAX];
     auto clear_acc = [&]() {
 #pragma unroll
         for (int j = 0; j < RPL; ++j)
 #pragma unroll
-            for (int b = 0; b < (kAccLds ? 1 : BMAX); ++b) acc[j][b] = 0.f;
-        if (kAccLds) {
-#pragma unroll
-            for (int i = 0; i < RPL * BMAX; ++i) sacc[i * kStepThreads + tid] = 0.f;  // own slots only
-        }
+            for (int b = 0; b < BMAX; ++b) acc[j][b] = 0.f;
     };
     clear_acc();
 
@@ -745,8 +740,7 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
                 if (b >= a.batch) continue;
-                const float part = kAccLds ? sacc[(j * BMAX + b) * kStepThreads + tid] : acc[j][kAccLds ? 0 : b];
-                const uint32_t pv = __float_as_uint(part);
+                const uint32_t pv = __float_as_uint(acc[j][b]);
                 const auto sw = __builtin_amdgcn_permlane32_swap(pv, pv, false, false);
                 const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
                 if (h == 0 && rv) {
@@ -820,23 +814,13 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
                 if (b < a.batch) sv[b * 512 + tid] = U.ac * to_f32(U.xv[b]);
         }
         __syncthreads();
-        if constexpr (!kAccLds) {
 #pragma unroll
-            for (int b = 0; b < BMAX; ++b) {
-                if (b < a.batch) {
-                    float S[RPL];
-                    row_pass(U, mine, last, cu.rg, b, std::integral_constant<bool, SI == 0 && GS>{}, S);
-#pragma unroll
-                    for (int j = 0; j < RPL; ++j) acc[j][kAccLds ? 0 : b] += S[j];
-                    __syncthreads();
-                }
-            }
-        } else {
-            for (int b = 0; b < a.batch; ++b) {
+        for (int b = 0; b < BMAX; ++b) {
+            if (b < a.batch) {
                 float S[RPL];
                 row_pass(U, mine, last, cu.rg, b, std::integral_constant<bool, SI == 0 && GS>{}, S);
 #pragma unroll
-                for (int j = 0; j < RPL; ++j) sacc[(j * BMAX + b) * kStepThreads + tid] += S[j];
+                for (int j = 0; j < RPL; ++j) acc[j][b] += S[j];
                 __syncthreads();
             }
         }
@@ -904,7 +888,7 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
 // tiles and batch up to 4 stay within. (Asking for 4 waves per SIMD instead makes the compiler
 // issue the table lookups in smaller batches, which costs more than it gains.)
 template <typename XT, int RPL, int BMAX, bool XL, bool GS>
-__global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8(StepParams P) {
+__global__ __launch_bounds__(kStepThreads, 2) void k_gemv8(StepParams P) {
     step_body<XT, RPL, BMAX, XL, GS>(P, (int)blockIdx.x);
 }
 
@@ -917,7 +901,7 @@ struct GroupParams {
 };
 
 template <typename XT, int RPL, int BMAX, bool XL>
-__global__ __launch_bounds__(kStepThreads, (BMAX <= 4 ? 2 : 1)) void k_gemv8_group(GroupParams GP) {
+__global__ __launch_bounds__(kStepThreads, 2) void k_gemv8_group(GroupParams GP) {
     const int b = (int)blockIdx.x;
     int i = 0;
     while (i + 1 < GP.count && b >= GP.start[i + 1]) ++i;
@@ -1113,16 +1097,30 @@ static hipError_t dispatch_instance(int batch, int rpl, bool xl, F f) {
         return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 1>{}, std::false_type{});
     }
     if (batch <= 2) return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 2>{}, std::false_type{});
-    if (batch <= 4) return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 4>{}, std::false_type{});
-    if (batch <= 8) return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 8>{}, std::false_type{});
-    return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 16>{}, std::false_type{});
+    if (batch <= kBatchChunk) return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 4>{}, std::false_type{});
+    return hipErrorInvalidValue;  // larger batches run as chunks of kBatchChunk rows
 }
 
-// The gather of a refinement segment goes through LDS when the activation block fits (in whole
-// 16-byte pieces, so that no load straddles the end of x).
+// The gather of a refinement segment goes through LDS when the activation block fits (in whole,
+// aligned 16-byte pieces, so that no load straddles the end of x).
 static bool gather_in_lds(const StepArgs& a) {
     const uint64_t xbytes = (uint64_t)a.batch * (uint64_t)a.ldx * (a.x_dtype == UBW_F16 ? 2u : 4u);
-    return xbytes <= kXlBytes && xbytes % 16 == 0;
+    return xbytes <= kXlBytes && xbytes % 16 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15u) == 0;
+}
+
+// Batches above kBatchChunk rows run as consecutive launches of at most kBatchChunk activation
+// rows each (the weights are read once per chunk). Per activation row a launch builds and
+// searches its tables again, so a chunk costs the same per row as one launch of the whole
+// batch would; what chunking keeps is the 4-row instance's footprint (80 KiB of LDS, two
+// workgroups per CU), which measured twice as fast per row as 8- or 16-row instances holding
+// one workgroup per CU.
+static StepArgs batch_chunk(const StepArgs& a, int r0) {
+    StepArgs c = a;
+    const int64_t xs = a.x_dtype == UBW_F16 ? 2 : 4;
+    c.x = static_cast<const char*>(a.x) + (int64_t)r0 * a.ldx * xs;
+    c.y = a.y + (int64_t)r0 * a.N;
+    c.batch = a.batch - r0 < kBatchChunk ? a.batch - r0 : kBatchChunk;
+    return c;
 }
 
 int max_rows_per_group(int batch) { return batch <= 1 ? 4 : 1; }
@@ -1174,7 +1172,7 @@ static hipError_t make_params(const StepArgs& a, StepParams& P) {
     return hipSuccess;
 }
 
-hipError_t launch_step(const StepArgs& a, hipStream_t s) {
+static hipError_t launch_step_rows(const StepArgs& a, hipStream_t s) {
     StepParams P;
     hipError_t e = make_params(a, P);
     if (e != hipSuccess) return e;
@@ -1197,7 +1195,16 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s) {
 }
 
 // Several GEMVs that share x, batch, dtype and rows_per_group, in one launch.
-hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s) {
+hipError_t launch_step(const StepArgs& a, hipStream_t s) {
+    if (a.batch <= kBatchChunk) return launch_step_rows(a, s);
+    for (int r0 = 0; r0 < a.batch; r0 += kBatchChunk) {
+        hipError_t e = launch_step_rows(batch_chunk(a, r0), s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+static hipError_t launch_step_group_rows(const StepArgs* a, int count, hipStream_t s) {
     if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
     GroupParams GP{};
     GP.count = count;
@@ -1217,6 +1224,18 @@ hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s) {
     };
     if (a[0].x_dtype == UBW_F16) return dispatch_instance<__half>(a[0].batch, a[0].rows_per_group, xl, go);
     return dispatch_instance<float>(a[0].batch, a[0].rows_per_group, xl, go);
+}
+
+hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
+    if (a[0].batch <= kBatchChunk) return launch_step_group_rows(a, count, s);
+    for (int r0 = 0; r0 < a[0].batch; r0 += kBatchChunk) {
+        StepArgs c[kMaxGroup];
+        for (int i = 0; i < count; ++i) c[i] = batch_chunk(a[i], r0);
+        hipError_t e = launch_step_group_rows(c, count, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace ubw

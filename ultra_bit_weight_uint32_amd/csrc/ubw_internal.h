@@ -31,6 +31,7 @@ constexpr int kSliceCols = 256;
 constexpr int kTileWords = kTileRows * kSliceWords;  // 2048 words = 8 KiB per base per tile
 constexpr int kThreads = 256;
 constexpr int kMaxGroup = UBW_MAX_GROUP;  // GEMVs per grouped launch
+constexpr int kBatchChunk = 4;          // activation rows per launch (larger batches: several)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
