@@ -100,13 +100,10 @@ def test_geometry_rejects():
     assert L.ubw_lut_gemv_geometry(*base, 3, 1, *tail) == ERANGE      # rows_per_group not in {1,2,4}
     assert L.ubw_lut_gemv_geometry(*base, 8, 1, *tail) == ERANGE
     assert L.ubw_lut_gemv_geometry(*base, 1, -1, *tail) == ERANGE     # workgroups < 0
-    b2 = list(base)
-    b2[10] = 2                                                        # batch 2 allows only 1 row tile
-    assert L.ubw_lut_gemv_geometry(*b2, 4, 1, *tail) == ERANGE
-    assert L.ubw_lut_gemv_geometry(*b2, 2, 1, *tail) == ERANGE
-    b4 = list(base)
-    b4[10] = 4                                                        # batch 4 allows only 1 row tile
-    assert L.ubw_lut_gemv_geometry(*b4, 2, 1, *tail) == ERANGE
+    for batch in (2, 4, 16):                                          # batches: 1 or 2 row tiles
+        bb = list(base)
+        bb[10] = batch
+        assert L.ubw_lut_gemv_geometry(*bb, 4, 1, *tail) == ERANGE
     vcm = list(base)
     vcm[13] = 1                                                       # vcm without idx
     assert L.ubw_lut_gemv_geometry(*vcm, 1, 1, *tail) == EINVAL

@@ -198,8 +198,6 @@ def test_gemv_geometries_batched(batch):
     n, k = 3 * 256 + 5, 3 * 256 + 1
     g = make_integer_gemv(rng, n, k, 3, batch=batch)
     for rpg in (1, 2):
-        if rpg > 1 and batch > 1:
-            continue
         for wgs in (1, 4, 0):
             y = torch.zeros((batch, n), device=DEV)
             ubw.lut_gemv_geometry(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y,
@@ -278,7 +276,8 @@ def test_vcm_integer_exact(k, s, batch, ns):
 
 def test_vcm_geometries_integer_exact():
     n, k, s = 600, 3000, 700
-    for batch, rpg, wgs in ((2, 1, 0), (2, 1, 1), (2, 1, 3), (1, 2, 3), (1, 2, 0), (1, 4, 5), (1, 1, 7)):
+    for batch, rpg, wgs in ((2, 1, 0), (2, 1, 1), (2, 1, 3), (1, 2, 3), (1, 2, 0), (1, 4, 5), (1, 1, 7), (2, 2, 0),
+                            (3, 2, 3), (7, 2, 0)):
         rng = np.random.default_rng(21 + batch)
         g = make_integer_gemv(rng, n, k, 1, s=s, ns=2, batch=batch)
         ps = pack(g.bits_s, s)

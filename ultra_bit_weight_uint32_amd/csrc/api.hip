@@ -23,14 +23,14 @@ int64_t packed_words_of(int nb, int64_t N, int64_t K) {
     return (int64_t)nb * ceil_div(N, kTileRows) * ceil_div(K, kSliceCols) * kTileWords;
 }
 
-// Rows per unit: the largest of 4, 2, 1 row tiles (within what the batch allows) that still
-// leaves at least two units per CU on a 256-CU device. Tables are built once per unit and
-// activation row, so more rows per unit means fewer table entries per lookup; enough units
-// keep every workgroup's prefetch pipeline busy.
+// Rows per unit: 2 row tiles when the list still holds enough units to keep every workgroup
+// busy (the tables, built once per unit and activation row, then serve 512 rows), else 1.
+// Measured on the configs' shapes: 2 tiles win on the 70B gate/up/down (26.6 vs 28.9 us at
+// batch 1, 62 vs 81 us at batch 4) and lose on 4096 x 4096 (6.9 vs 5.9 us); 4 tiles (one
+// workgroup per CU: 166+ VGPRs) never won, and stay reachable through the geometry export.
 int choose_rows(int64_t NT, int64_t units_per_tile_row_group, int batch) {
-    for (int r : {4, 2}) {
-        if (r <= max_rows_per_group(batch) && ceil_div(NT, r) * units_per_tile_row_group >= 512) return r;
-    }
+    const int64_t need = batch > 1 ? 768 : 1024;
+    if (2 <= max_rows_per_group(batch) && ceil_div(NT, 2) * units_per_tile_row_group >= need) return 2;
     return 1;
 }
 

@@ -1096,8 +1096,14 @@ static hipError_t dispatch_instance(int batch, int rpl, bool xl, F f) {
         if (rpl >= 2) return f(XT{}, integral_constant<int, 2>{}, integral_constant<int, 1>{}, std::false_type{});
         return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 1>{}, std::false_type{});
     }
-    if (batch <= 2) return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 2>{}, std::false_type{});
-    if (batch <= kBatchChunk) return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 4>{}, std::false_type{});
+    if (batch <= 2) {
+        if (rpl >= 2) return f(XT{}, integral_constant<int, 2>{}, integral_constant<int, 2>{}, std::false_type{});
+        return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 2>{}, std::false_type{});
+    }
+    if (batch <= kBatchChunk) {
+        if (rpl >= 2) return f(XT{}, integral_constant<int, 2>{}, integral_constant<int, 4>{}, std::false_type{});
+        return f(XT{}, integral_constant<int, 1>{}, integral_constant<int, 4>{}, std::false_type{});
+    }
     return hipErrorInvalidValue;  // larger batches run as chunks of kBatchChunk rows
 }
 
@@ -1123,7 +1129,7 @@ static StepArgs batch_chunk(const StepArgs& a, int r0) {
     return c;
 }
 
-int max_rows_per_group(int batch) { return batch <= 1 ? 4 : 1; }
+int max_rows_per_group(int batch) { return batch <= 1 ? 4 : 2; }
 
 // The step reads every buffer through 32-bit buffer offsets below 2^31 (kOob is out of range).
 bool step_buffers_fit(const StepArgs& a) {
