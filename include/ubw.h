@@ -298,7 +298,7 @@ int ubw_gram(const void* x, int x_dtype, int64_t T, int64_t K, float scale, floa
  *              Cholesky factor of H_d (the upper triangle is left partly updated)
  *   W          fp32 [N][K], the layer's dense weights
  *   d, score   OUT fp32 [K];  idx OUT int32 [s], 1 <= s <= K
- *   workspace  ubw_saliency_workspace_bytes(N, K) bytes (about 2 K^2 + N K / 16 bytes:
+ *   workspace  ubw_saliency_workspace_bytes(N, K) bytes (about 2 K^2 + N K / 16 + 64 K bytes:
  *              the factor's block inverses and the triangular solve's blocks), caller-owned.
  *              On return its float 0 holds lambda and float 1 an error code: 0 none, 1 a
  *              pivot was not positive (H_d not positive definite in fp32), 2 the selection

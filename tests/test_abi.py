@@ -234,7 +234,7 @@ def test_saliency_rejects():
     assert L.ubw_saliency_workspace_bytes(100, 0, ctypes.byref(sz)) == EINVAL
     assert L.ubw_saliency_workspace_bytes(100, 300, ctypes.byref(sz)) == 0
     nblk = 5
-    assert sz.value == 4 * (16 + nblk * 4096 + 4096 * nblk * (nblk + 1) // 2 + 2 * 300 + 300)
+    assert sz.value == 4 * (16 + nblk * 4096 + 4096 * nblk * (nblk + 1) // 2 + 2 * 300 + 16 * 300)
     need = sz.value
     args = dict(H=FAKE, K=300, damp=0.01, W=FAKE, N=100, s=10, d=FAKE, score=FAKE, idx=FAKE, ws=FAKE, wsb=need,
                 stream=None)

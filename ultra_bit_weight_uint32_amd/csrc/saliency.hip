@@ -9,19 +9,20 @@
 // are the salient columns, returned ascending.
 //
 // Kernels:
-//   k_gram         H = scale X^T X on the matrix cores (v_mfma_f32_32x32x8f16): the one dense
-//                  contraction of the method. 128 x 128 tiles of H per workgroup, 32 rows of X
-//                  per step staged through LDS transposed so that each lane's 4 consecutive
-//                  k values are one 8-byte LDS read.
+//   k_gram         H = scale X^T X on the matrix cores (v_mfma_f32_32x32x16_f16): the one
+//                  dense contraction of the method. One workgroup per 128 x 128 tile of the
+//                  upper triangle (mirrored), X double-buffered through LDS 32 rows per stage.
 //   k_damp         lambda from the diagonal, added to it.
 //   k_chol_diag    Cholesky of one 64 x 64 diagonal block in LDS, and the inverse of that
 //                  factor (kept for the panel and for the inverse's diagonal).
 //   k_chol_panel   L_ik = A_ik L_kk^-T for the block rows below.
 //   k_chol_update  A_ij -= L_ik L_jk^T for the trailing lower blocks.
-//   k_inv_diag     one workgroup per 64-column block k solves L Z = E_k (rows >= 64 k) block
-//                  row by block row and sums the squares of Z's columns: d_j = ||L^-1 e_j||^2.
+//   k_trsm_row / k_trsm_update   the solve L Z = I right-looking by block rows (every step one
+//                  launch of independent 64 x 64 block products); k_colnorm then sums the
+//                  squares of Z's columns: d_j = ||L^-1 e_j||^2.
 //   k_score_part / k_score_finish   column sums of W^2 in row chunks, then score = sum / d^2.
-//   k_rank         rank of every score (count of larger scores, equal ones at lower indices).
+//   k_rank         rank of every score (count of larger scores, equal ones at lower indices),
+//                  in 16 partial counts per score over slices of the scores.
 //   k_select       the columns of rank < s, ascending, by one prefix scan.
 // Everything after the Gram matrix is fp32 vector arithmetic in a fixed order.
 #include <hip/hip_fp16.h>
@@ -36,21 +37,89 @@ namespace ubw {
 
 namespace {
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kGT = 128;  // H tile per workgroup
-constexpr int kGS = 32;   // rows of X per step
-constexpr int kGP = 8;    // LDS row padding (halves)
+constexpr int kGS = 32;   // rows of X per stage
+constexpr int kGP = 8;    // LDS row padding (halves): 80-byte rows keep 16-byte reads aligned
 
-__global__ __launch_bounds__(256) void k_gram(const __half* __restrict__ X, int T, int K, float scale,
+// Upper-triangle tile p (tiles (ti, tj) with ti <= tj, row-major) of an nt x nt tile grid.
+__device__ __forceinline__ void upper_tile(int p, int nt, int& ti, int& tj) {
+    int r = 0, rem = p;
+    while (rem >= nt - r) {
+        rem -= nt - r;
+        ++r;
+    }
+    ti = r;
+    tj = r + rem;
+}
+
+// One workgroup per tile (ti <= tj) of H = scale X^T X (H is symmetric: the tile is written at
+// (ti, tj) and mirrored at (tj, ti)). Four waves, each a 64 x 64 quarter as 2 x 2 tiles of
+// v_mfma_f32_32x32x16_f16. X streams through LDS 32 rows per stage, two buffers: the next
+// stage's loads are issued before this stage's matrix instructions. Each thread loads 4 rows x
+// 2 columns per task (4-byte loads, consecutive threads on consecutive column pairs) and stores
+// them transposed as two 8-byte LDS writes, [column][row], so that a lane's 8 consecutive rows
+// (its k values) are one 16-byte LDS read. k is summed over, so any assignment of rows to
+// (lane half, element) that is the same for both operands gives X^T X.
+// pairs: K even and X 4-byte aligned, so every column pair is one aligned 4-byte load.
+__global__ __launch_bounds__(256) void k_gram(const __half* __restrict__ X, int T, int K, int pairs, float scale,
                                               float* __restrict__ H) {
-    __shared__ __align__(16) _Float16 sA[kGT][kGS + kGP];  // X[t0 + t][i0 + i] at [i][t]
-    __shared__ __align__(16) _Float16 sB[kGT][kGS + kGP];  // X[t0 + t][j0 + j] at [j][t]
-    const int i0 = blockIdx.y * kGT, j0 = blockIdx.x * kGT;
+    __shared__ __align__(16) _Float16 sA[2][kGT][kGS + kGP];
+    __shared__ __align__(16) _Float16 sB[2][kGT][kGS + kGP];
+    const int nt = (K + kGT - 1) / kGT;
+    int ti, tj;
+    upper_tile(blockIdx.x, nt, ti, tj);
+    const int i0 = ti * kGT, j0 = tj * kGT;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv >> 1, wn = wv & 1;  // this wave's 64 x 64 quarter of the tile
-    const _Float16* Xh = reinterpret_cast<const _Float16*>(X);
+    const int wm = wv >> 1, wn = wv & 1;
+    const uint16_t* Xu = reinterpret_cast<const uint16_t*>(X);
+    // load tasks: task q = tid + 256 e (e = 0, 1): rows 4 (q / 64) .. +3, columns 2 (q % 64), +1
+    uint32_t ra[2][4], rb[2][4];
+    auto load = [&](int t0) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int q = tid + 256 * e;
+            const int tr = 4 * (q >> 6), c = 2 * (q & 63);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = t0 + tr + u;
+                const int64_t off = (int64_t)t * K;
+                uint32_t va = 0, vb = 0;
+                const int ia = i0 + c, jb = j0 + c;
+                if (t < T && pairs) {  // c even, K even: a pair starting below K ends below K
+                    if (ia < K) va = *reinterpret_cast<const uint32_t*>(Xu + off + ia);
+                    if (jb < K) vb = *reinterpret_cast<const uint32_t*>(Xu + off + jb);
+                } else if (t < T) {
+                    if (ia + 1 < K) va = (uint32_t)Xu[off + ia] | ((uint32_t)Xu[off + ia + 1] << 16);
+                    else if (ia < K) va = Xu[off + ia];
+                    if (jb + 1 < K) vb = (uint32_t)Xu[off + jb] | ((uint32_t)Xu[off + jb + 1] << 16);
+                    else if (jb < K) vb = Xu[off + jb];
+                }
+                ra[e][u] = va;
+                rb[e][u] = vb;
+            }
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int q = tid + 256 * e;
+            const int tr = 4 * (q >> 6), c = 2 * (q & 63);
+            // column c: low halves of rows tr..tr+3; column c + 1: high halves
+            auto lo2 = [](uint32_t p, uint32_t q) { return (p & 0xFFFFu) | (q << 16); };
+            auto hi2 = [](uint32_t p, uint32_t q) { return (p >> 16) | (q & 0xFFFF0000u); };
+            const uint2 a0 = make_uint2(lo2(ra[e][0], ra[e][1]), lo2(ra[e][2], ra[e][3]));
+            const uint2 a1 = make_uint2(hi2(ra[e][0], ra[e][1]), hi2(ra[e][2], ra[e][3]));
+            const uint2 b0 = make_uint2(lo2(rb[e][0], rb[e][1]), lo2(rb[e][2], rb[e][3]));
+            const uint2 b1 = make_uint2(hi2(rb[e][0], rb[e][1]), hi2(rb[e][2], rb[e][3]));
+            *reinterpret_cast<uint2*>(&sA[buf][c][tr]) = a0;
+            *reinterpret_cast<uint2*>(&sA[buf][c + 1][tr]) = a1;
+            *reinterpret_cast<uint2*>(&sB[buf][c][tr]) = b0;
+            *reinterpret_cast<uint2*>(&sB[buf][c + 1][tr]) = b1;
+        }
+    };
     float16_t acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -58,32 +127,32 @@ __global__ __launch_bounds__(256) void k_gram(const __half* __restrict__ X, int 
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+    load(0);
+    store(0);
+    __syncthreads();
+    int buf = 0;
     for (int t0 = 0; t0 < T; t0 += kGS) {
-        for (int e = tid; e < kGS * kGT; e += 256) {
-            const int t = e / kGT, c = e % kGT;
-            const bool tv = t0 + t < T;
-            const int64_t rowoff = (int64_t)(t0 + t) * K;
-            sA[c][t] = (tv && i0 + c < K) ? Xh[rowoff + i0 + c] : (_Float16)0;
-            sB[c][t] = (tv && j0 + c < K) ? Xh[rowoff + j0 + c] : (_Float16)0;
-        }
-        __syncthreads();
+        const bool more = t0 + kGS < T;
+        if (more) load(t0 + kGS);  // in flight during this stage's matrix instructions
 #pragma unroll
-        for (int kk = 0; kk < kGS; kk += 8) {
-            half4_t a[2], b[2];
-            const int ko = kk + 4 * (lane >> 5);
+        for (int kk = 0; kk < kGS; kk += 16) {
+            half8_t a[2], b[2];
+            const int ko = kk + 8 * (lane >> 5);
 #pragma unroll
             for (int m = 0; m < 2; ++m)
-                a[m] = *reinterpret_cast<const half4_t*>(&sA[wm * 64 + m * 32 + (lane & 31)][ko]);
+                a[m] = *reinterpret_cast<const half8_t*>(&sA[buf][wm * 64 + m * 32 + (lane & 31)][ko]);
 #pragma unroll
             for (int n = 0; n < 2; ++n)
-                b[n] = *reinterpret_cast<const half4_t*>(&sB[wn * 64 + n * 32 + (lane & 31)][ko]);
+                b[n] = *reinterpret_cast<const half8_t*>(&sB[buf][wn * 64 + n * 32 + (lane & 31)][ko]);
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int n = 0; n < 2; ++n)
-                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x8f16(a[m], b[n], acc[m][n], 0, 0, 0);
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[n], acc[m][n], 0, 0, 0);
         }
+        if (more) store(buf ^ 1);  // the other buffer: last read before the previous barrier
         __syncthreads();
+        buf ^= 1;
     }
     // result element (row 8 (v / 4) + 4 (lane / 32) + v % 4, column lane % 32) of each 32 x 32 tile
 #pragma unroll
@@ -94,7 +163,11 @@ __global__ __launch_bounds__(256) void k_gram(const __half* __restrict__ X, int 
             for (int v = 0; v < 16; ++v) {
                 const int i = i0 + wm * 64 + m * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                 const int j = j0 + wn * 64 + n * 32 + (lane & 31);
-                if (i < K && j < K) H[(int64_t)i * K + j] = scale * acc[m][n][v];
+                if (i < K && j < K) {
+                    const float h = scale * acc[m][n][v];
+                    H[(int64_t)i * K + j] = h;
+                    if (ti != tj) H[(int64_t)j * K + i] = h;
+                }
             }
 }
 
@@ -128,13 +201,18 @@ constexpr int kCB = 64;  // Cholesky block
 
 // Cholesky of diagonal block kb (lower, in LDS), written back, and its inverse to Linv[kb].
 // Rows/columns past K act as an identity block.
-__global__ __launch_bounds__(256) void k_chol_diag(float* A, int K, int kb, float* Linv, float* misc) {
+// 1024 threads: each of the 128 steps below is a short chain of LDS reads and multiply-adds
+// per thread, and 16 waves keep several chains in flight (measured per 64 x 64 block: one wave
+// 303 us, 4 waves 108 us, 16 waves 66 us).
+constexpr int kDiagThreads = 1024;
+
+__global__ __launch_bounds__(kDiagThreads) void k_chol_diag(float* A, int K, int kb, float* Linv, float* misc) {
     __shared__ float L[kCB][kCB + 1];
     __shared__ float Z[kCB][kCB + 1];
     const int tid = threadIdx.x;
     const int o = kb * kCB;
     const int n = K - o < kCB ? K - o : kCB;
-    for (int e = tid; e < kCB * kCB; e += 256) {
+    for (int e = tid; e < kCB * kCB; e += kDiagThreads) {
         const int r = e / kCB, c = e % kCB;
         L[r][c] = (r < n && c < n) ? A[(int64_t)(o + r) * K + o + c] : (r == c ? 1.f : 0.f);
     }
@@ -147,32 +225,34 @@ __global__ __launch_bounds__(256) void k_chol_diag(float* A, int K, int kb, floa
         }
         const float piv = sqrtf(p);
         __syncthreads();
-        for (int r = c + 1 + tid; r < kCB; r += 256) L[r][c] /= piv;
+        for (int r = c + 1 + tid; r < kCB; r += kDiagThreads) L[r][c] /= piv;
         __syncthreads();
         if (tid == 0) L[c][c] = piv;
         // trailing update of the lower triangle: L[r][q] -= L[r][c] L[q][c], c < q <= r
-        const int m = kCB - c - 1;
-        for (int e = tid; e < m * m; e += 256) {
-            const int r = c + 1 + e / m, q = c + 1 + e % m;
-            if (q <= r) L[r][q] -= L[r][c] * L[q][c];
+        // (thread: column q = tid % 64, rows tid / 64 + 16 k)
+        {
+            const int q = tid & 63;
+            if (q > c)
+                for (int r = c + 1 + (tid >> 6); r < kCB; r += kDiagThreads / 64)
+                    if (q <= r) L[r][q] -= L[r][c] * L[q][c];
         }
         __syncthreads();
     }
-    // inverse of the lower factor: column c by forward substitution (one thread per column)
-    if (tid < kCB) {
-        const int c = tid;
-        for (int r = 0; r < kCB; ++r) {
-            float v = (r == c) ? 1.f : 0.f;
-            if (r < c) {
-                Z[r][c] = 0.f;
-                continue;
-            }
-            for (int q = c; q < r; ++q) v -= L[r][q] * Z[q][c];
-            Z[r][c] = v / L[r][r];
-        }
-    }
+    // inverse of the lower factor, right-looking: Z = I; for each q, row q of Z is final once
+    // divided by L[q][q], and is then eliminated from the rows below (all threads at once)
+    for (int e = tid; e < kCB * kCB; e += kDiagThreads) Z[e / kCB][e % kCB] = (e / kCB == e % kCB) ? 1.f : 0.f;
     __syncthreads();
-    for (int e = tid; e < kCB * kCB; e += 256) {
+    for (int q = 0; q < kCB; ++q) {
+        if (tid <= q) Z[q][tid] /= L[q][q];
+        __syncthreads();
+        {  // rows below q, columns 0..q (thread: column tid % 64, rows tid / 64 + 16 k)
+            const int c = tid & 63;
+            if (c <= q)
+                for (int r = q + 1 + (tid >> 6); r < kCB; r += kDiagThreads / 64) Z[r][c] -= L[r][q] * Z[q][c];
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < kCB * kCB; e += kDiagThreads) {
         const int r = e / kCB, c = e % kCB;
         if (r < n && c < n && c <= r) A[(int64_t)(o + r) * K + o + c] = L[r][c];
         Linv[(int64_t)kb * kCB * kCB + e] = Z[r][c];
@@ -266,97 +346,131 @@ __global__ __launch_bounds__(256) void k_chol_update(float* A, int K, int kb) {
         }
 }
 
-// Offset (floats) of block column k's Z in the scratch: whole 64 x 64 blocks for the block
-// rows k .. nblk - 1 (K padded to whole blocks).
-__host__ __device__ inline int64_t z_offset(int64_t k, int64_t K) {
+// The triangular solve L Z = I for the inverse's diagonal d_j = sum_i Z[i][j]^2, right-looking
+// by block rows so that each step is one launch of independent 64 x 64 block products:
+//   step r: Z_rc = Linv_r B_rc for c <= r (B_rr = I: Z_rr = Linv_r), then
+//           B_ic -= L_ir Z_rc for every i > r, c <= r.
+// B and Z share the scratch blocks (lower block triangle, block (i, c) at z_offset(c) + (i - c)
+// blocks), zero-filled first. Rows and columns past K: zero rows of L, identity padding of Linv.
+__host__ __device__ inline int64_t z_offset(int64_t c, int64_t K) {
     const int64_t Kp = (K + kCB - 1) / kCB * kCB;
-    return (int64_t)kCB * (k * Kp - (int64_t)kCB * k * (k - 1) / 2);
+    return (int64_t)kCB * (c * Kp - (int64_t)kCB * c * (c - 1) / 2);
+}
+__device__ __forceinline__ float* z_block(float* Zs, int i, int c, int K) {
+    return Zs + z_offset(c, K) + (int64_t)(i - c) * kCB * kCB;
 }
 
-// Block column k = blockIdx.x: Z_i = Linv_i (delta_ik I - sum_{k <= m < i} L_im Z_m) for the
-// block rows i >= k, then d_j = sum over those rows of Z[.][j]^2 for the 64 columns of block k.
-__global__ __launch_bounds__(256) void k_inv_diag(const float* A, int K, const float* Linv, float* Zs, float* d) {
-    __shared__ float S[kCB][kCB + 1];
-    __shared__ float M[kCB][kCB + 1];
+__global__ __launch_bounds__(256) void k_zero(float* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+// 64 x 64 x 64 product in LDS by 256 threads (4 x 4 outputs each): out[r][c] = sum_q P[r][q] Q[q][c].
+__device__ __forceinline__ void block_mm(float (*P)[kCB + 1], float (*Q)[kCB + 1], float out[4][4]) {
     const int tid = threadIdx.x;
-    const int kb = blockIdx.x;
-    const int nblk = (K + kCB - 1) / kCB;
-    float* Z = Zs + z_offset(kb, K);  // Z_i at rows (i - kb) * 64 .. , 64 columns, row-major
     const int r0 = 4 * (tid >> 4), c0 = tid & 15;
-    float dsum[4] = {0.f, 0.f, 0.f, 0.f};  // columns c0 + 16 b, rows r0 .. r0 + 3 of every block
-    for (int ib = kb; ib < nblk; ++ib) {
-        const int ro = ib * kCB;
-        const int nr = K - ro < kCB ? K - ro : kCB;
-        float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) out[a][b] = 0.f;
+    for (int q = 0; q < kCB; ++q) {
+        float p[4], v[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) p[a] = P[r0 + a][q];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v[b] = Q[q][c0 + 16 * b];
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = (ib == kb && r0 + a == c0 + 16 * b) ? 1.f : 0.f;
-        for (int mb = kb; mb < ib; ++mb) {
-            const int mo = mb * kCB;
-            __syncthreads();
-            for (int e = tid; e < kCB * kCB; e += 256) {
-                const int r = e / kCB, c = e % kCB;
-                S[r][c] = (r < nr) ? A[(int64_t)(ro + r) * K + mo + c] : 0.f;  // L_im (block mb is full)
-                M[r][c] = Z[(int64_t)(mb - kb) * kCB * kCB + e];                 // Z_m
-            }
-            __syncthreads();
-            for (int q = 0; q < kCB; ++q) {
-                float s[4], z[4];
+            for (int b = 0; b < 4; ++b) out[a][b] += p[a] * v[b];
+    }
+}
+
+// Step r, part 1: workgroup c (0..r) forms Z_rc = Linv_r B_rc (Z_rr = Linv_r).
+__global__ __launch_bounds__(256) void k_trsm_row(const float* Linv, float* Zs, int K, int r) {
+    __shared__ float P[kCB][kCB + 1];
+    __shared__ float Q[kCB][kCB + 1];
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x;
+    float* Z = z_block(Zs, r, c, K);
+    const float* Li = Linv + (int64_t)r * kCB * kCB;
+    if (c == r) {
+        for (int e = tid; e < kCB * kCB; e += 256) Z[e] = Li[e];
+        return;
+    }
+    for (int e = tid; e < kCB * kCB; e += 256) {
+        P[e / kCB][e % kCB] = Li[e];
+        Q[e / kCB][e % kCB] = Z[e];
+    }
+    __syncthreads();
+    float out[4][4];
+    block_mm(P, Q, out);
+    const int r0 = 4 * (tid >> 4), c0 = tid & 15;
 #pragma unroll
-                for (int a = 0; a < 4; ++a) s[a] = S[r0 + a][q];
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) z[b] = M[q][c0 + 16 * b];
+        for (int b = 0; b < 4; ++b) Z[(r0 + a) * kCB + c0 + 16 * b] = out[a][b];
+}
+
+// Step r, part 2: workgroup (i - r - 1, c) for i > r, c <= r: B_ic -= L_ir Z_rc.
+__global__ __launch_bounds__(256) void k_trsm_update(const float* A, float* Zs, int K, int r) {
+    __shared__ float P[kCB][kCB + 1];
+    __shared__ float Q[kCB][kCB + 1];
+    const int tid = threadIdx.x;
+    const int i = r + 1 + blockIdx.x, c = blockIdx.y;
+    const int ro = i * kCB, co = r * kCB;  // L_ir: rows of block i, columns of block r (full)
+    const int nr = K - ro < kCB ? K - ro : kCB;
+    const float* Zr = z_block(Zs, r, c, K);
+    for (int e = tid; e < kCB * kCB; e += 256) {
+        const int rr = e / kCB, cc = e % kCB;
+        P[rr][cc] = rr < nr ? A[(int64_t)(ro + rr) * K + co + cc] : 0.f;
+        Q[rr][cc] = Zr[e];
+    }
+    __syncthreads();
+    float out[4][4];
+    block_mm(P, Q, out);
+    float* B = z_block(Zs, i, c, K);
+    const int r0 = 4 * (tid >> 4), c0 = tid & 15;
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) acc[a][b] -= s[a] * z[b];
-            }
-        }
-        // Z_i = Linv_i acc: stage acc in S, Linv_i in M
-        __syncthreads();
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) S[r0 + a][c0 + 16 * b] = acc[a][b];
-        for (int e = tid; e < kCB * kCB; e += 256) M[e / kCB][e % kCB] = Linv[(int64_t)ib * kCB * kCB + e];
-        __syncthreads();
-        float z[4][4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) z[a][b] = 0.f;
-        for (int q = 0; q < kCB; ++q) {
-            float l[4], s[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) l[a] = M[r0 + a][q];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) s[b] = S[q][c0 + 16 * b];
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) z[a][b] += l[a] * s[b];
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float v = (r0 + a < nr) ? z[a][b] : 0.f;  // rows past K: identity padding
-                Z[(int64_t)(ib - kb) * kCB * kCB + (r0 + a) * kCB + c0 + 16 * b] = v;
-                dsum[b] += v * v;
+        for (int b = 0; b < 4; ++b) B[(r0 + a) * kCB + c0 + 16 * b] -= out[a][b];
+}
+
+constexpr int kSplit = 16;  // partial sums per column in the norm and rank passes
+
+// Partial column norms: workgroup (c, g) sums the squares of column block c of Z over the block
+// rows i = c + g, c + g + kSplit, ... into aux[g][j].
+__global__ __launch_bounds__(256) void k_colnorm(const float* Zs, int K, float* aux) {
+    __shared__ float part[4][kCB];
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x, g = blockIdx.y;
+    const int nblk = (K + kCB - 1) / kCB;
+    const int col = tid & 63, rg = tid >> 6;  // 4 row groups of 16 rows
+    float s = 0.f;
+    for (int i = c + g; i < nblk; i += kSplit) {
+        const float* Z = Zs + z_offset(c, K) + (int64_t)(i - c) * kCB * kCB;
+        const int nr = K - i * kCB < kCB ? K - i * kCB : kCB;
+        for (int rr = rg * 16; rr < rg * 16 + 16; ++rr)
+            if (rr < nr) {
+                const float v = Z[rr * kCB + col];
+                s += v * v;
             }
     }
-    // sum dsum over the 16 row groups of threads sharing a column
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < 4; ++b) S[tid >> 4][c0 + 16 * b] = dsum[b];
+    part[rg][col] = s;
     __syncthreads();
     if (tid < kCB) {
-        float t = 0.f;
-        for (int g = 0; g < 16; ++g) t += S[g][tid];
-        const int j = kb * kCB + tid;
-        if (j < K) d[j] = t;
+        const int j = c * kCB + tid;
+        if (j < K) aux[(int64_t)g * K + j] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
     }
+}
+
+__global__ __launch_bounds__(256) void k_colnorm_finish(const float* aux, int K, float* d) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= K) return;
+    float s = 0.f;
+    for (int g = 0; g < kSplit; ++g) s += aux[(int64_t)g * K + j];
+    d[j] = s;
 }
 
 // score: column sums of W^2 over row chunks, then score_j = sum / d_j^2.
@@ -383,35 +497,44 @@ __global__ __launch_bounds__(256) void k_score_finish(const float* part, int chu
     score[j] = s / (d[j] * d[j]);
 }
 
-// rank[j] = #{i : score_i > score_j} + #{i < j : score_i == score_j}; sel[j] = rank < s.
-__global__ __launch_bounds__(256) void k_rank(const float* score, int K, int s, int* sel) {
+// Partial ranks: workgroup (bx, g) counts, for its 256 scores j, the i in slice g of [0, K) with
+// score_i > score_j, or equal with i < j; the rank of j is the sum over the kSplit slices.
+__global__ __launch_bounds__(256) void k_rank(const float* score, int K, int* cnt) {
     __shared__ float tile[256];
     const int j = blockIdx.x * 256 + threadIdx.x;
+    const int g = blockIdx.y;
+    const int per = (K + kSplit - 1) / kSplit;
+    const int b0 = g * per, b1 = b0 + per < K ? b0 + per : K;
     const float v = j < K ? score[j] : 0.f;
     int rank = 0;
-    for (int t0 = 0; t0 < K; t0 += 256) {
+    for (int t0 = b0; t0 < b1; t0 += 256) {
         __syncthreads();
-        tile[threadIdx.x] = t0 + (int)threadIdx.x < K ? score[t0 + threadIdx.x] : 0.f;
+        tile[threadIdx.x] = t0 + (int)threadIdx.x < b1 ? score[t0 + threadIdx.x] : 0.f;
         __syncthreads();
-        const int n = K - t0 < 256 ? K - t0 : 256;
+        const int n = b1 - t0 < 256 ? b1 - t0 : 256;
         for (int q = 0; q < n; ++q) {
             const float u = tile[q];
             rank += (u > v || (u == v && t0 + q < j)) ? 1 : 0;
         }
     }
-    if (j < K) sel[j] = rank < s ? 1 : 0;
+    if (j < K) cnt[(int64_t)g * K + j] = rank;
 }
 
 // One workgroup of 1024 threads: idx = the selected columns in ascending order (at most s of
 // them: ranks are distinct for any scores that compare, so exactly s are selected; NaN scores,
 // which compare with nothing, can break that, and then misc[1] is set to 2).
-__global__ __launch_bounds__(1024) void k_select(const int* sel, int K, int s, int32_t* idx, float* misc) {
+__global__ __launch_bounds__(1024) void k_select(const int* rk, int K, int s, int32_t* idx, float* misc) {
     __shared__ int cnt[1024];
     const int tid = threadIdx.x;
     const int per = (K + 1023) / 1024;
     const int b = tid * per, e = b + per < K ? b + per : K;
+    auto selected = [&](int j) {
+        int r = 0;
+        for (int g = 0; g < kSplit; ++g) r += rk[(int64_t)g * K + j];
+        return r < s ? 1 : 0;
+    };
     int c = 0;
-    for (int j = b; j < e; ++j) c += sel[j];
+    for (int j = b; j < e; ++j) c += selected(j);
     cnt[tid] = c;
     __syncthreads();
     // exclusive scan over the 1024 counts (Hillis-Steele on a copy)
@@ -423,22 +546,24 @@ __global__ __launch_bounds__(1024) void k_select(const int* sel, int K, int s, i
     }
     int pos = cnt[tid] - c;
     for (int j = b; j < e; ++j)
-        if (sel[j] && pos < s) idx[pos++] = j;
+        if (selected(j) && pos < s) idx[pos++] = j;
     if (tid == 1023 && cnt[1023] != s) misc[1] = 2.f;
 }
 
 }  // namespace
 
 hipError_t launch_gram(const void* x, int T, int K, float scale, float* H, hipStream_t s) {
-    const unsigned g = (unsigned)((K + kGT - 1) / kGT);
-    hipLaunchKernelGGL(k_gram, dim3(g, g), dim3(256), 0, s, (const __half*)x, T, K, scale, H);
+    const int64_t nt = (K + kGT - 1) / kGT;
+    const int pairs = (K % 2 == 0 && (reinterpret_cast<uintptr_t>(x) & 3u) == 0) ? 1 : 0;
+    hipLaunchKernelGGL(k_gram, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, s, (const __half*)x, T, K, pairs,
+                       scale, H);
     return hipGetLastError();
 }
 
 int64_t saliency_workspace_floats(int64_t N, int64_t K) {
     const int64_t nblk = ceil_div(K, kCB);
     const int64_t chunks = ceil_div(N, kSChunk);
-    return 16 + nblk * kCB * kCB + z_offset(nblk, K) + chunks * K + K;
+    return 16 + nblk * kCB * kCB + z_offset(nblk, K) + chunks * K + kSplit * K;
 }
 
 hipError_t launch_saliency(float* H, int K, float damp, const float* W, int N, int s, float* d, float* score,
@@ -449,10 +574,11 @@ hipError_t launch_saliency(float* H, int K, float damp, const float* W, int N, i
     float* Linv = ws + 16;
     float* Z = Linv + (int64_t)nblk * kCB * kCB;
     float* part = Z + z_offset(nblk, K);
-    int* sel = reinterpret_cast<int*>(part + (int64_t)chunks * K);
+    float* aux = part + (int64_t)chunks * K;  // kSplit x K: norm partials, then rank partials
+    int* rk = reinterpret_cast<int*>(aux);
     hipLaunchKernelGGL(k_damp, dim3(1), dim3(256), 0, st, H, K, damp, misc);
     for (int kb = 0; kb < nblk; ++kb) {
-        hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(256), 0, st, H, K, kb, Linv, misc);
+        hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(kDiagThreads), 0, st, H, K, kb, Linv, misc);
         const int m = nblk - kb - 1;
         if (m > 0) {
             hipLaunchKernelGGL(k_chol_panel, dim3(m), dim3(256), 0, st, H, K, kb, Linv);
@@ -461,12 +587,22 @@ hipError_t launch_saliency(float* H, int K, float damp, const float* W, int N, i
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_inv_diag, dim3(nblk), dim3(256), 0, st, H, K, Linv, Z, d);
+    const int64_t zn = z_offset(nblk, K);
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)((zn + 255) / 256)), dim3(256), 0, st, Z, zn);
+    for (int r = 0; r < nblk; ++r) {
+        hipLaunchKernelGGL(k_trsm_row, dim3(r + 1), dim3(256), 0, st, Linv, Z, K, r);
+        if (r + 1 < nblk)
+            hipLaunchKernelGGL(k_trsm_update, dim3(nblk - r - 1, r + 1), dim3(256), 0, st, H, Z, K, r);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_colnorm, dim3(nblk, kSplit), dim3(256), 0, st, Z, K, aux);
+    hipLaunchKernelGGL(k_colnorm_finish, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, aux, K, d);
     const unsigned cb = (unsigned)((K + 255) / 256);
     hipLaunchKernelGGL(k_score_part, dim3(cb, chunks), dim3(256), 0, st, W, N, K, part);
     hipLaunchKernelGGL(k_score_finish, dim3(cb), dim3(256), 0, st, part, chunks, K, d, score);
-    hipLaunchKernelGGL(k_rank, dim3(cb), dim3(256), 0, st, score, K, s, sel);
-    hipLaunchKernelGGL(k_select, dim3(1), dim3(1024), 0, st, sel, K, s, idx, misc);
+    hipLaunchKernelGGL(k_rank, dim3(cb, kSplit), dim3(256), 0, st, score, K, rk);
+    hipLaunchKernelGGL(k_select, dim3(1), dim3(1024), 0, st, rk, K, s, idx, misc);
     return hipGetLastError();
 }
 
