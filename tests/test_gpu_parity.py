@@ -773,3 +773,23 @@ def test_saliency_flags_a_matrix_that_is_not_definite():
     w = torch.ones((4, k), device=DEV)
     _, _, _, ws = ubw.hessian_saliency(h, w, 10)
     assert host(ws)[1] != 0
+
+
+@pytest.mark.parametrize("batch", [5, 6, 13])
+@pytest.mark.parametrize("k", [1000, 1501])
+def test_batch_chunks_ragged(batch, k):
+    """Batches above 4 rows run as 4-row launches: ragged last chunk, activation blocks that go
+    through LDS (K = 1000: 4 rows of fp16 fit) or not, each mode of the step, grouped too."""
+    rng = np.random.default_rng(batch * 10 + k)
+    g = make_integer_gemv(rng, 700, k, 2, s=60, ns=2, batch=batch)
+    ref = oracle_gemv(g)
+    for mode in MODES:
+        y = torch.full((batch, g.n), float("nan"), device=DEV)
+        assert np.array_equal(gpu_gemv(g, y=y, mode=mode), ref), mode
+    y0 = rng.integers(-50, 50, (batch, g.n)).astype(np.float32)
+    assert np.array_equal(gpu_gemv(g, y=dev(y0), accumulate=True), ref + y0)
+    h = make_integer_gemv(rng, 300, k, 1, batch=batch)
+    shared_x([g, h], g.x)
+    outs = ubw.lut_gemv_multi([multi_entry(g), multi_entry(h, ws=False)], dev(g.x), k)
+    assert np.array_equal(host(outs[0]).astype(np.float64), ref)
+    assert np.array_equal(host(outs[1]).astype(np.float64), oracle_gemv(h))
