@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the headline line: time every GEMV and layer of the 7B MLP (config 4) and the "
                          "70B layer (config 5) at their batches, the group-scale variant, the offline fit and the saliency search")
+    ap.add_argument("--profile-shape", type=str, default=None, metavar="N,K,NB,B",
+                    help="instead of the headline line: run `--steps` cold ubw_lut_gemv calls of an N x K GEMV with "
+                         "NB bases at batch B (no refinement), for counter collection under rocprofv3")
     ap.add_argument("--profile-run", action="store_true",
                     help="for hardware-counter runs: a 64 MiB device copy (known bytes, to scale the counters) "
                          "then --steps cold steps; prints one line, no timing")
@@ -81,6 +84,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_shape:
+        profile_shape(torch, ubw, dev, args.profile_shape, args.steps)
+        return
     if args.configs:
         config_sweep(torch, ubw, dev)
         gs_sweep(torch, ubw, dev)
@@ -321,6 +327,29 @@ def config_sweep(torch, ubw, dev):
             torch.cuda.empty_cache()
         del base
         torch.cuda.empty_cache()
+
+
+def profile_shape(torch, ubw, dev, spec, steps):
+    """Cold calls of one GEMV shape (for rocprofv3 --pmc / --kernel-trace runs)."""
+    from workloads import make_gemv
+    n, k, nb, b = (int(v) for v in spec.split(","))
+    g = make_gemv(np.random.default_rng(1), "profile", n, k, nb, batch=b)
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a).to(dev)
+
+    base = dict(packed=ubw.pack_bases(t(g.bits), nb, n, k), ar=t(g.alpha_r), ac=t(g.alpha_c), x=t(g.x))
+    per = sum(v.numel() * v.element_size() for v in base.values())
+    copies = [{kk: v.clone() for kk, v in base.items()} for _ in range(max(2, -(-COLD_BYTES // per)))]
+    for c in copies:
+        c["ws"] = ubw.workspace(n, dev)
+    y = torch.zeros((b, n), device=dev)
+    for i in range(steps):
+        c = copies[i % len(copies)]
+        ubw.lut_gemv(c["packed"], c["ar"], c["ac"], c["x"], n, k, y=y, workspace=c["ws"])
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_shape": [n, k, nb, b], "steps": steps, "cold_copies": len(copies)}), flush=True)
 
 
 def gs_sweep(torch, ubw, dev):
