@@ -23,14 +23,15 @@ int64_t packed_words_of(int nb, int64_t N, int64_t K) {
     return (int64_t)nb * ceil_div(N, kTileRows) * ceil_div(K, kSliceCols) * kTileWords;
 }
 
-// Rows per unit: 2 row tiles when the list still holds enough units to keep every workgroup
-// busy (the tables, built once per unit and activation row, then serve 512 rows), else 1.
-// Measured on the configs' shapes: 2 tiles win on the 70B gate/up/down (26.6 vs 28.9 us at
-// batch 1, 62 vs 81 us at batch 4) and lose on 4096 x 4096 (6.9 vs 5.9 us); 4 tiles (one
-// workgroup per CU: 166+ VGPRs) never won, and stay reachable through the geometry export.
+// Rows per unit: 2 row tiles when the list still holds at least 768 units (enough to keep every
+// workgroup busy; the tables, built once per unit and activation row, then serve 512 rows),
+// else 1. Measured on the configs' shapes: 2 tiles win on the 70B gate/up/down (26.6 vs 28.9 us
+// at batch 1, 62 vs 81 us at batch 4) and on the grouped q/k/v (1000 units: 14.3 vs 16.2 us),
+// tie on 8192 x 8192 alone (800 units) and lose on 4096 x 4096 (128 units: 6.9 vs 5.9 us);
+// 4 tiles (one workgroup per CU: 166+ VGPRs) never won, and stay reachable through the
+// geometry export.
 int choose_rows(int64_t NT, int64_t units_per_tile_row_group, int batch) {
-    const int64_t need = batch > 1 ? 768 : 1024;
-    if (2 <= max_rows_per_group(batch) && ceil_div(NT, 2) * units_per_tile_row_group >= need) return 2;
+    if (2 <= max_rows_per_group(batch) && ceil_div(NT, 2) * units_per_tile_row_group >= 768) return 2;
     return 1;
 }
 
