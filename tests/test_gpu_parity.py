@@ -793,3 +793,18 @@ def test_batch_chunks_ragged(batch, k):
     outs = ubw.lut_gemv_multi([multi_entry(g), multi_entry(h, ws=False)], dev(g.x), k)
     assert np.array_equal(host(outs[0]).astype(np.float64), ref)
     assert np.array_equal(host(outs[1]).astype(np.float64), oracle_gemv(h))
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_fp32_activations_in_variants(batch):
+    """fp32 activations through the group-scale variant and the grouped launch (integer exact)."""
+    rng = np.random.default_rng(400 + batch)
+    k = 900
+    g = make_integer_gemv(rng, 600, k, 2, s=50, ns=1, batch=batch, x_dtype=np.float32)
+    h = make_integer_gemv(rng, 300, k, 3, batch=batch, x_dtype=np.float32)
+    shared_x([g, h], g.x)
+    arg = gs_scales(rng, g)
+    assert np.array_equal(gpu_gs(g, arg), oracle_gs(g, arg))
+    outs = ubw.lut_gemv_multi([multi_entry(g), multi_entry(h)], dev(g.x), k)
+    assert np.array_equal(host(outs[0]).astype(np.float64), oracle_gemv(g))
+    assert np.array_equal(host(outs[1]).astype(np.float64), oracle_gemv(h))
