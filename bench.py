@@ -38,8 +38,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs", action="store_true",
-                    help="instead of the headline line: time every GEMV and layer of the 7B MLP (config 4) and the "
-                         "70B layer (config 5) at their batches, the group-scale variant, the offline fit and the saliency search")
+                    help="instead of the headline line: time every GEMV and layer of the 7B MLP and the "
+                         "70B layer at their batches, the group-scale variant, the offline fit and the saliency search")
     ap.add_argument("--profile-shape", type=str, default=None, metavar="N,K,NB,B",
                     help="instead of the headline line: run `--steps` cold ubw_lut_gemv calls of an N x K GEMV with "
                          "NB bases at batch B (no refinement), for counter collection under rocprofv3")
@@ -80,7 +80,7 @@ def main():
 
     import torch
     import ultra_bit_weight_uint32_amd as ubw
-    from workloads import algorithmic_bytes, config3
+    from workloads import algorithmic_bytes, attn_proj_7b
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -93,7 +93,7 @@ def main():
         fit_sweep(torch, ubw, dev)
         saliency_sweep(torch, ubw, dev)
         return
-    wl = config3(seed=0)
+    wl = attn_proj_7b(seed=0)
     g = wl.gemvs[0]
     n, k, nb, s, ns, batch = g.n, g.k, g.nb, g.s, g.ns, g.batch
 
@@ -258,13 +258,13 @@ def run_queued(torch, launch, count):
 def config_sweep(torch, ubw, dev):
     """Per-GEMV and per-layer times of configs 4 and 5 (cold: each timed loop rotates through at least
     COLD_BYTES of distinct copies), printed as one JSON line per measurement."""
-    from workloads import algorithmic_bytes, config4, config5
+    from workloads import algorithmic_bytes, mlp_7b, decoder_layer_70b
 
     def t(a):
         a = np.ascontiguousarray(a)
         return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a).to(dev)
 
-    for label, wl in (("7B MLP (config 4)", config4(seed=0)), ("70B decoder layer (config 5)", config5(seed=0))):
+    for label, wl in (("7B MLP", mlp_7b(seed=0)), ("70B decoder layer", decoder_layer_70b(seed=0))):
         base = []
         for g in wl.gemvs:
             base.append(dict(packed=ubw.pack_bases(t(g.bits), g.nb, g.n, g.k), ar=t(g.alpha_r), ac=t(g.alpha_c),
@@ -356,15 +356,15 @@ def gs_sweep(torch, ubw, dev):
     """The group-scale variant (one fp16 row scale per 128 columns) on the 7B attention
     projection (with its refinement) and the 7B MLP up projection, batch 1, cold, one JSON line
     each, next to the per-row call on the same data."""
-    from workloads import algorithmic_bytes, config3, config4
+    from workloads import algorithmic_bytes, attn_proj_7b, mlp_7b
 
     def t(a):
         a = np.ascontiguousarray(a)
         return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a).to(dev)
 
     rng = np.random.default_rng(5)
-    for label, g in (("7B attention projection (config 3)", config3(seed=0).gemvs[0]),
-                     ("7B MLP up (config 4)", config4(seed=0).gemvs[0].with_batch(1))):
+    for label, g in (("7B attention projection", attn_proj_7b(seed=0).gemvs[0]),
+                     ("7B MLP up", mlp_7b(seed=0).gemvs[0].with_batch(1))):
         cols = ubw.group_scale_cols(g.k)
         arg = rng.uniform(0.05, 0.5, size=(g.nb, g.n, cols)).astype(np.float16)
         base = dict(packed=ubw.pack_bases(t(g.bits), g.nb, g.n, g.k), arg=t(ubw.arrange_group_scales(arg)),
@@ -467,7 +467,7 @@ def saliency_sweep(torch, ubw, dev):
 
 def cpu_baseline(g, step_bytes, seconds):
     """The oracle as it stands (fp64 dequantize + naive matvec, OpenMP over rows) on the host
-    cores, on whole config calls until about `seconds` have passed."""
+    cores, on whole calls of the step until about `seconds` have passed."""
     import oracle
     cores = oracle.max_threads()
     kw = g.refine_kwargs()

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import ultra_bit_weight_uint32_amd as ubw
-from workloads import (config1, config2, config3, config4, config5, draw_bits, make_gemv, make_integer_gemv,
+from workloads import (single_gemv_256x512, ternary_stack_256x768, attn_proj_7b, mlp_7b, decoder_layer_70b, draw_bits, make_gemv, make_integer_gemv,
                        words_per_row)
 
 torch = pytest.importorskip("torch")
@@ -351,14 +351,14 @@ def test_ternary_gemv_integer_exact():
     assert np.array_equal(host(y).astype(np.float64), oracle.ternary_gemv(w, np.full(n, 2.0, np.float32), x))
 
 
-def test_config2_ternary_stack():
+def test_ternary_stack_chained():
     """4 x (256 -> 768 -> 256) ternary layers over 64 tokens, fp16 activations between layers.
     Every layer is checked on the GPU's own fp16 input (teacher forcing) at the elementwise 1e-3
     bar. The end-to-end output is compared with the oracle's own chain norm-wise: the two chains
     re-round slightly different fp32 results to fp16 after each of the 8 layers, so outputs
     near zero can differ by more than 1e-3 of themselves while the row stays within ~1e-4 of
     its largest entry."""
-    wl = config2()
+    wl = ternary_stack_256x768()
     enc = [ubw.ternary_encode(dev(L.w), dev(L.scale)) for L in wl.ternary]
     xt = dev(wl.tokens)
     worst = 0.0
@@ -386,20 +386,20 @@ def test_config2_ternary_stack():
 # ------------------------------------------------------------------------------------------
 # the workloads at full size, in the launch configuration the benchmark uses
 
-def test_config1_full():
-    g = config1().gemvs[0]
+def test_single_gemv_256x512_full():
+    g = single_gemv_256x512().gemvs[0]
     assert max_rel_err(gpu_gemv(g), oracle_gemv(g)) <= TOL
 
 
 @pytest.mark.parametrize("mode", MODES)
-def test_config3_full(mode):
-    g = config3().gemvs[0]
+def test_attn_proj_7b_full(mode):
+    g = attn_proj_7b().gemvs[0]
     assert max_rel_err(gpu_gemv(g, mode=mode), oracle_gemv(g)) <= TOL
     assert max_rel_err(gpu_gemv(g, refine=False, mode=mode), oracle_gemv(g, refine=False)) <= TOL
 
 
-def test_config4_full():
-    wl = config4()
+def test_mlp_7b_full():
+    wl = mlp_7b()
     for g in wl.gemvs:
         for b in wl.batches:
             gb = g.with_batch(b)
@@ -416,8 +416,8 @@ def sampled_rows(g, rows):
     return s
 
 
-def test_config5_full_sampled():
-    wl = config5()
+def test_decoder_layer_70b_sampled():
+    wl = decoder_layer_70b()
     rng = np.random.default_rng(55)
     for g in wl.gemvs:
         rows = np.sort(rng.choice(g.n, size=min(g.n, 384), replace=False))
@@ -505,10 +505,10 @@ def test_multi_single_gemv_matches_single_call():
     assert np.array_equal(host(out).astype(np.float64), oracle_gemv(g))
 
 
-def test_multi_config5_sampled():
+def test_multi_layer_70b_sampled():
     """70B-shaped q/k/v and gate/up groups on one shared fp16 x each (batch 1 and 16): sampled
     rows against the oracle within the float tolerance."""
-    wl = config5()
+    wl = decoder_layer_70b()
     by = {g.name: g for g in wl.gemvs}
     rng = np.random.default_rng(56)
     for names in (("q", "k", "v"), ("gate", "up")):
@@ -663,7 +663,7 @@ def test_fit_fp16_input_and_zeros():
     check_fit(w, 2, 3)
 
 
-def test_fit_config3_shape():
+def test_fit_4096x4096():
     """4096 x 4096 (the 7B projection), 2 bases, 5 rounds: every scale and the residual."""
     rng = np.random.default_rng(8)
     res = check_fit(fit_matrix(rng, 4096, 4096), 2, 5)

@@ -142,14 +142,14 @@ class Workload:
     batches: Tuple[int, ...] = (1,)
 
 
-def config1(seed: int = 0) -> Workload:
+def single_gemv_256x512(seed: int = 0) -> Workload:
     """Single binary GEMV: 256 x 512, one base, alpha ~ U(0.1, 1.0), fp32 x, group width 8."""
     rng = np.random.default_rng(seed)
     g = make_gemv(rng, "gemv256x512", 256, 512, 1, alpha=(0.1, 1.0), x_dtype=np.float32)
-    return Workload("cfg1_binary_256x512", "256x512, 1 base, fp32 x", [g])
+    return Workload("binary_256x512", "256x512, 1 base, fp32 x", [g])
 
 
-def config2(seed: int = 0, tokens: int = 64) -> Workload:
+def ternary_stack_256x768(seed: int = 0, tokens: int = 64) -> Workload:
     """Ternary tiny-LM linear stack: 4 layers of d=256 -> 768 -> 256, weights in {-1,0,+1} each
     with probability 1/3, per-row scale ~ U(0.01, 0.1), fp16 token vectors, batch 1."""
     rng = np.random.default_rng(seed)
@@ -160,38 +160,39 @@ def config2(seed: int = 0, tokens: int = 64) -> Workload:
             sc = draw_uniform(rng, 0.01, 0.1, n)
             layers.append(TernaryLayer(f"l{li}_{nm}", w, sc))
     toks = rng.standard_normal((tokens, 256)).astype(np.float16)
-    return Workload("cfg2_ternary_stack", "4 x (256->768->256) ternary, 64 tokens", ternary=layers, tokens=toks)
+    return Workload("ternary_stack", "4 x (256->768->256) ternary, 64 tokens", ternary=layers, tokens=toks)
 
 
-def config3(seed: int = 0) -> Workload:
+def attn_proj_7b(seed: int = 0) -> Workload:
     """7B-shaped attention projection: 4096 x 4096, 2 bases, 5% salient columns with 2
     refinement bases, alpha ~ U(0.05, 0.5), fp16 x, batch 1."""
     rng = np.random.default_rng(seed)
     k = 4096
     g = make_gemv(rng, "proj4096", 4096, k, 2, s=salient_count(0.05, k), ns=2)
-    return Workload("cfg3_proj_4096x4096", "4096x4096, 2 bases + 5% salient (2 refinement bases)", [g])
+    return Workload("proj_4096x4096", "4096x4096, 2 bases + 5% salient (2 refinement bases)", [g])
 
 
-def config4(seed: int = 0) -> Workload:
+def mlp_7b(seed: int = 0) -> Workload:
     """7B-shaped MLP: up 4096 -> 11008 and down 11008 -> 4096, 2 bases + 3% salient with 1
     refinement base, fp16 x (down input ReLU'd), batch 1, 4, 8 (x drawn at batch 8)."""
     rng = np.random.default_rng(seed)
     up = make_gemv(rng, "up", 11008, 4096, 2, s=salient_count(0.03, 4096), ns=1, batch=8)
     down = make_gemv(rng, "down", 4096, 11008, 2, s=salient_count(0.03, 11008), ns=1, batch=8, relu=True)
-    return Workload("cfg4_mlp_7b", "up 4096->11008, down 11008->4096", [up, down], batches=(1, 4, 8))
+    return Workload("mlp_7b", "up 4096->11008, down 11008->4096", [up, down], batches=(1, 4, 8))
 
 
-def config5(seed: int = 0) -> Workload:
+def decoder_layer_70b(seed: int = 0) -> Workload:
     """70B-shaped decoder layer: q, k, v, o, gate, up, down with 3 bases + 5% salient columns
     (2 refinement bases), fp16 x, batch 1 and 16 (x drawn at batch 16)."""
     rng = np.random.default_rng(seed)
     shapes = (("q", 8192, 8192), ("k", 1024, 8192), ("v", 1024, 8192), ("o", 8192, 8192),
               ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672))
     gs = [make_gemv(rng, nm, n, k, 3, s=salient_count(0.05, k), ns=2, batch=16) for nm, n, k in shapes]
-    return Workload("cfg5_layer_70b", "70B decoder layer, 7 GEMVs", gs, batches=(1, 16))
+    return Workload("layer_70b", "70B decoder layer, 7 GEMVs", gs, batches=(1, 16))
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {f.__name__: f for f in (single_gemv_256x512, ternary_stack_256x768, attn_proj_7b, mlp_7b,
+                                        decoder_layer_70b)}
 
 
 def algorithmic_bytes(n: int, k: int, nb: int, batch: int, x_bytes: int, s: int = 0, ns: int = 0) -> int:
