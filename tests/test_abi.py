@@ -284,3 +284,16 @@ def test_arrange_group_scales_layout():
     with pytest.raises(ValueError):
         ubw.arrange_group_scales(a[:, :, :5])
     assert [ubw.group_scale_cols(k) for k in (1, 128, 129, 256, 257, 700)] == [2, 2, 2, 2, 4, 6]
+
+
+def test_operands_beyond_32_bit_offsets_rejected():
+    """The step addresses every operand through 32-bit buffer offsets: an operand of 2 GiB or more
+    is refused on the host (UBW_EUNSUPPORTED) before anything is enqueued."""
+    big_n = 300_000_000                                    # 2 bases x 300M rows of fp32 alpha_r: 2.4 GB
+    assert gemv_args(N=big_n) == EUNSUP
+    assert gemv_args(K=300_000_000) == EUNSUP              # alpha_c 2.4 GB
+    assert gemv_args(N=64, K=600_000_000, batch=2) == EUNSUP  # x 2.4 GB
+    L = ubw.lib()
+    args = dict(packed=FAKE, arg=FAKE, ac=FAKE, nb=2, gsize=128, idx=None, s=0, packed_s=None, ar_s=None, ac_s=None,
+                ns=0, N=big_n, K=300, g=8, x=FAKE, x_dtype=1, batch=1, y=FAKE, acc=0, ws=None, wsb=0, stream=None)
+    assert L.ubw_lut_gemv_gs(*args.values()) == EUNSUP
