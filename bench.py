@@ -88,6 +88,7 @@ def main():
         profile_shape(torch, ubw, dev, args.profile_shape, args.steps)
         return
     if args.configs:
+        small_sweep(torch, ubw, dev)
         config_sweep(torch, ubw, dev)
         gs_sweep(torch, ubw, dev)
         fit_sweep(torch, ubw, dev)
@@ -350,6 +351,49 @@ def profile_shape(torch, ubw, dev, spec, steps):
         ubw.lut_gemv(c["packed"], c["ar"], c["ac"], c["x"], n, k, y=y, workspace=c["ws"])
     torch.cuda.synchronize()
     print(json.dumps({"profile_shape": [n, k, nb, b], "steps": steps, "cold_copies": len(copies)}), flush=True)
+
+
+def small_sweep(torch, ubw, dev):
+    """The two cache-resident workloads, reported as time per call (launch-latency bound):
+    the single 256 x 512 GEMV (1 base, fp32 x) and the ternary stack (4 x 256 -> 768 -> 256, two
+    half-scale bases per layer), 64 tokens one after another, each through 8 chained launches.
+    The timed chain feeds each layer's fp32 output straight to the next layer as fp32 x (the
+    kernel reads fp32 activations); the parity test rounds to fp16 between layers instead."""
+    from workloads import single_gemv_256x512, ternary_stack_256x768
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a).to(dev)
+
+    g = single_gemv_256x512(seed=0).gemvs[0]
+    packed = ubw.pack_bases(t(g.bits), g.nb, g.n, g.k)
+    ar, ac, x = t(g.alpha_r), t(g.alpha_c), t(g.x)
+    ws = ubw.workspace(g.n, dev)
+    y = torch.empty((1, g.n), dtype=torch.float32, device=dev)
+    ubw.lut_gemv(packed, ar, ac, x, g.n, g.k, y=y, workspace=ws)
+    us = run_queued(torch, lambda i: ubw.lut_gemv(packed, ar, ac, x, g.n, g.k, y=y, workspace=ws), 400) * 1e3 / 400
+    print(json.dumps({"sweep": "single GEMV 256 x 512, 1 base, fp32 x", "batch": 1, "us": round(us, 2),
+                      "note": "cache-resident: launch-latency bound"}), flush=True)
+
+    wl = ternary_stack_256x768(seed=0)
+    enc = [ubw.ternary_encode(t(L.w), t(L.scale)) for L in wl.ternary]
+    shapes = [L.w.shape for L in wl.ternary]
+    wss = [ubw.workspace(n, dev) for n, _ in shapes]
+    outs = [torch.empty((1, n), dtype=torch.float32, device=dev) for n, _ in shapes]
+    toks = t(wl.tokens.astype(np.float32))
+
+    def token(i):
+        a = toks[i % toks.shape[0]:i % toks.shape[0] + 1]
+        for (packed, ar, ac), (n, k), w, o in zip(enc, shapes, wss, outs):
+            a = ubw.lut_gemv(packed, ar, ac, a, n, k, y=o, workspace=w)
+
+    token(0)
+    ntok = toks.shape[0]
+    ms = run_queued(torch, token, ntok)
+    print(json.dumps({"sweep": "ternary stack 4 x (256 -> 768 -> 256), 8 chained GEMVs per token",
+                      "tokens": ntok, "us_per_token": round(ms * 1e3 / ntok, 2),
+                      "us_per_gemv": round(ms * 1e3 / ntok / len(enc), 2),
+                      "tokens_per_s": round(ntok / ms * 1e3, 1)}), flush=True)
 
 
 def gs_sweep(torch, ubw, dev):
