@@ -89,6 +89,7 @@ def main():
         return
     if args.configs:
         small_sweep(torch, ubw, dev)
+        load_time_sweep(torch, ubw, dev)
         config_sweep(torch, ubw, dev)
         gs_sweep(torch, ubw, dev)
         fit_sweep(torch, ubw, dev)
@@ -394,6 +395,42 @@ def small_sweep(torch, ubw, dev):
                       "tokens": ntok, "us_per_token": round(ms * 1e3 / ntok, 2),
                       "us_per_gemv": round(ms * 1e3 / ntok / len(enc), 2),
                       "tokens_per_s": round(ntok / ms * 1e3, 1)}), flush=True)
+
+
+def load_time_sweep(torch, ubw, dev):
+    """The load-time kernels at the 70B gate shape (28672 x 8192, 3 bases): packing canonical
+    words into tiles, packing from int8 signs, the ternary two-base encoding (one 28672 x 8192
+    int8 matrix), and the tables written to memory (batch 16, 3 bases, K = 8192). HBM-bound:
+    bytes = what each must read and write."""
+    n, k, nb = 28672, 8192, 3
+    kw = (k + 31) // 32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    words = torch.randint(-2**31, 2**31 - 1, (nb, n, kw), dtype=torch.int32, device=dev, generator=gen)
+    signs = torch.randint(-1, 2, (nb, n, k), dtype=torch.int8, device=dev, generator=gen)
+    out = torch.empty(ubw.packed_words(nb, n, k), dtype=torch.int32, device=dev)
+    tern = signs[0].contiguous()
+    scale = torch.rand(n, device=dev, generator=gen)
+    x = torch.randn((16, k), device=dev, generator=gen).half()
+    ac = torch.rand((nb, k), device=dev, generator=gen)
+    packed_bytes = out.numel() * 4
+    cases = [
+        ("pack canonical words -> tiles", lambda i: ubw.pack_bases(words, nb, n, k, out=out), words.numel() * 4 + packed_bytes),
+        ("pack int8 signs -> tiles", lambda i: ubw.pack_bases(signs, nb, n, k, out=out), signs.numel() + packed_bytes),
+        ("ternary encode (one int8 matrix -> 2 bases)", lambda i: ubw.ternary_encode(tern, scale),
+         tern.numel() + ubw.packed_words(2, n, k) * 4 + 4 * (3 * n + 2 * k)),
+        ("tables into memory (b 16, 3 bases, K 8192)", lambda i: ubw.build_lut(x, ac),
+         16 * nb * (k // 8) * 256 * 4 + x.numel() * 2 + ac.numel() * 4),
+    ]
+    for name, fn, by in cases:
+        fn(0)
+        reps = 20
+        ms = run_queued(torch, fn, reps) / reps
+        print(json.dumps({"sweep": "load-time kernels", "kernel": name, "ms": round(ms, 4),
+                          "GBps": round(by / ms / 1e6, 1), "pct_of_peak": round(by / ms / 1e6 / PEAK_GBS * 100, 2),
+                          "bytes": by}), flush=True)
+    del words, signs, out
+    torch.cuda.empty_cache()
 
 
 def gs_sweep(torch, ubw, dev):

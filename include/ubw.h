@@ -103,7 +103,8 @@ int ubw_pack_bases(const void* src, int src_fmt, int nb, int64_t N, int64_t K, i
  *   scale    fp32 [N] per-row scale of the ternary layer
  *   packed   uint32 [ubw_packed_words(2, N, K, g)] output
  *   alpha_r  fp32 [2][N] output;  alpha_c  fp32 [2][K] output
- * Errors: UBW_EINVAL, UBW_EUNSUPPORTED (g), UBW_EALIGN (packed), UBW_EHIP.
+ * Errors: UBW_EINVAL, UBW_EUNSUPPORTED (g), UBW_EALIGN (packed), UBW_ERANGE (more than
+ *         INT_MAX * 256 packed words), UBW_EHIP.
  */
 int ubw_ternary_encode(const int8_t* w, const float* scale, int64_t N, int64_t K, int g,
                        uint32_t* packed, float* alpha_r, float* alpha_c, void* stream);

@@ -253,6 +253,9 @@ def test_other_entry_points_reject():
     assert L.ubw_pack_bases(None, 0, 1, 8, 8, 8, FAKE, None) == EINVAL
     assert L.ubw_pack_bases(FAKE, 5, 1, 8, 8, 8, FAKE, None) == EUNSUP
     assert L.ubw_pack_bases(FAKE, 0, 1, 8, 8, 3, FAKE, None) == EUNSUP
+    big = 1 << 29                                                      # 2^29 x 2^29 signs: 2^53 bits
+    assert L.ubw_pack_bases(FAKE, 0, 1, big, big, 8, FAKE, None) == ERANGE
+    assert L.ubw_ternary_encode(FAKE, FAKE, big, big, 8, FAKE, FAKE, FAKE, None) == ERANGE
     assert L.ubw_pack_bases(FAKE, 0, 1, 8, 8, 8, MISALIGNED, None) == EALIGN
     assert L.ubw_ternary_encode(None, FAKE, 8, 8, 8, FAKE, FAKE, FAKE, None) == EINVAL
     assert L.ubw_ternary_encode(FAKE, FAKE, 8, 8, 8, MISALIGNED, FAKE, FAKE, None) == EALIGN

@@ -134,6 +134,7 @@ int ubw_ternary_encode(const int8_t* w, const float* scale, int64_t N, int64_t K
     if (!w || !scale || !packed || !alpha_r || !alpha_c || !fits_int(N) || !fits_int(K)) return UBW_EINVAL;
     if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
     if (!aligned16(packed)) return UBW_EALIGN;
+    if (packed_words_of(2, N, K) > (int64_t)INT_MAX * 256) return UBW_ERANGE;
     return hip_status(launch_ternary(w, scale, (int)N, (int)K, packed, alpha_r, alpha_c, as_stream(stream)));
 }
 

@@ -191,11 +191,12 @@ __device__ __forceinline__ PackPos pack_pos(int64_t o, int nb, int KT) {
     const int e = (int)(o & 3);
     const int rho = (int)((o >> 2) & 255);
     const int q = (int)((o >> 10) & 1);
-    const int64_t rest = o >> 11;
-    const int k = (int)(rest % nb);
-    const int64_t tile = rest / nb;
-    const int ks = (int)(tile % KT);
-    const int rt = (int)(tile / KT);
+    // o < 2^39 (the host caps the packed size at INT_MAX * 256 words): the tile index fits 32 bits
+    const uint32_t rest = (uint32_t)(o >> 11);
+    const int k = (int)(rest % (uint32_t)nb);
+    const uint32_t tile = rest / (uint32_t)nb;
+    const int ks = (int)(tile % (uint32_t)KT);
+    const int rt = (int)(tile / (uint32_t)KT);
     const int s = 4 * q + e;
     const int wi = s ^ xor_words(rho);
     return PackPos{k, rt * kTileRows + rho, ks * kSliceWords + wi, xor_bytes(rho)};
@@ -216,19 +217,39 @@ __global__ void k_pack_canon(const uint32_t* __restrict__ src, int nb, int N, in
     dst[o] = bytes_for_row(val, p.c);
 }
 
+// Bits of 32 int8 values of a row (columns c0 .. c0 + 31; columns >= K read as bit 0): bit b is
+// v > 0 (ge = false) or v >= 0 (ge = true). Whole, aligned 32-byte runs are read as two 16-byte
+// loads (four threads cover 128 contiguous bytes of a row), ragged ones byte by byte.
+__device__ __forceinline__ uint32_t int8_bits(const int8_t* r, int c0, int K, bool ge) {
+    uint32_t val = 0;
+    if (c0 + 32 <= K && (reinterpret_cast<uintptr_t>(r + c0) & 15u) == 0) {
+        const uint4 a = *reinterpret_cast<const uint4*>(r + c0);
+        const uint4 b = *reinterpret_cast<const uint4*>(r + c0 + 16);
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int8_t v = (int8_t)(w[i >> 2] >> (8 * (i & 3)));
+            if (ge ? v >= 0 : v > 0) val |= 1u << i;
+        }
+        return val;
+    }
+    for (int i = 0; i < 32; ++i) {
+        const int col = c0 + i;
+        if (col < K) {
+            const int8_t v = r[col];
+            if (ge ? v >= 0 : v > 0) val |= 1u << i;
+        }
+    }
+    return val;
+}
+
 __global__ void k_pack_int8(const int8_t* __restrict__ src, int nb, int N, int K, int KT, int64_t total,
                             uint32_t* __restrict__ dst) {
     const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (o >= total) return;
     const PackPos p = pack_pos(o, nb, KT);
     uint32_t val = 0;
-    if (p.row < N) {
-        const int8_t* r = src + ((int64_t)p.k * N + p.row) * K;
-        for (int b = 0; b < 32; ++b) {
-            const int col = p.wcol * 32 + b;
-            if (col < K && r[col] > 0) val |= 1u << b;
-        }
-    }
+    if (p.row < N) val = int8_bits(src + ((int64_t)p.k * N + p.row) * K, p.wcol * 32, K, false);
     dst[o] = bytes_for_row(val, p.c);
 }
 
@@ -240,16 +261,7 @@ __global__ void k_ternary_bits(const int8_t* __restrict__ w, int N, int K, int K
     if (o >= total) return;
     const PackPos p = pack_pos(o, 2, KT);
     uint32_t val = 0;
-    if (p.row < N) {
-        const int8_t* r = w + (int64_t)p.row * K;
-        for (int b = 0; b < 32; ++b) {
-            const int col = p.wcol * 32 + b;
-            if (col < K) {
-                const int8_t v = r[col];
-                if (p.k == 0 ? (v >= 0) : (v > 0)) val |= 1u << b;
-            }
-        }
-    }
+    if (p.row < N) val = int8_bits(w + (int64_t)p.row * K, p.wcol * 32, K, p.k == 0);
     dst[o] = bytes_for_row(val, p.c);
 }
 
