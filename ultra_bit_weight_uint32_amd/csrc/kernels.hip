@@ -257,12 +257,20 @@ __global__ void k_pack_int8(const int8_t* __restrict__ src, int nb, int N, int K
 // w = +1 -> (+1,+1), w = -1 -> (-1,-1), w = 0 -> (+1,-1).
 __global__ void k_ternary_bits(const int8_t* __restrict__ w, int N, int K, int KT, int64_t total,
                                uint32_t* __restrict__ dst) {
-    const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // one thread per base-0 word; the base-1 word at the same position is in the next tile
+    // (tiles of one slice are [base][...] adjacent), and both come from the same 32 bytes
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t o = ((t >> 11) << 12) | (t & 2047);  // tile pair t / 2048, word t % 2048 of base 0
     if (o >= total) return;
     const PackPos p = pack_pos(o, 2, KT);
-    uint32_t val = 0;
-    if (p.row < N) val = int8_bits(w + (int64_t)p.row * K, p.wcol * 32, K, p.k == 0);
-    dst[o] = bytes_for_row(val, p.c);
+    uint32_t v0 = 0, v1 = 0;
+    if (p.row < N) {
+        const int8_t* r = w + (int64_t)p.row * K;
+        v0 = int8_bits(r, p.wcol * 32, K, true);
+        v1 = int8_bits(r, p.wcol * 32, K, false);
+    }
+    dst[o] = bytes_for_row(v0, p.c);
+    dst[o + kTileWords] = bytes_for_row(v1, p.c);
 }
 
 __global__ void k_ternary_scales(const float* __restrict__ scale, int N, int K, float* __restrict__ alpha_r,
@@ -968,7 +976,7 @@ hipError_t launch_ternary(const int8_t* w, const float* scale, int N, int K, uin
                           float* alpha_c, hipStream_t s) {
     const int NT = (int)ceil_div(N, kTileRows), KT = (int)ceil_div(K, kSliceCols);
     const int64_t total = (int64_t)2 * NT * KT * kTileWords;
-    hipLaunchKernelGGL(k_ternary_bits, dim3(grid_for(total, 256)), dim3(256), 0, s, w, N, K, KT, total, packed);
+    hipLaunchKernelGGL(k_ternary_bits, dim3(grid_for(total / 2, 256)), dim3(256), 0, s, w, N, K, KT, total, packed);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_ternary_scales, dim3(grid_for(N > K ? N : K, 256)), dim3(256), 0, s, scale, N, K, alpha_r,
