@@ -209,7 +209,7 @@ def test_fit_rejects():
     assert L.ubw_fit_workspace_bytes(0, 10, ctypes.byref(sz)) == EINVAL
     assert L.ubw_fit_workspace_bytes(10, 10, None) == EINVAL
     assert L.ubw_fit_workspace_bytes(100, 300, ctypes.byref(sz)) == 0
-    assert sz.value == 4 * (2 * 300 + 2 + 2)                      # 2 row chunks of 64, 2 column blocks
+    assert sz.value == 4 * (2 * 300 + 2 + 5)                      # 2 row chunks of 64, 5 blocks of 64 columns
     need = sz.value
     args = dict(w=FAKE, dt=0, N=100, K=300, nb=2, iters=3, bits=FAKE, ar=FAKE, ac=FAKE, res=FAKE, ws=FAKE,
                 wsb=need, stream=None)

@@ -111,18 +111,36 @@ __global__ __launch_bounds__(kFitThreads) void k_fit_colsum(const float* R, int 
     }
 }
 
-// alpha_c[j] = sum_c part[c][j] / sum_c sq[c] (0 when the denominator is 0); each column
-// block also writes sqc[b] = sum of alpha_c^2 over its columns.
+// alpha_c[j] = sum_c part[c][j] / sum_c sq[c] (0 when the denominator is 0); each workgroup
+// also writes sqc[b] = sum of alpha_c^2 over its kFinCols columns. A workgroup takes 64
+// columns (one per lane); its 4 waves split the chunks, each with 4 independent sums so that
+// the loads overlap, and the wave sums are added in a fixed order.
+constexpr int kFinCols = 64;
 __global__ __launch_bounds__(kFitThreads) void k_fit_colfinish(const float* part, const float* sq, int chunks,
                                                                int K, float* ac, float* sqc) {
     __shared__ float red[4];
-    const int j = blockIdx.x * kFitThreads + threadIdx.x;
-    float den = 0.f;
-    for (int c = 0; c < chunks; ++c) den += sq[c];
-    float v = 0.f;
+    __shared__ float colp[4][kFinCols];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int j = blockIdx.x * kFinCols + lane;
+    float d = 0.f;
+    for (int c = threadIdx.x; c < chunks; c += kFitThreads) d += sq[c];
+    const float den = block_sum(d, red);
+    float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f;
     if (j < K) {
-        float num = 0.f;
-        for (int c = 0; c < chunks; ++c) num += part[(int64_t)c * K + j];
+        int c = wv;
+        for (; c + 12 < chunks; c += 16) {
+            n0 += part[(int64_t)c * K + j];
+            n1 += part[(int64_t)(c + 4) * K + j];
+            n2 += part[(int64_t)(c + 8) * K + j];
+            n3 += part[(int64_t)(c + 12) * K + j];
+        }
+        for (; c < chunks; c += 4) n0 += part[(int64_t)c * K + j];
+    }
+    colp[wv][lane] = (n0 + n1) + (n2 + n3);
+    __syncthreads();
+    float v = 0.f;
+    if (wv == 0 && j < K) {
+        const float num = (colp[0][lane] + colp[1][lane]) + (colp[2][lane] + colp[3][lane]);
         v = den > 0.f ? num / den : 0.f;
         ac[j] = v;
     }
@@ -130,7 +148,9 @@ __global__ __launch_bounds__(kFitThreads) void k_fit_colfinish(const float* part
     if (threadIdx.x == 0) sqc[blockIdx.x] = t;
 }
 
-// alpha_r[r] = sum_j |R[r][j]| ac[j] / sum_b sqc[b] (0 when the denominator is 0).
+// alpha_r[r] = sum_j |R[r][j]| ac[j] / sum_b sqc[b] (0 when the denominator is 0); the
+// denominator's partials are read by all threads at once and added in the same tree order
+// in every workgroup.
 __global__ __launch_bounds__(kFitThreads) void k_fit_rowals(const float* R, int K, const float* ac,
                                                             const float* sqc, int cblocks, float* ar) {
     __shared__ float red[4];
@@ -139,8 +159,9 @@ __global__ __launch_bounds__(kFitThreads) void k_fit_rowals(const float* R, int 
     float s = 0.f;
     for (int j = threadIdx.x; j < K; j += kFitThreads) s += fabsf(R[row + j]) * ac[j];
     s = block_sum(s, red);
-    float den = 0.f;
-    for (int b = 0; b < cblocks; ++b) den += sqc[b];
+    float dp = 0.f;
+    for (int b = threadIdx.x; b < cblocks; b += kFitThreads) dp += sqc[b];
+    const float den = block_sum(dp, red);
     if (threadIdx.x == 0) ar[r] = den > 0.f ? s / den : 0.f;
 }
 
@@ -155,6 +176,7 @@ hipError_t fit_t(const WT* w, int N, int K, int nb, int iters, uint32_t* bits, f
     const int kw = (K + 31) / 32;
     const int chunks = (N + kFitChunk - 1) / kFitChunk;
     const int cblocks = (K + kFitThreads - 1) / kFitThreads;
+    const int fblocks = (K + kFinCols - 1) / kFinCols;
     float* part = ws;
     float* sq = part + (int64_t)chunks * K;
     float* sqc = sq + chunks;
@@ -168,8 +190,8 @@ hipError_t fit_t(const WT* w, int N, int K, int nb, int iters, uint32_t* bits, f
         hipLaunchKernelGGL(k_fit_ones, dim3(cblocks), dim3(kFitThreads), 0, s, ac, K);
         for (int it = 0; it < iters; ++it) {
             hipLaunchKernelGGL(k_fit_colsum, dim3(cblocks, chunks), dim3(kFitThreads), 0, s, R, N, K, ar, part, sq);
-            hipLaunchKernelGGL(k_fit_colfinish, dim3(cblocks), dim3(kFitThreads), 0, s, part, sq, chunks, K, ac, sqc);
-            hipLaunchKernelGGL(k_fit_rowals, dim3(N), dim3(kFitThreads), 0, s, R, K, ac, sqc, cblocks, ar);
+            hipLaunchKernelGGL(k_fit_colfinish, dim3(fblocks), dim3(kFitThreads), 0, s, part, sq, chunks, K, ac, sqc);
+            hipLaunchKernelGGL(k_fit_rowals, dim3(N), dim3(kFitThreads), 0, s, R, K, ac, sqc, fblocks, ar);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -183,7 +205,7 @@ hipError_t fit_t(const WT* w, int N, int K, int nb, int iters, uint32_t* bits, f
 
 int64_t fit_workspace_floats(int64_t N, int64_t K) {
     const int64_t chunks = ceil_div(N, kFitChunk);
-    return chunks * K + chunks + ceil_div(K, kFitThreads);
+    return chunks * K + chunks + ceil_div(K, kFinCols);
 }
 
 hipError_t launch_fit(const void* w, int w_dtype, int N, int K, int nb, int iters, uint32_t* bits, float* alpha_r,

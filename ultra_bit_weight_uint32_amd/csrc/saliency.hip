@@ -23,7 +23,8 @@
 //   k_score_part / k_score_finish   column sums of W^2 in row chunks, then score = sum / d^2.
 //   k_rank         rank of every score (count of larger scores, equal ones at lower indices),
 //                  in 16 partial counts per score over slices of the scores.
-//   k_select       the columns of rank < s, ascending, by one prefix scan.
+//   k_rank_finish  adds the partial counts: one flag per column, rank < s.
+//   k_select       the flagged columns, ascending, by one prefix scan.
 // Everything after the Gram matrix is fp32 vector arithmetic in a fixed order.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -201,61 +202,64 @@ constexpr int kCB = 64;  // Cholesky block
 
 // Cholesky of diagonal block kb (lower, in LDS), written back, and its inverse to Linv[kb].
 // Rows/columns past K act as an identity block.
-// 1024 threads: each of the 128 steps below is a short chain of LDS reads and multiply-adds
-// per thread, and 16 waves keep several chains in flight (measured per 64 x 64 block: one wave
-// 303 us, 4 waves 108 us, 16 waves 66 us).
+// Both eliminations defer their divisions so that each step needs one barrier: step c of the
+// factorization subtracts S[r][c] S[q][c] / S[c][c] from the trailing lower triangle of the
+// unscaled Schur complement S, which leaves column c untouched (it is scaled by the root of its
+// pivot at the end); step q of the inverse (solve L Z = I by rows) eliminates with row q of Z
+// divided on the fly, which leaves row q untouched (divided when written out).
+// 1024 threads: each step is a short chain of LDS reads and multiply-adds per thread, and 16
+// waves keep several chains in flight.
 constexpr int kDiagThreads = 1024;
 
 __global__ __launch_bounds__(kDiagThreads) void k_chol_diag(float* A, int K, int kb, float* Linv, float* misc) {
     __shared__ float L[kCB][kCB + 1];
     __shared__ float Z[kCB][kCB + 1];
+    __shared__ float piv[kCB];
     const int tid = threadIdx.x;
     const int o = kb * kCB;
     const int n = K - o < kCB ? K - o : kCB;
     for (int e = tid; e < kCB * kCB; e += kDiagThreads) {
         const int r = e / kCB, c = e % kCB;
         L[r][c] = (r < n && c < n) ? A[(int64_t)(o + r) * K + o + c] : (r == c ? 1.f : 0.f);
+        Z[r][c] = r == c ? 1.f : 0.f;
     }
     __syncthreads();
+    // thread: column q = tid % 64, rows tid / 64 + 16 k
+    const int q = tid & 63;
     for (int c = 0; c < kCB; ++c) {
         float p = L[c][c];
-        if (!(p > 0.f)) {  // not positive definite in fp32: flag it, keep going with a tiny pivot
-            if (tid == 0) misc[1] = 1.f;
-            p = 1e-30f;
-        }
-        const float piv = sqrtf(p);
-        __syncthreads();
-        for (int r = c + 1 + tid; r < kCB; r += kDiagThreads) L[r][c] /= piv;
-        __syncthreads();
-        if (tid == 0) L[c][c] = piv;
-        // trailing update of the lower triangle: L[r][q] -= L[r][c] L[q][c], c < q <= r
-        // (thread: column q = tid % 64, rows tid / 64 + 16 k)
-        {
-            const int q = tid & 63;
-            if (q > c)
-                for (int r = c + 1 + (tid >> 6); r < kCB; r += kDiagThreads / 64)
-                    if (q <= r) L[r][q] -= L[r][c] * L[q][c];
+        if (!(p > 0.f)) p = 1e-30f;  // not positive definite in fp32: flagged below
+        if (q > c) {
+            const float m = L[q][c] / p;
+            for (int r = c + 1 + (tid >> 6); r < kCB; r += kDiagThreads / 64)
+                if (q <= r) L[r][q] -= L[r][c] * m;
         }
         __syncthreads();
     }
-    // inverse of the lower factor, right-looking: Z = I; for each q, row q of Z is final once
-    // divided by L[q][q], and is then eliminated from the rows below (all threads at once)
-    for (int e = tid; e < kCB * kCB; e += kDiagThreads) Z[e / kCB][e % kCB] = (e / kCB == e % kCB) ? 1.f : 0.f;
+    if (tid < kCB) {
+        const float p = L[tid][tid];
+        if (!(p > 0.f)) misc[1] = 1.f;  // keep going with a tiny pivot
+        piv[tid] = sqrtf(p > 0.f ? p : 1e-30f);
+    }
     __syncthreads();
-    for (int q = 0; q < kCB; ++q) {
-        if (tid <= q) Z[q][tid] /= L[q][q];
-        __syncthreads();
-        {  // rows below q, columns 0..q (thread: column tid % 64, rows tid / 64 + 16 k)
-            const int c = tid & 63;
-            if (c <= q)
-                for (int r = q + 1 + (tid >> 6); r < kCB; r += kDiagThreads / 64) Z[r][c] -= L[r][q] * Z[q][c];
+    for (int e = tid; e < kCB * kCB; e += kDiagThreads) {
+        const int r = e / kCB, c = e % kCB;
+        if (r > c) L[r][c] /= piv[c];
+        else if (r == c) L[r][c] = piv[c];
+    }
+    __syncthreads();
+    for (int qq = 0; qq < kCB; ++qq) {
+        const int c = q;  // column of Z
+        if (c <= qq) {
+            const float u = Z[qq][c] / L[qq][qq];  // final Z[qq][c]
+            for (int r = qq + 1 + (tid >> 6); r < kCB; r += kDiagThreads / 64) Z[r][c] -= L[r][qq] * u;
         }
         __syncthreads();
     }
     for (int e = tid; e < kCB * kCB; e += kDiagThreads) {
         const int r = e / kCB, c = e % kCB;
         if (r < n && c < n && c <= r) A[(int64_t)(o + r) * K + o + c] = L[r][c];
-        Linv[(int64_t)kb * kCB * kCB + e] = Z[r][c];
+        Linv[(int64_t)kb * kCB * kCB + e] = Z[r][c] / L[r][r];  // entries above the diagonal are 0
     }
 }
 
@@ -492,8 +496,17 @@ __global__ __launch_bounds__(256) void k_score_finish(const float* part, int chu
                                                       float* score) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     if (j >= K) return;
-    float s = 0.f;
-    for (int c = 0; c < chunks; ++c) s += part[(int64_t)c * K + j];
+    // four independent sums so the loads of the partials overlap, added in a fixed order
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    int c = 0;
+    for (; c + 3 < chunks; c += 4) {
+        s0 += part[(int64_t)c * K + j];
+        s1 += part[(int64_t)(c + 1) * K + j];
+        s2 += part[(int64_t)(c + 2) * K + j];
+        s3 += part[(int64_t)(c + 3) * K + j];
+    }
+    for (; c < chunks; ++c) s0 += part[(int64_t)c * K + j];
+    const float s = (s0 + s1) + (s2 + s3);
     score[j] = s / (d[j] * d[j]);
 }
 
@@ -523,16 +536,22 @@ __global__ __launch_bounds__(256) void k_rank(const float* score, int K, int* cn
 // One workgroup of 1024 threads: idx = the selected columns in ascending order (at most s of
 // them: ranks are distinct for any scores that compare, so exactly s are selected; NaN scores,
 // which compare with nothing, can break that, and then misc[1] is set to 2).
-__global__ __launch_bounds__(1024) void k_select(const int* rk, int K, int s, int32_t* idx, float* misc) {
+// sel[j] = rank_j < s, the rank being the sum of the kSplit partial counts (in place: rk[j]
+// holds the flag afterwards).
+__global__ __launch_bounds__(256) void k_rank_finish(int* rk, int K, int s) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= K) return;
+    int r = 0;
+    for (int g = 0; g < kSplit; ++g) r += rk[(int64_t)g * K + j];
+    rk[j] = r < s ? 1 : 0;
+}
+
+__global__ __launch_bounds__(1024) void k_select(const int* sel, int K, int s, int32_t* idx, float* misc) {
     __shared__ int cnt[1024];
     const int tid = threadIdx.x;
     const int per = (K + 1023) / 1024;
     const int b = tid * per, e = b + per < K ? b + per : K;
-    auto selected = [&](int j) {
-        int r = 0;
-        for (int g = 0; g < kSplit; ++g) r += rk[(int64_t)g * K + j];
-        return r < s ? 1 : 0;
-    };
+    auto selected = [&](int j) { return sel[j]; };
     int c = 0;
     for (int j = b; j < e; ++j) c += selected(j);
     cnt[tid] = c;
@@ -602,6 +621,7 @@ hipError_t launch_saliency(float* H, int K, float damp, const float* W, int N, i
     hipLaunchKernelGGL(k_score_part, dim3(cb, chunks), dim3(256), 0, st, W, N, K, part);
     hipLaunchKernelGGL(k_score_finish, dim3(cb), dim3(256), 0, st, part, chunks, K, d, score);
     hipLaunchKernelGGL(k_rank, dim3(cb, kSplit), dim3(256), 0, st, score, K, rk);
+    hipLaunchKernelGGL(k_rank_finish, dim3(cb), dim3(256), 0, st, rk, K, s);
     hipLaunchKernelGGL(k_select, dim3(1), dim3(1024), 0, st, rk, K, s, idx, misc);
     return hipGetLastError();
 }
