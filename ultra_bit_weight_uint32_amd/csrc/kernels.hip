@@ -438,8 +438,9 @@ struct StepParams {
     int Urg;          // units per row group, both segments
     int U;            // units in the whole list (< 2^31)
     int G;            // workgroups
+    int Gu;           // workgroups with units (the first Gu); the others only zero y
     int mode;
-    int Q, R;         // U = Q G + R: workgroup g takes Q units, plus one if g < R
+    int Q, R;         // U = Q Gu + R: workgroup g < Gu takes Q units, plus one if g < R
     FastDiv dUS[2];   // division by US[si]
     FastDiv dNb[2];   // division by seg[si].nb
 };
@@ -608,9 +609,13 @@ __device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const Step
     }
 }
 
-// First unit of workgroup g's range: the first R workgroups take Q + 1 units, the rest Q.
+// First unit of workgroup g's range: the first R workgroups take Q + 1 units, the rest of the
+// first Gu take Q, and the workgroups past Gu none. (The first workgroups start first; with
+// one per CU and two units on some, measured on 4096 x 4096 with 5% salient columns: longer
+// ranges first 6.12 us, in the middle 6.36 us, last 7.02 us.)
 __device__ __forceinline__ uint32_t range_start(const StepParams& P, uint32_t g) {
-    return g * (uint32_t)P.Q + (g < (uint32_t)P.R ? g : (uint32_t)P.R);
+    const uint32_t x = g * (uint32_t)P.Q + (g < (uint32_t)P.R ? g : (uint32_t)P.R);
+    return x < (uint32_t)P.U ? x : (uint32_t)P.U;  // from g = Gu on: Gu Q + R = U
 }
 
 // The body of a step: workgroup g of the P.G that work on the GEMV described by P.
@@ -660,10 +665,11 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
     // does so right after requesting its first unit's data, so the wait for the exchanges
     // overlaps that request and covers nothing else.
     const bool first_mode = P.mode == kModeFirst;
-    // Row group rg is zeroed by workgroup (rg + off) mod G. With off = NRG (when G >= 2 NRG) the
-    // zeroing workgroups are not the first ones, which the device places on CUs that also receive
-    // the workgroups beyond one per CU.
-    const int zoff = 2 * P.NRG <= P.G ? P.NRG : 0;
+    // Row group rg is zeroed by workgroup (rg + off) mod G. With workgroups that have no units
+    // (G > Gu) those do it (off = Gu), so that no workgroup with units waits for the exchanges;
+    // otherwise, with off = NRG (when G >= 2 NRG), the zeroing workgroups are not the first ones,
+    // which the device places on CUs that also receive the workgroups beyond one per CU.
+    const int zoff = P.G > P.Gu ? P.Gu : (2 * P.NRG <= P.G ? P.NRG : 0);
     const int zrg0 = g >= zoff ? g - zoff : g - zoff + P.G;  // first row group this workgroup zeroes
     bool zpend = first_mode && zrg0 < P.NRG;
     auto rg_word = [&](int rg) { return a.ws + kWsHeaderWords + kWsRowGroupWords * rg; };
@@ -1030,15 +1036,35 @@ static int64_t resident_capacity_group() {
     return capacity_of(k_gemv8_group<XT, RPL, BMAX, XL>, cap);
 }
 
-// Split of P's units over G workgroups and the final output mode; zero-fills y first when the
-// single-launch protocol cannot be used (no workspace, or too many units per row group).
-static hipError_t finish_params(StepParams& P, int64_t G, hipStream_t s) {
-    P.G = (int)G;
-    P.Q = P.U / P.G;
-    P.R = P.U - P.Q * P.G;
+// Workgroups with units for U units when the device holds cap at once (two per CU): one per
+// CU at batch 1 when the units fit in two per CU. A second workgroup on a CU runs behind the
+// first (the CU issues the older waves' instructions first), so with one unit each the doubled
+// CUs finish last; one workgroup per CU taking two units where needed ends sooner (measured,
+// batch 1, K = 4096: 272 units 6.36 -> 6.24 us, 384 units 6.53 -> 6.44, 512 units
+// 7.16 -> 6.61). With more units, or a larger batch, two workgroups per CU hide more latency.
+static int64_t default_workgroups(int64_t U, int64_t cap, int batch) {
+    const int64_t cus = cap / 2;
+    if (batch == 1 && U > cus && U <= cap) return cus;
+    return cap;
+}
+
+// Split of P's units over Gu workgroups and the final output mode; zero-fills y first when the
+// single-launch protocol cannot be used (no workspace, or too many units per row group). With
+// the single-launch protocol, every workgroup taking the same number of units (R = 0) and room
+// on the device (Gu + NRG <= cap), NRG more workgroups without units zero y, one row group
+// each: the exchanges' round trip then delays no workgroup with units (measured on 4096 x 4096,
+// 256 units: 5.84 -> 5.36 us). With R > 0 the zeroing workgroups (from NRG on) are ones with
+// the shorter ranges, which finish before the longer ones anyway, and extra workgroups would
+// only crowd the CUs of the longer ones (4096 x 4096 with 5% salient columns, 272 units:
+// 6.12 us without, 6.29 us with).
+static hipError_t finish_params(StepParams& P, int64_t Gu, int64_t cap, hipStream_t s) {
+    P.Gu = (int)Gu;
+    P.G = (int)Gu;
+    P.Q = P.U / P.Gu;
+    P.R = P.U - P.Q * P.Gu;
     // every workgroup holds exactly one whole row group (one segment only: a refinement
     // segment's units of a row group sit in another part of the list): plain stores
-    const bool whole_rows = P.G == P.NRG && P.US[1] == 0;
+    const bool whole_rows = P.Gu == P.NRG && P.US[1] == 0;
     if (P.mode == kModeFirst && whole_rows) P.mode = kModeStore;
     // the arrival field counts a row group's units (Urg) and must not overflow into the generation
     if (P.mode == kModeFirst && (P.a.ws == nullptr || P.Urg + 1 > (int)kArrMask)) {
@@ -1046,6 +1072,7 @@ static hipError_t finish_params(StepParams& P, int64_t G, hipStream_t s) {
         if (e != hipSuccess) return e;
         P.mode = kModeAtomic;
     }
+    if (P.mode == kModeFirst && P.R == 0 && Gu + P.NRG <= cap) P.G = (int)(Gu + P.NRG);
     return hipSuccess;
 }
 
@@ -1054,17 +1081,18 @@ static hipError_t launch_step_t(StepParams P, hipStream_t s) {
     const int64_t cap = resident_capacity<XT, RPL, BMAX, XL, GS>();
     if (cap <= 0) return hipErrorInvalidConfiguration;
     // Never more workgroups than the device holds at once: the flag waits rely on it.
-    int64_t G = P.a.workgroups > 0 ? P.a.workgroups : cap;
+    int64_t G = P.a.workgroups > 0 ? P.a.workgroups : default_workgroups(P.U, cap, P.a.batch);
     G = G < cap ? G : cap;
     G = G < P.U ? G : P.U;
-    hipError_t e = finish_params(P, G, s);
+    hipError_t e = finish_params(P, G, cap, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_gemv8<XT, RPL, BMAX, XL, GS>), dim3((unsigned)P.G), dim3(kStepThreads), 0, s, P);
     return hipGetLastError();
 }
 
 // Grouped launch: the workgroups the device holds at once (at most the total units) are shared
-// out in proportion to each GEMV's units, at least one each.
+// out in proportion to each GEMV's units, at least one each. (One per CU, as default_workgroups
+// picks for single launches, measured slower here: 70B q+k+v at batch 1 14.4 -> 17.0 us.)
 template <typename XT, int RPL, int BMAX, bool XL>
 static hipError_t launch_group_t(GroupParams GP, hipStream_t s) {
     const int64_t cap = resident_capacity_group<XT, RPL, BMAX, XL>();
@@ -1091,7 +1119,7 @@ static hipError_t launch_group_t(GroupParams GP, hipStream_t s) {
     }
     GP.start[0] = 0;
     for (int i = 0; i < GP.count; ++i) {
-        hipError_t e = finish_params(GP.p[i], Gi[i], s);
+        hipError_t e = finish_params(GP.p[i], Gi[i], 0, s);
         if (e != hipSuccess) return e;
         GP.start[i + 1] = GP.start[i] + (int)Gi[i];
     }
