@@ -59,8 +59,11 @@ typedef enum {
 enum { UBW_F32 = 0, UBW_F16 = 1 };                       /* activation dtypes */
 enum { UBW_SRC_CANON_BITS = 0, UBW_SRC_INT8_SIGNS = 1 };  /* ubw_pack_bases sources */
 
-/* Largest batch one GEMV call accepts. Batches above 4 rows are processed as consecutive
- * launches of 4 activation rows each on the call's stream. */
+/* Largest batch one GEMV call accepts. Batches of 9 rows or more run in one launch on the
+ * matrix cores (the sign bits expanded to fp16 +-1, v = alpha_c * x split into fp16 high and
+ * low parts, fp32 accumulation: the same result as the tables up to fp32 summation order) when
+ * the call has per-row scales and at most six bases (main + refinement); otherwise batches
+ * above 4 rows run through the tables as consecutive launches of 4 rows on the call's stream. */
 #define UBW_MAX_BATCH 16
 /* columns per row scale in ubw_lut_gemv_gs */
 #define UBW_GROUP_COLS 128
@@ -329,7 +332,7 @@ int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, i
 /*
  * Test and tuning export: ubw_lut_gemv (mode = 0), ubw_vcm_gather_refine (mode = 1) or the
  * main bases of ubw_lut_gemv_gs (mode = 2: alpha_r is then its fp16 alpha_rg) with an
- * explicit launch geometry. The kernel walks a list of units (a unit: rows_per_group tiles of
+ * explicit launch geometry, always through the tables (at every batch). The kernel walks a list of units (a unit: rows_per_group tiles of
  * 256 rows x two (256-column slice, base) items) split into equal contiguous ranges over
  * `workgroups` persistent workgroups (0 = as many as the device holds at once; larger values
  * are capped to that). rows_per_group is 1, 2 or 4 for batch 1 and 1 or 2 above

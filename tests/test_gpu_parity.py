@@ -808,3 +808,45 @@ def test_fp32_activations_in_variants(batch):
     outs = ubw.lut_gemv_multi([multi_entry(g), multi_entry(h)], dev(g.x), k)
     assert np.array_equal(host(outs[0]).astype(np.float64), oracle_gemv(g))
     assert np.array_equal(host(outs[1]).astype(np.float64), oracle_gemv(h))
+
+
+# ------------------------------------------------------------------------------------------
+# batches of 9+ rows on the matrix cores (default path) vs the tables (explicit geometry)
+
+@pytest.mark.parametrize("n,k,nb,s,ns,batch,xdt,xscale", [
+    (300, 200, 2, 0, 0, 9, np.float16, 1.0),         # one slice: one chunk, plain stores
+    (1000, 3000, 3, 300, 2, 16, np.float32, 1e4),    # large activations: staging scale < 1
+    (777, 1501, 3, 100, 3, 9, np.float32, 1e-5),     # tiny activations: staging scale > 1
+    (4100, 700, 1, 37, 1, 12, np.float16, 1.0),      # many row tiles, ragged last tile
+    (256, 4096, 2, 205, 2, 16, np.float16, 1.0),     # one row tile, many chunks
+])
+def test_matrix_core_batches_match_oracle(n, k, nb, s, ns, batch, xdt, xscale):
+    rng = np.random.default_rng(n + k + batch)
+    g = make_gemv(rng, "mc", n, k, nb, s=s, ns=ns, batch=batch, x_dtype=np.float32)
+    g.x = (g.x * xscale).astype(xdt)
+    ref = oracle_gemv(g)
+    for mode in MODES:
+        y = torch.full((batch, n), float("nan"), device=DEV)
+        assert max_rel_err(gpu_gemv(g, y=y, mode=mode), ref) <= TOL, mode
+    # accumulate into values of the result's own size (fp32 sums at a larger scale would round
+    # away more than the tolerance of a small result)
+    y0 = (rng.standard_normal((batch, n)) * np.abs(ref).max()).astype(np.float32)
+    got = gpu_gemv(g, y=dev(y0), accumulate=True)
+    assert max_rel_err(got, ref + y0.astype(np.float64)) <= TOL
+
+
+def test_matrix_core_and_tables_agree_and_seven_bases_fall_back():
+    """The same integer problem through the matrix cores (default) and the tables (explicit
+    geometry) gives the same exact result; with seven bases the default path is the tables."""
+    rng = np.random.default_rng(77)
+    n, k = 700, 1300
+    for nb, ns in ((3, 3), (4, 3)):
+        g = make_integer_gemv(rng, n, k, nb, s=90, ns=ns, batch=10)
+        ref = oracle_gemv(g)
+        assert np.array_equal(gpu_gemv(g, mode="fused"), ref), (nb, ns)
+        y = torch.zeros((10, n), device=DEV)
+        ubw.lut_gemv_geometry(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y,
+                              rows_per_group=1)
+        ubw.lut_gemv_geometry(pack(g.bits_s, g.s), dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), n, g.s, y,
+                              idx=dev(g.idx), k=k, accumulate=True, rows_per_group=1)
+        assert np.array_equal(host(y).astype(np.float64), ref), (nb, ns)

@@ -10,7 +10,7 @@ import time
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libubw.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "fit.hip", "saliency.hip", "api.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "mfma.hip", "fit.hip", "saliency.hip", "api.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -362,6 +362,7 @@ int ubw_lut_gemv_geometry(const uint32_t* packed, const void* alpha_r, const flo
     }
     a.rows_per_group = rows_per_group;
     a.workgroups = workgroups;
+    a.tables_only = 1;
     return run_step(a, stream);
 }
 

@@ -1248,8 +1248,12 @@ static hipError_t launch_step_rows(const StepArgs& a, hipStream_t s) {
     return dispatch_instance<float>(a.batch, a.rows_per_group, xl, go);
 }
 
-// Several GEMVs that share x, batch, dtype and rows_per_group, in one launch.
+static bool use_mfma(const StepArgs& a) {
+    return !a.tables_only && a.batch >= kMfmaMinBatch && mfma_step_supported(a);
+}
+
 hipError_t launch_step(const StepArgs& a, hipStream_t s) {
+    if (use_mfma(a)) return launch_step_mfma(a, s);
     if (a.batch <= kBatchChunk) return launch_step_rows(a, s);
     for (int r0 = 0; r0 < a.batch; r0 += kBatchChunk) {
         hipError_t e = launch_step_rows(batch_chunk(a, r0), s);
@@ -1280,8 +1284,19 @@ static hipError_t launch_step_group_rows(const StepArgs* a, int count, hipStream
     return dispatch_instance<float>(a[0].batch, a[0].rows_per_group, xl, go);
 }
 
+// Several GEMVs that share x, batch, dtype and rows_per_group, in one launch (on the matrix
+// cores: one launch per GEMV).
 hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s) {
     if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
+    bool all_mfma = true;
+    for (int i = 0; i < count; ++i) all_mfma = all_mfma && use_mfma(a[i]);
+    if (all_mfma) {
+        for (int i = 0; i < count; ++i) {
+            hipError_t e = launch_step_mfma(a[i], s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     if (a[0].batch <= kBatchChunk) return launch_step_group_rows(a, count, s);
     for (int r0 = 0; r0 < a[0].batch; r0 += kBatchChunk) {
         StepArgs c[kMaxGroup];

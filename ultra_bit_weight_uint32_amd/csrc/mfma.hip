@@ -1,0 +1,351 @@
+// The GEMV step for several activation rows at once on the matrix cores.
+//
+// "FluxBin" technical summary, "1. Algorithm innovation" and "2. Kernel design": each base is
+// (alpha_r alpha_c^T) (.) B with B in {-1,+1}, so y_b = sum_k alpha_r^(k) (.) (B^(k) v_b^(k)) with
+// v_b^(k) = alpha_c^(k) (.) x_b. The page's table lookup replaces the multiply-adds of one
+// activation row; with several rows the tables must be built and searched once per row, while
+// B^(k) V^(k) (V = the rows' v side by side) is a dense contraction whose cost does not grow with
+// the rows up to the matrix instruction's width. Here the sign bits are expanded to fp16 +-1
+// (exact) and multiplied on v_mfma_f32_16x16x32_f16 against V split into fp16 high and low
+// parts (v = hi + lo to about 2^-22 relative), accumulating in fp32: the result matches the
+// table path's fp32 arithmetic up to summation order. Each activation row of a staged slice is
+// scaled by a power of two (exact) that puts its largest |v| in [2^14, 2^15), so no value
+// overflows fp16 and small ones keep their precision; the MFMA result of the slice is scaled
+// back before it is added to the running sums. Main bases and the salient refinement (columns
+// gathered through idx) go through the same loop.
+//
+// Workgroup (row tile rt, chunk kc): 256 threads, 4 waves, wave w owns tile rows 64 w .. +63 as
+// four 16-row blocks. For each base and each 256-column slice of the chunk:
+//   * the packed words of the wave's rows are loaded (the tile layout: row rho's 8 words as two
+//     16-byte halves, slot s holding canonical word s ^ ((rho & 31) >> 2) with bytes permuted by
+//     rho & 3); each lane takes the canonical byte g = lane / 16 of every word of its row,
+//   * v = alpha_c * x for the slice's 256 columns and up to 16 activation rows goes to LDS as
+//     fp16 hi and lo (each thread a row's 8 column pairs 32 i + 2 cg, so that the 16 threads
+//     of a row read consecutive columns),
+//   * per 32-column step t: A = the 16 rows' 8 sign bits of columns 32 t + 8 g .. + 7, expanded
+//     through a 256-entry table to 8 halves; B = v hi (then lo) of the same columns; two MFMAs.
+// The k order inside an operand only has to be the same for A and B (k is summed over): lane
+// group g holds columns 8 g .. 8 g + 7 of the step in both. At the end each lane holds
+// D[4 g + j][lane mod 16] of each 16-row block: row 4 g + j, activation row lane mod 16; it
+// scales by alpha_r of every base and adds into y (atomics when the columns are split over
+// several workgroups). Per slice the sums are scaled by alpha_r of the slice's base and added
+// to one running sum per (row, activation row); the next slice's loads are issued before this
+// slice's matrix work, so they arrive under it.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "ubw_internal.h"
+
+namespace ubw {
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMmThreads = 256;
+constexpr int kMmBatch = 16;     // activation rows per launch (the MFMA's N)
+constexpr int kMmSlots = 6;      // main + refinement bases per launch
+constexpr int kBStride = 132;    // dwords per activation row of a staged slice (128 + 4: no bank conflicts)
+
+struct MmSeg {
+    const uint32_t* packed;
+    const float* alpha_r;  // [nb][N]
+    const float* alpha_c;  // [nb][Kv]
+    const int32_t* idx;    // [Kv] or nullptr
+    int nb, Kv, KT;
+};
+
+struct MmParams {
+    MmSeg seg[2];
+    const void* x;
+    int64_t ldx;
+    float* y;
+    int N, NT, batch;
+    int ST;      // slices over both segments (seg[0].KT + seg[1].KT)
+    int KC;      // column chunks (grid y)
+    int atomic;  // 1: add into y with atomics, 0: store
+};
+
+__device__ __forceinline__ float x_at(const float* x, int64_t i) { return x[i]; }
+__device__ __forceinline__ float x_at(const __half* x, int64_t i) { return __half2float(x[i]); }
+
+// Raw buffer loads: an offset at or beyond the descriptor's size returns 0 and touches no
+// memory, so loads that are not wanted are issued with a size-0 descriptor instead of being
+// branched around (a branch would make the compiler wait for each load inside it).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* base = (void*)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint32_t ld32(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0); }
+__device__ __forceinline__ uint32_t ldx_raw(Rsrc r, uint32_t i, float*) { return ld32(r, 4u * i); }
+__device__ __forceinline__ uint32_t ldx_raw(Rsrc r, uint32_t i, __half*) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)(2u * i), 0, 0);
+}
+__device__ __forceinline__ float x_from_raw(uint32_t v, float*) { return __uint_as_float(v); }
+__device__ __forceinline__ float x_from_raw(uint32_t v, __half*) { return __half2float(__ushort_as_half((unsigned short)v)); }
+
+__device__ __forceinline__ uint32_t f16_bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
+
+template <typename XT>
+__global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
+    __shared__ __align__(16) uint32_t s_lut[256 * 4];                     // byte -> 8 halves of +-1
+    __shared__ __align__(16) uint32_t s_v[2][kMmBatch * kBStride];         // staged v: hi, lo
+    __shared__ int s_e[kMmBatch];                                          // staged row b holds v * 2^-e[b]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int rt = blockIdx.x;
+    const int s0 = (int)((int64_t)blockIdx.y * P.ST / P.KC);
+    const int s1 = (int)((int64_t)(blockIdx.y + 1) * P.ST / P.KC);
+    const XT* x = static_cast<const XT*>(P.x);
+
+    {  // expansion table: entry e, half i = +1 (0x3C00) if bit i of e is set, else -1 (0xBC00)
+        uint32_t d[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = (tid >> (2 * q)) & 1u ? 0x3C00u : 0xBC00u;
+            const uint32_t hi = (tid >> (2 * q + 1)) & 1u ? 0x3C00u : 0xBC00u;
+            d[q] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint4*>(&s_lut[4 * tid]) = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+
+    // Per 16-row block m of this wave: the lane's row is rho = 64 w + 16 m + r16, whose slots are
+    // permuted by a = ((rho & 31) >> 2) = 4 (m & 1) + (r16 >> 2) and bytes by c = r16 & 3.
+    const int bp = g ^ (r16 & 3);                    // physical byte holding canonical byte g
+    const int alo = r16 >> 2;                        // low two bits of a (the same for every m)
+    const uint32_t unperm = 0x03020100u ^ (0x01010101u * (uint32_t)alo);
+
+    // running sums of y for the lane's 16 (row, activation row) pairs: D[4 g + j][r16] of block m
+    float acc[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m][j] = 0.f;
+
+    const MmSeg S0 = P.seg[0], S1 = P.seg[1];
+    const int nb0 = S0.nb, nbt = S0.nb + S1.nb;
+    // staging role: activation row b, the 8 column pairs 32 i + 2 cg (+1), i < 8: at each step
+    // the 16 threads of a row read 32 consecutive columns (coalesced)
+    const int b = tid >> 4, cg = tid & 15;
+    const bool brow = b < P.batch;
+    const XT* xr = x + (int64_t)(brow ? b : 0) * P.ldx;
+#pragma unroll
+    for (int slot = 0; slot < kMmSlots; ++slot) {
+        if (slot >= nbt) break;
+        const int si = slot < nb0 ? 0 : 1;
+        const int k = si ? slot - nb0 : slot;
+        const MmSeg sg = si ? S1 : S0;
+        const int lo = si ? (s0 > S0.KT ? s0 - S0.KT : 0) : s0;
+        const int hi = si ? s1 - S0.KT : (s1 < S0.KT ? s1 : S0.KT);
+        if (lo >= hi) continue;
+        const int nitems = sg.KT * sg.nb;
+        const float* acr = sg.alpha_c + (int64_t)k * sg.Kv;
+        // alpha_r of this base at the lane's 16 rows
+        float ar[4][4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = rt * kTileRows + 64 * w + 16 * m + 4 * g + j;
+                ar[m][j] = sg.alpha_r[(int64_t)k * P.N + (row < P.N ? row : P.N - 1)];
+            }
+        // Loads of one slice: the wave's packed rows, alpha_c and (main segment) x or
+        // (refinement) idx of the staged columns. Every load is issued (clamped to a valid address,
+        // the value dropped later) before any is used.
+        uint4 p0[4], p1[4];
+        uint32_t xi[16], xw[16], aw[16];  // idx (refinement), raw x bits (main), alpha_c bits
+        const Rsrc r_ac = rsrc(acr, (uint32_t)sg.Kv * 4u);
+        const Rsrc r_idx = rsrc(S1.idx, si ? (uint32_t)sg.Kv * 4u : 0u);
+        // descriptors are uniform over the wave: x as a whole, the row in the offset
+        const Rsrc r_xd = rsrc(x, si ? 0u : (uint32_t)P.batch * (uint32_t)P.ldx * (uint32_t)sizeof(XT));
+        const uint32_t xrow = (uint32_t)(brow ? b : 0) * (uint32_t)P.ldx;
+        auto issue = [&](int ks) {
+            const uint4* tb =
+                reinterpret_cast<const uint4*>(sg.packed + ((int64_t)rt * nitems + (int64_t)ks * sg.nb + k) * kTileWords);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int rho = 64 * w + 16 * m + r16;
+                p0[m] = tb[rho];
+                p1[m] = tb[kTileRows + rho];
+            }
+            const int col0 = ks * kSliceCols + 2 * cg;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int col = col0 + 32 * (i >> 1) + (i & 1);
+                const uint32_t cc = (uint32_t)(col < sg.Kv ? col : sg.Kv - 1);
+                aw[i] = ld32(r_ac, 4u * cc);
+                xi[i] = ld32(r_idx, 4u * cc);
+                xw[i] = ldx_raw(r_xd, xrow + cc, (XT*)nullptr);
+            }
+        };
+        issue(lo);
+        for (int ks = lo; ks < hi; ++ks) {
+            // stage v = alpha_c * x of this slice, each activation row scaled by 2^-e
+            {
+                float xv[16];
+                if (si) {  // the gather through idx (the loads wait here, where they are used anyway)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {  // in range by contract
+                        const int c = xi[i] < (uint64_t)P.ldx ? (int)xi[i] : (int)P.ldx - 1;
+                        xv[i] = x_at(xr, c);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) xv[i] = x_from_raw(xw[i], (XT*)nullptr);
+                }
+                const int col0 = ks * kSliceCols + 2 * cg;
+                float v[16];
+                float mx = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int col = col0 + 32 * (i >> 1) + (i & 1);
+                    v[i] = brow && col < sg.Kv ? __uint_as_float(aw[i]) * xv[i] : 0.f;
+                    mx = fmaxf(mx, fabsf(v[i]));
+                }
+                // the 16 threads of row b are 16 consecutive lanes
+#pragma unroll
+                for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+                int eb = 0;
+                if (mx > 0.f) {
+                    int E;
+                    frexpf(mx, &E);  // mx in [2^(E-1), 2^E)
+                    eb = E - 15;
+                }
+                if (cg == 0) s_e[b] = eb;
+                uint32_t hv[8], lv[8];
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float v0 = ldexpf(v[i], -eb), v1 = ldexpf(v[i + 1], -eb);
+                    const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+                    const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
+                    hv[i / 2] = f16_bits(h0) | (f16_bits(h1) << 16);
+                    lv[i / 2] = f16_bits(l0) | (f16_bits(l1) << 16);
+                }
+                // the pair of columns 32 i + 2 cg (+1) is dword 16 i + cg of the row
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    s_v[0][b * kBStride + 16 * i + cg] = hv[i];
+                    s_v[1][b * kBStride + 16 * i + cg] = lv[i];
+                }
+            }
+            // canonical byte g of words 0..7 of each row, in word order: two dwords per block
+            uint32_t cb[4][2];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t W[8] = {p0[m].x, p0[m].y, p0[m].z, p0[m].w, p1[m].x, p1[m].y, p1[m].z, p1[m].w};
+                uint32_t E[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) E[q] = __builtin_amdgcn_ubfe(W[q], 8 * bp, 8);
+                // slot q holds word q ^ a: word t is in slot t ^ a; a's bit 2 is (m & 1)
+                const int sw = (m & 1) ? 4 : 0;
+                const uint32_t d0 = E[0 ^ sw] | (E[1 ^ sw] << 8) | (E[2 ^ sw] << 16) | (E[3 ^ sw] << 24);
+                const uint32_t d1 = E[4 ^ sw] | (E[5 ^ sw] << 8) | (E[6 ^ sw] << 16) | (E[7 ^ sw] << 24);
+                cb[m][0] = __builtin_amdgcn_perm(0u, d0, unperm);  // byte j = byte j ^ alo
+                cb[m][1] = __builtin_amdgcn_perm(0u, d1, unperm);
+            }
+            // the next slice's loads run under this slice's matrix work
+            if (ks + 1 < hi) issue(ks + 1);
+            __syncthreads();
+            float4_t c[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) c[m] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint4 bh = *reinterpret_cast<const uint4*>(&s_v[0][r16 * kBStride + 16 * t + 4 * g]);
+                const uint4 bl = *reinterpret_cast<const uint4*>(&s_v[1][r16 * kBStride + 16 * t + 4 * g]);
+                const half8_t Bh = __builtin_bit_cast(half8_t, bh);
+                const half8_t Bl = __builtin_bit_cast(half8_t, bl);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t e = (cb[m][t >> 2] >> (8 * (t & 3))) & 0xFFu;
+                    const half8_t A = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(&s_lut[4 * e]));
+                    c[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, c[m], 0, 0, 0);
+                    c[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, c[m], 0, 0, 0);
+                }
+            }
+            // D's column is activation row r16: undo that row's staging scale, apply alpha_r
+            const int ec = s_e[r16];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[m][j] += ar[m][j] * ldexpf(c[m][j], ec);
+            __syncthreads();  // s_v and s_e are restaged next
+        }
+    }
+
+    // y[b][row] (+)= the running sums
+    if (r16 >= P.batch) return;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = rt * kTileRows + 64 * w + 16 * m + 4 * g + j;
+            if (row >= P.N) continue;
+            float* dst = P.y + (int64_t)r16 * P.N + row;
+            if (P.atomic) atomicAdd(dst, acc[m][j]);
+            else *dst = acc[m][j];
+        }
+    }
+}
+
+}  // namespace
+
+bool mfma_step_supported(const StepArgs& a) {
+    if (a.gs || a.batch < 1 || a.batch > kMmBatch || !step_buffers_fit(a)) return false;
+    const int nbt = a.seg[0].nb + (a.nseg > 1 ? a.seg[1].nb : 0);
+    return nbt >= 1 && nbt <= kMmSlots;
+}
+
+hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s) {
+    if (!mfma_step_supported(a)) return hipErrorInvalidValue;
+    MmParams P{};
+    for (int i = 0; i < 2; ++i) {
+        if (i < a.nseg) {
+            const Segment& sg = a.seg[i];
+            P.seg[i] = MmSeg{sg.packed, static_cast<const float*>(sg.alpha_r), sg.alpha_c, sg.idx, sg.nb, sg.Kv,
+                             (int)ceil_div(sg.Kv, kSliceCols)};
+        } else {
+            P.seg[i] = MmSeg{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+        }
+    }
+    if (a.nseg > 1 && a.seg[1].idx == nullptr) return hipErrorInvalidValue;
+    P.x = a.x;
+    P.ldx = a.ldx;
+    P.y = a.y;
+    P.N = a.N;
+    P.NT = (int)ceil_div(a.N, kTileRows);
+    P.batch = a.batch;
+    P.ST = P.seg[0].KT + P.seg[1].KT;
+    if (P.ST < 1) return hipErrorInvalidValue;
+    // as many workgroups as the device holds at once (one round), split over whole slices
+    int cus = 0, dev = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, a.x_dtype == UBW_F16 ? (const void*)k_pm1_mfma<__half>
+                                                                                  : (const void*)k_pm1_mfma<float>,
+                                                     kMmThreads, 0) != hipSuccess)
+        return hipErrorInvalidConfiguration;
+    const int64_t cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    int64_t kc = cap / P.NT;
+    kc = kc < 1 ? 1 : (kc > P.ST ? P.ST : kc);
+    kc = kc > 65535 ? 65535 : kc;
+    P.KC = (int)kc;
+    P.atomic = (a.accumulate || P.KC > 1) ? 1 : 0;
+    if (!a.accumulate && P.KC > 1) {
+        hipError_t e = launch_fill_zero(a.y, (int64_t)a.batch * a.N, s);
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)P.NT, (unsigned)P.KC);
+    if (a.x_dtype == UBW_F16) hipLaunchKernelGGL(k_pm1_mfma<__half>, grid, dim3(kMmThreads), 0, s, P);
+    else hipLaunchKernelGGL(k_pm1_mfma<float>, grid, dim3(kMmThreads), 0, s, P);
+    return hipGetLastError();
+}
+
+}  // namespace ubw

@@ -62,6 +62,7 @@ struct StepArgs {
     uint32_t* ws;           // zero-initialised counters (single-launch y = result), or nullptr
     int rows_per_group;     // row tiles per unit: 1, 2 or 4 (<= max_rows_per_group(batch))
     int workgroups;         // persistent workgroups to launch, 0 = as many as fit at once
+    int tables_only;        // 1: the table kernels at every batch (explicit geometry)
 };
 
 // Workspace of the single-launch y = result mode: a 16-word header (word 0: error flag), then
@@ -79,9 +80,19 @@ hipError_t launch_ternary(const int8_t* w, const float* scale, int N, int K, uin
 hipError_t launch_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, int nb, int K,
                             int g, float* lut, hipStream_t s);
 hipError_t launch_extract(const uint32_t* packed, int nb, int N, int K, int g, uint16_t* out, hipStream_t s);
+// A step: batches of kMfmaMinBatch rows or more on the matrix cores (unless a.tables_only or
+// the step has group scales or more than six bases), smaller ones through the tables.
 hipError_t launch_step(const StepArgs& a, hipStream_t s);
 // Several steps sharing x (same x, batch, dtype, rows_per_group) in one launch.
 hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s);
+// Steps of several activation rows on the matrix cores (mfma.hip): up to 16 rows per launch,
+// at most six bases (main + refinement), per-row alpha_r only. Their cost hardly depends on the
+// rows while the tables' grows with every 4-row chunk; measured, the matrix cores win from three
+// chunks on (70B gate 28672 x 8192: 147 us for 16 rows vs 62 us per 4-row chunk; 7B up
+// 11008 x 4096: 28.7 us vs 16 us per chunk).
+constexpr int kMfmaMinBatch = 9;
+bool mfma_step_supported(const StepArgs& a);
+hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s);
 // Whether every buffer of a step is small enough for the kernel's 32-bit buffer offsets.
 bool step_buffers_fit(const StepArgs& a);
 
