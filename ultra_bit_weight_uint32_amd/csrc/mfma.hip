@@ -30,7 +30,8 @@
 // scales by alpha_r of every base and adds into y (atomics when the columns are split over
 // several workgroups). Per slice the sums are scaled by alpha_r of the slice's base and added
 // to one running sum per (row, activation row); the next slice's loads are issued before this
-// slice's matrix work, so they arrive under it.
+// slice's matrix work, so they arrive under it, and the staging area is double-buffered, so one
+// barrier per slice suffices and a wave done with a slice's matrix work stages the next.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -96,8 +97,10 @@ __device__ __forceinline__ uint32_t f16_bits(_Float16 h) { return (uint32_t)__bu
 template <typename XT>
 __global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
     __shared__ __align__(16) uint32_t s_lut[256 * 4];                     // byte -> 8 halves of +-1
-    __shared__ __align__(16) uint32_t s_v[2][kMmBatch * kBStride];         // staged v: hi, lo
-    __shared__ int s_e[kMmBatch];                                          // staged row b holds v * 2^-e[b]
+    // staged v (hi, lo) and row scales (row b holds v * 2^-e[b]), two buffers: a slice is staged
+    // into one while the other is still read by the previous slice's matrix work
+    __shared__ __align__(16) uint32_t s_v[2][2][kMmBatch * kBStride];
+    __shared__ int s_e[2][kMmBatch];
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
@@ -137,6 +140,7 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
     const int b = tid >> 4, cg = tid & 15;
     const bool brow = b < P.batch;
     const XT* xr = x + (int64_t)(brow ? b : 0) * P.ldx;
+    int buf = 0;
 #pragma unroll
     for (int slot = 0; slot < kMmSlots; ++slot) {
         if (slot >= nbt) break;
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
                     frexpf(mx, &E);  // mx in [2^(E-1), 2^E)
                     eb = E - 15;
                 }
-                if (cg == 0) s_e[b] = eb;
+                if (cg == 0) s_e[buf][b] = eb;
                 uint32_t hv[8], lv[8];
 #pragma unroll
                 for (int i = 0; i < 16; i += 2) {
@@ -232,8 +236,8 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
                 // the pair of columns 32 i + 2 cg (+1) is dword 16 i + cg of the row
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    s_v[0][b * kBStride + 16 * i + cg] = hv[i];
-                    s_v[1][b * kBStride + 16 * i + cg] = lv[i];
+                    s_v[buf][0][b * kBStride + 16 * i + cg] = hv[i];
+                    s_v[buf][1][b * kBStride + 16 * i + cg] = lv[i];
                 }
             }
             // canonical byte g of words 0..7 of each row, in word order: two dwords per block
@@ -259,8 +263,8 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
             for (int m = 0; m < 4; ++m) c[m] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const uint4 bh = *reinterpret_cast<const uint4*>(&s_v[0][r16 * kBStride + 16 * t + 4 * g]);
-                const uint4 bl = *reinterpret_cast<const uint4*>(&s_v[1][r16 * kBStride + 16 * t + 4 * g]);
+                const uint4 bh = *reinterpret_cast<const uint4*>(&s_v[buf][0][r16 * kBStride + 16 * t + 4 * g]);
+                const uint4 bl = *reinterpret_cast<const uint4*>(&s_v[buf][1][r16 * kBStride + 16 * t + 4 * g]);
                 const half8_t Bh = __builtin_bit_cast(half8_t, bh);
                 const half8_t Bl = __builtin_bit_cast(half8_t, bl);
 #pragma unroll
@@ -272,12 +276,14 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
                 }
             }
             // D's column is activation row r16: undo that row's staging scale, apply alpha_r
-            const int ec = s_e[r16];
+            const int ec = s_e[buf][r16];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[m][j] += ar[m][j] * ldexpf(c[m][j], ec);
-            __syncthreads();  // s_v and s_e are restaged next
+            // The next slice is staged into the other buffer: its last readers (the slice before
+            // this one) have all passed this slice's barrier.
+            buf ^= 1;
         }
     }
 
