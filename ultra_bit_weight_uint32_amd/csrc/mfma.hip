@@ -25,13 +25,13 @@
 //   * per 32-column step t: A = the 16 rows' 8 sign bits of columns 32 t + 8 g .. + 7, expanded
 //     through a 256-entry table to 8 halves; B = v hi (then lo) of the same columns; two MFMAs.
 // The k order inside an operand only has to be the same for A and B (k is summed over): lane
-// group g holds columns 8 g .. 8 g + 7 of the step in both. At the end each lane holds
-// D[4 g + j][lane mod 16] of each 16-row block: row 4 g + j, activation row lane mod 16; it
-// scales by alpha_r of every base and adds into y (atomics when the columns are split over
-// several workgroups). Per slice the sums are scaled by alpha_r of the slice's base and added
-// to one running sum per (row, activation row); the next slice's loads are issued before this
-// slice's matrix work, so they arrive under it, and the staging area is double-buffered, so one
-// barrier per slice suffices and a wave done with a slice's matrix work stages the next.
+// group g holds columns 8 g .. 8 g + 7 of the step in both. Each lane holds D[4 g + j][lane
+// mod 16] of each 16-row block (row 4 g + j, activation row lane mod 16); per slice it scales
+// that back by the row's power of two and by alpha_r of the slice's base into one running sum
+// per (row, activation row), which goes into y at the end (atomics when the columns are split
+// over several workgroups). The next slice's loads are issued before this slice's matrix work,
+// so they arrive under it, and the staging area is double-buffered, so one barrier per slice
+// suffices and a wave done with a slice's matrix work stages the next.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
