@@ -304,6 +304,22 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
 
 }  // namespace
 
+// Workgroups of the instance the device holds at once (CUs x occupancy), queried once per
+// process (benign race: every thread computes the same value).
+template <typename XT>
+static int64_t mm_capacity() {
+    static int64_t cap = -1;
+    if (cap < 0) {
+        int cus = 0, dev = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pm1_mfma<XT>, kMmThreads, 0) != hipSuccess)
+            return 0;
+        cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    }
+    return cap;
+}
+
 bool mfma_step_supported(const StepArgs& a) {
     if (a.gs || a.batch < 1 || a.batch > kMmBatch || !step_buffers_fit(a)) return false;
     const int nbt = a.seg[0].nb + (a.nseg > 1 ? a.seg[1].nb : 0);
@@ -332,13 +348,8 @@ hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s) {
     P.ST = P.seg[0].KT + P.seg[1].KT;
     if (P.ST < 1) return hipErrorInvalidValue;
     // as many workgroups as the device holds at once (one round), split over whole slices
-    int cus = 0, dev = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, a.x_dtype == UBW_F16 ? (const void*)k_pm1_mfma<__half>
-                                                                                  : (const void*)k_pm1_mfma<float>,
-                                                     kMmThreads, 0) != hipSuccess)
-        return hipErrorInvalidConfiguration;
-    const int64_t cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    const int64_t cap = a.x_dtype == UBW_F16 ? mm_capacity<__half>() : mm_capacity<float>();
+    if (cap <= 0) return hipErrorInvalidConfiguration;
     int64_t kc = cap / P.NT;
     kc = kc < 1 ? 1 : (kc > P.ST ? P.ST : kc);
     kc = kc > 65535 ? 65535 : kc;
