@@ -7,7 +7,7 @@
 // B^(k) V^(k) (V = the rows' v side by side) is a dense contraction whose cost does not grow with
 // the rows up to the matrix instruction's width. Here the sign bits are expanded to fp16 +-1
 // (exact) and multiplied on v_mfma_f32_16x16x32_f16 against V split into fp16 high and low
-// parts (v = hi + lo to about 2^-22 relative), accumulating in fp32: the result matches the
+// parts (v = hi + lo to 2^-20 relative), accumulating in fp32: the result matches the
 // table path's fp32 arithmetic up to summation order. Each activation row of a staged slice is
 // scaled by a power of two (exact) that puts its largest |v| in [2^14, 2^15), so no value
 // overflows fp16 and small ones keep their precision; the MFMA result of the slice is scaled
@@ -92,7 +92,6 @@ __device__ __forceinline__ uint32_t ldx_raw(Rsrc r, uint32_t i, __half*) {
 __device__ __forceinline__ float x_from_raw(uint32_t v, float*) { return __uint_as_float(v); }
 __device__ __forceinline__ float x_from_raw(uint32_t v, __half*) { return __half2float(__ushort_as_half((unsigned short)v)); }
 
-__device__ __forceinline__ uint32_t f16_bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
 
 template <typename XT>
 __global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
@@ -180,14 +179,16 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
                 p0[m] = tb[rho];
                 p1[m] = tb[kTileRows + rho];
             }
-            const int col0 = ks * kSliceCols + 2 * cg;
+            // per-lane base offsets and a constant per element (the load's immediate offset);
+            // columns past Kv read 0 from alpha_c and idx (out of the descriptors' range) and
+            // are dropped at staging
+            const uint32_t col0 = (uint32_t)(ks * kSliceCols + 2 * cg);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int col = col0 + 32 * (i >> 1) + (i & 1);
-                const uint32_t cc = (uint32_t)(col < sg.Kv ? col : sg.Kv - 1);
-                aw[i] = ld32(r_ac, 4u * cc);
-                xi[i] = ld32(r_idx, 4u * cc);
-                xw[i] = ldx_raw(r_xd, xrow + cc, (XT*)nullptr);
+                const uint32_t d = 32u * (uint32_t)(i >> 1) + (uint32_t)(i & 1);
+                aw[i] = ld32(r_ac, 4u * col0 + 4u * d);
+                xi[i] = ld32(r_idx, 4u * col0 + 4u * d);
+                xw[i] = ldx_raw(r_xd, xrow + col0 + d, (XT*)nullptr);
             }
         };
         issue(lo);
@@ -227,11 +228,13 @@ __global__ __launch_bounds__(kMmThreads, 2) void k_pm1_mfma(MmParams P) {
                 uint32_t hv[8], lv[8];
 #pragma unroll
                 for (int i = 0; i < 16; i += 2) {
+                    // hi = v rounded toward zero to fp16 (a pair per instruction), lo = the
+                    // remainder (exact in fp32) rounded the same way: |v - hi - lo| < 2^-20 |v|
                     const float v0 = ldexpf(v[i], -eb), v1 = ldexpf(v[i + 1], -eb);
-                    const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-                    const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
-                    hv[i / 2] = f16_bits(h0) | (f16_bits(h1) << 16);
-                    lv[i / 2] = f16_bits(l0) | (f16_bits(l1) << 16);
+                    const auto hp = __builtin_amdgcn_cvt_pkrtz(v0, v1);
+                    const auto lp = __builtin_amdgcn_cvt_pkrtz(v0 - (float)hp[0], v1 - (float)hp[1]);
+                    hv[i / 2] = __builtin_bit_cast(uint32_t, hp);
+                    lv[i / 2] = __builtin_bit_cast(uint32_t, lp);
                 }
                 // the pair of columns 32 i + 2 cg (+1) is dword 16 i + cg of the row
 #pragma unroll
