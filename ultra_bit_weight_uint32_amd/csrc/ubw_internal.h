@@ -88,8 +88,8 @@ hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s);
 // Steps of several activation rows on the matrix cores (mfma.hip): up to 16 rows per launch,
 // at most six bases (main + refinement), per-row alpha_r only. Their cost hardly depends on the
 // rows while the tables' grows with every 4-row chunk; measured, the matrix cores win from three
-// chunks on (70B gate 28672 x 8192: 147 us for 16 rows vs 62 us per 4-row chunk; 7B up
-// 11008 x 4096: 28.7 us vs 16 us per chunk).
+// chunks on and are about even at two (8 rows: 7B MLP 63.8 us vs 62.8 us on the tables, 70B gate
+// 112 us vs 125 us), so the tables keep up to 8 rows.
 constexpr int kMfmaMinBatch = 9;
 bool mfma_step_supported(const StepArgs& a);
 hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s);
