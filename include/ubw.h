@@ -334,8 +334,10 @@ int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, i
  * main bases of ubw_lut_gemv_gs (mode = 2: alpha_r is then its fp16 alpha_rg) with an
  * explicit launch geometry, always through the tables (at every batch). The kernel walks a list of units (a unit: rows_per_group tiles of
  * 256 rows x two (256-column slice, base) items) split into equal contiguous ranges over
- * `workgroups` persistent workgroups (0 = as many as the device holds at once; larger values
- * are capped to that). rows_per_group is 1, 2 or 4 for batch 1 and 1 or 2 above
+ * `workgroups` persistent workgroups (0 = the default: as many as the device holds at once, or
+ * one per CU at batch 1 when the units fit in two per CU; larger values are capped to the
+ * device's capacity). With a workspace and equal ranges, the launch may add one workgroup per
+ * row group that only zeroes y. rows_per_group is 1, 2 or 4 for batch 1 and 1 or 2 above
  * (UBW_ERANGE otherwise). Results equal the default geometry's up to fp32 summation
  * order. For modes 0 and 2, idx is ignored and Kv = K; for mode 1, Kv = s. workspace as
  * ubw_lut_gemv. A mode outside 0..2 is UBW_ERANGE.
