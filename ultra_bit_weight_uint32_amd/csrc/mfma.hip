@@ -31,9 +31,10 @@
 // per (row, activation row), which goes into y at the end (atomics when the columns are split
 // over several workgroups). The staging area is double-buffered, so one barrier per slice
 // suffices and a wave done with a slice's matrix work stages the next. Each slice's loads are
-// issued when it is staged: holding the next slice's operands in registers would leave room
-// for two waves per SIMD, and three waves (139 VGPRs) hide more of the LDS and memory latency
-// (70B gate at 16 rows: 131 -> 113 us).
+// issued when it is staged, and alpha_r of the slot's base sits in LDS: holding the next slice's
+// operands or the 16 scales in registers would leave room for two or three waves per SIMD, and
+// four (127 VGPRs, 40 KiB of LDS per workgroup) hide more of the LDS and memory latency (70B
+// gate at 16 rows: 131 us at two, 113 us at three, 107 us at four).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -51,6 +52,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kMmThreads = 256;
 constexpr int kMmBatch = 16;     // activation rows per launch (the MFMA's N)
 constexpr int kMmSlots = 6;      // main + refinement bases per launch
+constexpr int kMmMinSlices = 3;  // slices per workgroup before the columns are split further
 constexpr int kBStride = 132;    // dwords per activation row of a staged slice (128 + 4: no bank conflicts)
 
 struct MmSeg {
@@ -98,13 +100,14 @@ __device__ __forceinline__ float x_from_raw(uint32_t v, __half*) { return __half
 
 
 template <typename XT>
-// three waves per SIMD: see the header
-__global__ __launch_bounds__(kMmThreads, 3) void k_pm1_mfma(MmParams P) {
+// four waves per SIMD: see the header
+__global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(MmParams P) {
     __shared__ __align__(16) uint32_t s_lut[256 * 4];                     // byte -> 8 halves of +-1
     // staged v (hi, lo) and row scales (row b holds v * 2^-e[b]), two buffers: a slice is staged
     // into one while the other is still read by the previous slice's matrix work
     __shared__ __align__(16) uint32_t s_v[2][2][kMmBatch * kBStride];
     __shared__ int s_e[2][kMmBatch];
+    __shared__ float s_ar[2][kTileRows];  // alpha_r of the slot's base at the tile's rows
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_pm1_mfma(MmParams P) {
     // the 16 threads of a row read 32 consecutive columns (coalesced)
     const int b = tid >> 4, cg = tid & 15;
     const bool brow = b < P.batch;
-    int buf = 0;
+    int buf = 0, arb = 0;
 #pragma unroll
     for (int slot = 0; slot < kMmSlots; ++slot) {
         if (slot >= nbt) break;
@@ -155,15 +158,13 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_pm1_mfma(MmParams P) {
         if (lo >= hi) continue;
         const int nitems = sg.KT * sg.nb;
         const float* acr = sg.alpha_c + (int64_t)k * sg.Kv;
-        // alpha_r of this base at the lane's 16 rows
-        float ar[4][4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = rt * kTileRows + 64 * w + 16 * m + 4 * g + j;
-                ar[m][j] = sg.alpha_r[(int64_t)k * P.N + (row < P.N ? row : P.N - 1)];
-            }
+        // alpha_r of this base at the tile's 256 rows, in LDS (two buffers by the slot's parity: a
+        // slower wave may still read the previous slot's; every slot with slices passes barriers
+        // before its buffer is written again)
+        {
+            const int row = rt * kTileRows + tid;
+            s_ar[arb][tid] = sg.alpha_r[(int64_t)k * P.N + (row < P.N ? row : P.N - 1)];
+        }
         // Loads of one slice: the wave's packed rows, alpha_c and (main segment) x or
         // (refinement) idx of the staged columns. Every load is issued (clamped to a valid address,
         // the value dropped later) before any is used.
@@ -288,11 +289,12 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_pm1_mfma(MmParams P) {
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[m][j] += ar[m][j] * ldexpf(c[m][j], ec);
+                for (int j = 0; j < 4; ++j) acc[m][j] += s_ar[arb][64 * w + 16 * m + 4 * g + j] * ldexpf(c[m][j], ec);
             // The next slice is staged into the other buffer: its last readers (the slice before
             // this one) have all passed this slice's barrier.
             buf ^= 1;
         }
+        arb ^= 1;
     }
 
     // y[b][row] (+)= the running sums
@@ -312,20 +314,24 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_pm1_mfma(MmParams P) {
 
 }  // namespace
 
-// Workgroups of the instance the device holds at once (CUs x occupancy), queried once per
-// process (benign race: every thread computes the same value).
+// Workgroups of the instance the device holds at once (CUs x occupancy) and the CU count,
+// queried once per process (benign race: every thread computes the same values).
+struct MmCapacity {
+    int64_t cap, cus;
+};
 template <typename XT>
-static int64_t mm_capacity() {
-    static int64_t cap = -1;
-    if (cap < 0) {
+static MmCapacity mm_capacity() {
+    static MmCapacity c{-1, -1};
+    if (c.cap < 0) {
         int cus = 0, dev = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pm1_mfma<XT>, kMmThreads, 0) != hipSuccess)
-            return 0;
-        cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+            return MmCapacity{0, 0};
+        c.cus = cus;
+        c.cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     }
-    return cap;
+    return c;
 }
 
 bool mfma_step_supported(const StepArgs& a) {
@@ -355,10 +361,18 @@ hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s) {
     P.batch = a.batch;
     P.ST = P.seg[0].KT + P.seg[1].KT;
     if (P.ST < 1) return hipErrorInvalidValue;
-    // as many workgroups as the device holds at once (one round), split over whole slices
-    const int64_t cap = a.x_dtype == UBW_F16 ? mm_capacity<__half>() : mm_capacity<float>();
-    if (cap <= 0) return hipErrorInvalidConfiguration;
-    int64_t kc = cap / P.NT;
+    // At most as many workgroups as the device holds at once (one round), split over whole
+    // slices. Each workgroup of a split chunk adds 16 x 256 partial sums to y with atomics and
+    // loads its own tile setup, so a chunk takes at least kMmMinSlices slices unless that would
+    // leave CUs idle (8192 x 8192 at 16 rows: 76 us at about one slice per chunk, 59 us at two,
+    // 52 us at three).
+    const MmCapacity mc = a.x_dtype == UBW_F16 ? mm_capacity<__half>() : mm_capacity<float>();
+    if (mc.cap <= 0) return hipErrorInvalidConfiguration;
+    int64_t kc = mc.cap / P.NT;
+    const int64_t kc_fill = ceil_div(mc.cus, (int64_t)P.NT);
+    const int64_t kc_min_slices = ceil_div((int64_t)P.ST, (int64_t)kMmMinSlices);
+    const int64_t kc_want = kc_fill > kc_min_slices ? kc_fill : kc_min_slices;
+    kc = kc > kc_want ? kc_want : kc;
     kc = kc < 1 ? 1 : (kc > P.ST ? P.ST : kc);
     kc = kc > 65535 ? 65535 : kc;
     P.KC = (int)kc;
