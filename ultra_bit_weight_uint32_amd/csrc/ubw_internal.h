@@ -87,10 +87,12 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s);
 // Steps of several activation rows on the matrix cores (mfma.hip): up to 16 rows per launch,
 // at most six bases (main + refinement), per-row alpha_r only. Their cost hardly depends on the
-// rows while the tables' grows with every 4-row chunk; measured, the matrix cores win from three
-// chunks on and are about even at two (8 rows: 7B MLP 63.8 us vs 62.8 us on the tables, 70B gate
-// 112 us vs 125 us), so the tables keep up to 8 rows.
-constexpr int kMfmaMinBatch = 9;
+// rows while the tables' grows with every activation row. Measured with salient refinement:
+// at 5-6 rows the tables still win on 7B MLP shapes (11008 x 4096, 2 bases: 27-29 us vs 30 us)
+// while the matrix cores already win on 70B shapes (28672 x 8192, 3 bases: 92-103 us vs 87 us);
+// at 7 rows the 7B shapes are even (31 us) and the 70B gate takes 117 us on the tables vs
+// 89 us; at 8 rows the matrix cores win everywhere. So they take 7 rows and more.
+constexpr int kMfmaMinBatch = 7;
 bool mfma_step_supported(const StepArgs& a);
 hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s);
 // Whether every buffer of a step is small enough for the kernel's 32-bit buffer offsets.
