@@ -416,6 +416,19 @@ def sampled_rows(g, rows):
     return s
 
 
+def test_large_matrix_five_and_six_rows_sampled():
+    """5 and 6 rows on the 70B gate shape (3 bases of 28672 x 8192: the matrix cores) and on
+    8192 x 8192 with 3 bases (the tables), sampled rows against the oracle."""
+    rng = np.random.default_rng(56)
+    for name, n, k in (("gate", 28672, 8192), ("q", 8192, 8192)):
+        g = make_gemv(rng, name, n, k, 3, s=410, ns=2, batch=6)
+        rows = np.sort(rng.choice(n, size=256, replace=False))
+        for b in (5, 6):
+            gb = g.with_batch(b)
+            y = gpu_gemv(gb)[:, rows]
+            assert max_rel_err(y, oracle_gemv(sampled_rows(gb, rows))) <= TOL, (name, b)
+
+
 def test_decoder_layer_70b_sampled():
     wl = decoder_layer_70b()
     rng = np.random.default_rng(55)

@@ -1249,7 +1249,8 @@ static hipError_t launch_step_rows(const StepArgs& a, hipStream_t s) {
 }
 
 static bool use_mfma(const StepArgs& a) {
-    return !a.tables_only && a.batch >= kMfmaMinBatch && mfma_step_supported(a);
+    if (a.tables_only || a.batch < kMfmaMinBatchLarge || !mfma_step_supported(a)) return false;
+    return a.batch >= kMfmaMinBatch || (int64_t)a.seg[0].nb * a.N * a.seg[0].Kv >= kMfmaLargeWeights;
 }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t s) {
