@@ -242,7 +242,9 @@ typedef struct ubw_gemv_desc {
  * Several steps that read the same activations (e.g. the q, k, v projections, or gate and up)
  * in ONE launch: for each desc, what ubw_lut_gemv_refined (idx != NULL) or ubw_lut_gemv
  * (idx == NULL) computes. The device's workgroups are shared out in proportion to each GEMV's
- * work; each GEMV's outputs and workspace are its own. The GEMVs of a call must not write
+ * work (on the matrix cores, when every GEMV of the call goes there, one grid covers all their
+ * row tiles, each GEMV with its own column split); each GEMV's outputs and workspace are its
+ * own. The GEMVs of a call must not write
  * overlapping outputs. Section "2. Kernel innovation" (unified kernel execution) carried over
  * to GEMVs that share x.
  *   descs        HOST array of count descriptors, 1 <= count <= UBW_MAX_GROUP

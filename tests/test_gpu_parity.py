@@ -461,7 +461,7 @@ def shared_x(gs, x):
     return gs
 
 
-@pytest.mark.parametrize("batch", [1, 3, 16])
+@pytest.mark.parametrize("batch", [1, 3, 8, 16])
 def test_multi_integer_exact(batch):
     """Mixed GEMVs (row counts from 5 to 1100, 1 to 3 bases, with and without refinement) on one
     x: every output exact, written over NaN or added to, with and without workspaces."""
@@ -509,6 +509,31 @@ def test_multi_eight_gemvs_and_workspace_reuse():
             assert np.array_equal(gpu_gemv(g, packed=e["packed"], ws=e["workspace"]), oracle_gemv(g))
     for e in es:
         assert host(e["workspace"])[0] == 0
+
+
+def test_multi_eight_gemvs_matrix_cores():
+    """UBW_MAX_GROUP GEMVs at 12 rows: one matrix-core launch over all their row tiles (each GEMV
+    with its own column split), exact, over NaN and accumulated, twice in a row."""
+    rng = np.random.default_rng(19)
+    k = 1300
+    gs = [make_integer_gemv(rng, n, k, 1 + i % 3, s=(40 + 300 * (i % 4 == 1) if i % 2 else 0),
+                            ns=(1 + i % 2 if i % 2 else 0), batch=12)
+          for i, n in enumerate((64, 1, 513, 256, 257, 900, 33, 1300))]
+    shared_x(gs, rng.integers(-8, 9, size=(12, k)).astype(np.float16))
+    ref = [oracle_gemv(g) for g in gs]
+    x = dev(gs[0].x)
+    for ws in (True, False):
+        es = [multi_entry(g, ws=ws) for g in gs]
+        for rep in range(2):
+            outs = ubw.lut_gemv_multi(es, x, k)
+            for i, (o, r) in enumerate(zip(outs, ref)):
+                assert np.array_equal(host(o).astype(np.float64), r), (ws, rep, i)
+        y0 = [rng.integers(-50, 50, (12, g.n)).astype(np.float32) for g in gs]
+        for e, a in zip(es, y0):
+            e["y"] = dev(a)
+        outs = ubw.lut_gemv_multi(es, x, k, accumulate=True)
+        for i, (o, r, a) in enumerate(zip(outs, ref, y0)):
+            assert np.array_equal(host(o).astype(np.float64), r + a), (ws, i, "accumulate")
 
 
 def test_multi_single_gemv_matches_single_call():

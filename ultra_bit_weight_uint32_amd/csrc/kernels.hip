@@ -1285,19 +1285,13 @@ static hipError_t launch_step_group_rows(const StepArgs* a, int count, hipStream
     return dispatch_instance<float>(a[0].batch, a[0].rows_per_group, xl, go);
 }
 
-// Several GEMVs that share x, batch, dtype and rows_per_group, in one launch (on the matrix
-// cores: one launch per GEMV).
+// Several GEMVs that share x, batch, dtype and rows_per_group, in one launch (on the tables, or
+// on the matrix cores when every GEMV of the group goes there).
 hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s) {
     if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
     bool all_mfma = true;
     for (int i = 0; i < count; ++i) all_mfma = all_mfma && use_mfma(a[i]);
-    if (all_mfma) {
-        for (int i = 0; i < count; ++i) {
-            hipError_t e = launch_step_mfma(a[i], s);
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
-    }
+    if (all_mfma) return launch_step_mfma_group(a, count, s);
     if (a[0].batch <= kBatchChunk) return launch_step_group_rows(a, count, s);
     for (int r0 = 0; r0 < a[0].batch; r0 += kBatchChunk) {
         StepArgs c[kMaxGroup];

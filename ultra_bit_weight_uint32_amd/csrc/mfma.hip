@@ -14,6 +14,9 @@
 // back before it is added to the running sums. Main bases and the salient refinement (columns
 // gathered through idx) go through the same loop.
 //
+// GEMVs that share x run in one launch: grid x covers their row tiles one GEMV after the other
+// (so the small k and v projections fill the CUs next to q), grid y the column chunks, each GEMV
+// with its own count (its workgroups beyond it exit at once).
 // Workgroup (row tile rt, chunk kc): 256 threads, 4 waves, wave w owns tile rows 64 w .. +63 as
 // four 16-row blocks. For each base and each 256-column slice of the chunk:
 //   * the packed words of the wave's rows are loaded (the tile layout: row rho's 8 words as two
@@ -63,15 +66,24 @@ struct MmSeg {
     int nb, Kv, KT;
 };
 
+// One GEMV of a launch.
 struct MmParams {
     MmSeg seg[2];
+    float* y;
+    int N, NT;
+    int ST;      // slices over both segments (seg[0].KT + seg[1].KT)
+    int KC;      // column chunks (grid y at most this GEMV's KC; workgroups beyond it exit)
+    int atomic;  // 1: add into y with atomics, 0: store
+};
+
+// GEMVs sharing x in one launch: grid x covers their row tiles one GEMV after the other.
+struct MmGroup {
+    MmParams p[kMaxGroup];
+    int tile0[kMaxGroup + 1];  // first grid x of GEMV i; tile0[count] = grid x
+    int count;
+    int batch;
     const void* x;
     int64_t ldx;
-    float* y;
-    int N, NT, batch;
-    int ST;      // slices over both segments (seg[0].KT + seg[1].KT)
-    int KC;      // column chunks (grid y)
-    int atomic;  // 1: add into y with atomics, 0: store
 };
 
 
@@ -101,20 +113,26 @@ __device__ __forceinline__ float x_from_raw(uint32_t v, __half*) { return __half
 
 template <typename XT>
 // four waves per SIMD: see the header
-__global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(MmParams P) {
+__global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
     __shared__ __align__(16) uint32_t s_lut[256 * 4];                     // byte -> 8 halves of +-1
     // staged v (hi, lo) and row scales (row b holds v * 2^-e[b]), two buffers: a slice is staged
     // into one while the other is still read by the previous slice's matrix work
     __shared__ __align__(16) uint32_t s_v[2][2][kMmBatch * kBStride];
     __shared__ int s_e[2][kMmBatch];
     __shared__ float s_ar[2][kTileRows];  // alpha_r of the slot's base at the tile's rows
+    int gi = 0;  // this workgroup's GEMV (uniform)
+    while (gi + 1 < G.count && (int)blockIdx.x >= G.tile0[gi + 1]) ++gi;
+    const MmParams& P = G.p[gi];
+    if ((int)blockIdx.y >= P.KC) return;  // the whole workgroup: no barrier is left waiting
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    const int rt = blockIdx.x;
+    const int rt = (int)blockIdx.x - G.tile0[gi];
     const int s0 = (int)((int64_t)blockIdx.y * P.ST / P.KC);
     const int s1 = (int)((int64_t)(blockIdx.y + 1) * P.ST / P.KC);
-    const XT* x = static_cast<const XT*>(P.x);
+    const XT* x = static_cast<const XT*>(G.x);
+    const int batch = G.batch;
+    const int64_t ldx = G.ldx;
 
     {  // expansion table: entry e, half i = +1 (0x3C00) if bit i of e is set, else -1 (0xBC00)
         uint32_t d[4];
@@ -145,7 +163,7 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(MmParams P) {
     // staging role: activation row b, the 8 column pairs 32 i + 2 cg (+1), i < 8: at each step
     // the 16 threads of a row read 32 consecutive columns (coalesced)
     const int b = tid >> 4, cg = tid & 15;
-    const bool brow = b < P.batch;
+    const bool brow = b < batch;
     int buf = 0, arb = 0;
 #pragma unroll
     for (int slot = 0; slot < kMmSlots; ++slot) {
@@ -173,11 +191,11 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(MmParams P) {
         const Rsrc r_ac = rsrc(acr, (uint32_t)sg.Kv * 4u);
         // this row tile's slab of the segment (all slices and bases): below 2 GiB (checked)
         const Rsrc r_w = rsrc(sg.packed + (int64_t)rt * nitems * kTileWords, (uint32_t)nitems * kTileWords * 4u);
-        const Rsrc r_xg = rsrc(x, si ? (uint32_t)P.batch * (uint32_t)P.ldx * (uint32_t)sizeof(XT) : 0u);
+        const Rsrc r_xg = rsrc(x, si ? (uint32_t)batch * (uint32_t)ldx * (uint32_t)sizeof(XT) : 0u);
         const Rsrc r_idx = rsrc(S1.idx, si ? (uint32_t)sg.Kv * 4u : 0u);
         // descriptors are uniform over the wave: x as a whole, the row in the offset
-        const Rsrc r_xd = rsrc(x, si ? 0u : (uint32_t)P.batch * (uint32_t)P.ldx * (uint32_t)sizeof(XT));
-        const uint32_t xrow = (uint32_t)(brow ? b : 0) * (uint32_t)P.ldx;
+        const Rsrc r_xd = rsrc(x, si ? 0u : (uint32_t)batch * (uint32_t)ldx * (uint32_t)sizeof(XT));
+        const uint32_t xrow = (uint32_t)(brow ? b : 0) * (uint32_t)ldx;
         auto issue = [&](int ks) {
             // the item's 8 KiB within this row tile's slab (32-bit offsets)
             const uint32_t ib = ((uint32_t)ks * (uint32_t)sg.nb + (uint32_t)k) * (kTileWords * 4u);
@@ -207,7 +225,7 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(MmParams P) {
                 if (si) {  // the gather through idx (the loads wait here, where they are used anyway)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {  // in range by contract
-                        const int c = xi[i] < (uint64_t)P.ldx ? (int)xi[i] : (int)P.ldx - 1;
+                        const int c = xi[i] < (uint64_t)ldx ? (int)xi[i] : (int)ldx - 1;
                         xv[i] = x_from_raw(ldx_raw(r_xg, xrow + (uint32_t)c, (XT*)nullptr), (XT*)nullptr);
                     }
                 } else {
@@ -298,7 +316,7 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(MmParams P) {
     }
 
     // y[b][row] (+)= the running sums
-    if (r16 >= P.batch) return;
+    if (r16 >= batch) return;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -340,51 +358,71 @@ bool mfma_step_supported(const StepArgs& a) {
     return nbt >= 1 && nbt <= kMmSlots;
 }
 
-hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s) {
-    if (!mfma_step_supported(a)) return hipErrorInvalidValue;
-    MmParams P{};
-    for (int i = 0; i < 2; ++i) {
-        if (i < a.nseg) {
-            const Segment& sg = a.seg[i];
-            P.seg[i] = MmSeg{sg.packed, static_cast<const float*>(sg.alpha_r), sg.alpha_c, sg.idx, sg.nb, sg.Kv,
-                             (int)ceil_div(sg.Kv, kSliceCols)};
-        } else {
-            P.seg[i] = MmSeg{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+hipError_t launch_step_mfma_group(const StepArgs* a, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
+    MmGroup G{};
+    G.count = count;
+    G.batch = a[0].batch;
+    G.x = a[0].x;
+    G.ldx = a[0].ldx;
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        if (!mfma_step_supported(a[i]) || a[i].x != a[0].x || a[i].batch != a[0].batch ||
+            a[i].x_dtype != a[0].x_dtype || a[i].ldx != a[0].ldx)
+            return hipErrorInvalidValue;
+        if (a[i].nseg > 1 && a[i].seg[1].idx == nullptr) return hipErrorInvalidValue;
+        MmParams& P = G.p[i];
+        for (int j = 0; j < 2; ++j) {
+            if (j < a[i].nseg) {
+                const Segment& sg = a[i].seg[j];
+                P.seg[j] = MmSeg{sg.packed, static_cast<const float*>(sg.alpha_r), sg.alpha_c, sg.idx, sg.nb, sg.Kv,
+                                 (int)ceil_div(sg.Kv, kSliceCols)};
+            } else {
+                P.seg[j] = MmSeg{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+            }
         }
+        P.y = a[i].y;
+        P.N = a[i].N;
+        P.NT = (int)ceil_div(a[i].N, kTileRows);
+        P.ST = P.seg[0].KT + P.seg[1].KT;
+        if (P.ST < 1) return hipErrorInvalidValue;
+        G.tile0[i] = (int)tiles;
+        tiles += P.NT;
     }
-    if (a.nseg > 1 && a.seg[1].idx == nullptr) return hipErrorInvalidValue;
-    P.x = a.x;
-    P.ldx = a.ldx;
-    P.y = a.y;
-    P.N = a.N;
-    P.NT = (int)ceil_div(a.N, kTileRows);
-    P.batch = a.batch;
-    P.ST = P.seg[0].KT + P.seg[1].KT;
-    if (P.ST < 1) return hipErrorInvalidValue;
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+    G.tile0[count] = (int)tiles;
     // At most as many workgroups as the device holds at once (one round), split over whole
     // slices. Each workgroup of a split chunk adds 16 x 256 partial sums to y with atomics and
     // loads its own tile setup, so a chunk takes at least kMmMinSlices slices unless that would
     // leave CUs idle (8192 x 8192 at 16 rows: 76 us at about one slice per chunk, 59 us at two,
-    // 52 us at three).
-    const MmCapacity mc = a.x_dtype == UBW_F16 ? mm_capacity<__half>() : mm_capacity<float>();
+    // 52 us at three). The GEMVs of a group share the round: each gets the same number of
+    // workgroups per row tile (or fewer, when it has fewer slices).
+    const MmCapacity mc = a[0].x_dtype == UBW_F16 ? mm_capacity<__half>() : mm_capacity<float>();
     if (mc.cap <= 0) return hipErrorInvalidConfiguration;
-    int64_t kc = mc.cap / P.NT;
-    const int64_t kc_fill = ceil_div(mc.cus, (int64_t)P.NT);
-    const int64_t kc_min_slices = ceil_div((int64_t)P.ST, (int64_t)kMmMinSlices);
-    const int64_t kc_want = kc_fill > kc_min_slices ? kc_fill : kc_min_slices;
-    kc = kc > kc_want ? kc_want : kc;
-    kc = kc < 1 ? 1 : (kc > P.ST ? P.ST : kc);
-    kc = kc > 65535 ? 65535 : kc;
-    P.KC = (int)kc;
-    P.atomic = (a.accumulate || P.KC > 1) ? 1 : 0;
-    if (!a.accumulate && P.KC > 1) {
-        hipError_t e = launch_fill_zero(a.y, (int64_t)a.batch * a.N, s);
-        if (e != hipSuccess) return e;
+    int64_t kc_grid = 1;
+    for (int i = 0; i < count; ++i) {
+        MmParams& P = G.p[i];
+        int64_t kc = mc.cap / tiles;
+        const int64_t kc_fill = ceil_div(mc.cus, tiles);
+        const int64_t kc_min_slices = ceil_div((int64_t)P.ST, (int64_t)kMmMinSlices);
+        const int64_t kc_want = kc_fill > kc_min_slices ? kc_fill : kc_min_slices;
+        kc = kc > kc_want ? kc_want : kc;
+        kc = kc < 1 ? 1 : (kc > P.ST ? P.ST : kc);
+        kc = kc > 65535 ? 65535 : kc;
+        P.KC = (int)kc;
+        kc_grid = kc > kc_grid ? kc : kc_grid;
+        P.atomic = (a[i].accumulate || P.KC > 1) ? 1 : 0;
+        if (!a[i].accumulate && P.KC > 1) {
+            hipError_t e = launch_fill_zero(a[i].y, (int64_t)a[i].batch * a[i].N, s);
+            if (e != hipSuccess) return e;
+        }
     }
-    const dim3 grid((unsigned)P.NT, (unsigned)P.KC);
-    if (a.x_dtype == UBW_F16) hipLaunchKernelGGL(k_pm1_mfma<__half>, grid, dim3(kMmThreads), 0, s, P);
-    else hipLaunchKernelGGL(k_pm1_mfma<float>, grid, dim3(kMmThreads), 0, s, P);
+    const dim3 grid((unsigned)tiles, (unsigned)kc_grid);
+    if (a[0].x_dtype == UBW_F16) hipLaunchKernelGGL(k_pm1_mfma<__half>, grid, dim3(kMmThreads), 0, s, G);
+    else hipLaunchKernelGGL(k_pm1_mfma<float>, grid, dim3(kMmThreads), 0, s, G);
     return hipGetLastError();
 }
+
+hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s) { return launch_step_mfma_group(&a, 1, s); }
 
 }  // namespace ubw

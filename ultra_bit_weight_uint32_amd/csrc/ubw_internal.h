@@ -101,6 +101,8 @@ constexpr int kMfmaMinBatchLarge = 5;
 constexpr int64_t kMfmaLargeWeights = int64_t(1) << 28;
 bool mfma_step_supported(const StepArgs& a);
 hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s);
+// Several GEMVs sharing x (same x, batch, dtype, ldx) in one matrix-core launch.
+hipError_t launch_step_mfma_group(const StepArgs* a, int count, hipStream_t s);
 // Whether every buffer of a step is small enough for the kernel's 32-bit buffer offsets.
 bool step_buffers_fit(const StepArgs& a);
 
