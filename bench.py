@@ -74,7 +74,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU share of a "
+        print("bench.py measures one GPU: this library has no multi-GPU path (the per-GPU share of a "
               "sharded matrix is the same kernel at a smaller N). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
