@@ -330,6 +330,21 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
     }
 }
 
+// y = 0 for the GEMVs of a launch whose column chunks all add with atomics: one launch for all.
+struct MmZero {
+    float* y[kMaxGroup];
+    int64_t end[kMaxGroup];  // outputs to clear in buffers 0 .. i together
+    int count;
+};
+
+__global__ void k_mm_zero(const MmZero Z) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int j = 0;
+    while (j < Z.count && i >= Z.end[j]) ++j;
+    if (j == Z.count) return;
+    Z.y[j][i - (j ? Z.end[j - 1] : 0)] = 0.f;
+}
+
 }  // namespace
 
 // Workgroups of the instance the device holds at once (CUs x occupancy) and the CU count,
@@ -400,6 +415,7 @@ hipError_t launch_step_mfma_group(const StepArgs* a, int count, hipStream_t s) {
     const MmCapacity mc = a[0].x_dtype == UBW_F16 ? mm_capacity<__half>() : mm_capacity<float>();
     if (mc.cap <= 0) return hipErrorInvalidConfiguration;
     int64_t kc_grid = 1;
+    MmZero Z{};
     for (int i = 0; i < count; ++i) {
         MmParams& P = G.p[i];
         int64_t kc = mc.cap / tiles;
@@ -413,9 +429,17 @@ hipError_t launch_step_mfma_group(const StepArgs* a, int count, hipStream_t s) {
         kc_grid = kc > kc_grid ? kc : kc_grid;
         P.atomic = (a[i].accumulate || P.KC > 1) ? 1 : 0;
         if (!a[i].accumulate && P.KC > 1) {
-            hipError_t e = launch_fill_zero(a[i].y, (int64_t)a[i].batch * a[i].N, s);
-            if (e != hipSuccess) return e;
+            Z.y[Z.count] = a[i].y;
+            Z.end[Z.count] = (Z.count ? Z.end[Z.count - 1] : 0) + (int64_t)a[i].batch * a[i].N;
+            ++Z.count;
         }
+    }
+    if (Z.count > 0) {
+        const int64_t n = Z.end[Z.count - 1];
+        if (ceil_div(n, 256) > INT32_MAX) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_mm_zero, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, Z);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)tiles, (unsigned)kc_grid);
     if (a[0].x_dtype == UBW_F16) hipLaunchKernelGGL(k_pm1_mfma<__half>, grid, dim3(kMmThreads), 0, s, G);
