@@ -536,6 +536,22 @@ def test_multi_eight_gemvs_matrix_cores():
             assert np.array_equal(host(o).astype(np.float64), r + a), (ws, i, "accumulate")
 
 
+def test_multi_matrix_cores_mixed_column_splits():
+    """K = 200 at 9 rows: a GEMV without refinement has one slice (plain stores, its extra
+    workgroups exit), one with refinement two (zero fill, then atomics), in one launch."""
+    rng = np.random.default_rng(29)
+    k = 200
+    gs = [make_integer_gemv(rng, 300, k, 2, batch=9),
+          make_integer_gemv(rng, 700, k, 3, s=50, ns=2, batch=9),
+          make_integer_gemv(rng, 17, k, 1, batch=9)]
+    shared_x(gs, rng.integers(-8, 9, size=(9, k)).astype(np.float16))
+    ref = [oracle_gemv(g) for g in gs]
+    es = [multi_entry(g, ws=False) for g in gs]
+    outs = ubw.lut_gemv_multi(es, dev(gs[0].x), k)
+    for i, (o, r) in enumerate(zip(outs, ref)):
+        assert np.array_equal(host(o).astype(np.float64), r), i
+
+
 def test_multi_single_gemv_matches_single_call():
     rng = np.random.default_rng(23)
     g = make_integer_gemv(rng, 1000, 3000, 3, s=150, ns=2, batch=1)
