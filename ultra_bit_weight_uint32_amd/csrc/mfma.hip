@@ -26,7 +26,8 @@
 //     fp16 hi and lo (each thread a row's 8 column pairs 32 i + 2 cg, so that the 16 threads
 //     of a row read consecutive columns),
 //   * per 32-column step t: A = the 16 rows' 8 sign bits of columns 32 t + 8 g .. + 7, expanded
-//     through a 256-entry table to 8 halves; B = v hi (then lo) of the same columns; two MFMAs.
+//     through a 256-entry table to 8 halves; B = v hi (then lo) of the same columns; two MFMAs
+//     (at 8 activation rows or fewer, one: hi of row b is column b, lo column 8 + b).
 // The k order inside an operand only has to be the same for A and B (k is summed over): lane
 // group g holds columns 8 g .. 8 g + 7 of the step in both. Each lane holds D[4 g + j][lane
 // mod 16] of each 16-row block (row 4 g + j, activation row lane mod 16); per slice it scales
@@ -111,7 +112,9 @@ __device__ __forceinline__ float x_from_raw(uint32_t v, float*) { return __uint_
 __device__ __forceinline__ float x_from_raw(uint32_t v, __half*) { return __half2float(__ushort_as_half((unsigned short)v)); }
 
 
-template <typename XT>
+// kPack (at most 8 activation rows): v hi of row b is the MFMA's column b and v lo its column
+// 8 + b, so one MFMA per step instead of two; the two columns' sums are added at the end.
+template <typename XT, bool kPack>
 // four waves per SIMD: see the header
 __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
     __shared__ __align__(16) uint32_t s_lut[256 * 4];                     // byte -> 8 halves of +-1
@@ -263,10 +266,20 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
                     lv[i / 2] = __builtin_bit_cast(uint32_t, lp);
                 }
                 // the pair of columns 32 i + 2 cg (+1) is dword 16 i + cg of the row
+                if (kPack) {
+                    if (b < 8) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    s_v[buf][0][b * kBStride + 16 * i + cg] = hv[i];
-                    s_v[buf][1][b * kBStride + 16 * i + cg] = lv[i];
+                        for (int i = 0; i < 8; ++i) {
+                            s_v[buf][0][b * kBStride + 16 * i + cg] = hv[i];
+                            s_v[buf][0][(b + 8) * kBStride + 16 * i + cg] = lv[i];
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        s_v[buf][0][b * kBStride + 16 * i + cg] = hv[i];
+                        s_v[buf][1][b * kBStride + 16 * i + cg] = lv[i];
+                    }
                 }
             }
             // canonical byte g of words 0..7 of each row, in word order: two dwords per block
@@ -291,19 +304,23 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const uint4 bh = *reinterpret_cast<const uint4*>(&s_v[buf][0][r16 * kBStride + 16 * t + 4 * g]);
-                const uint4 bl = *reinterpret_cast<const uint4*>(&s_v[buf][1][r16 * kBStride + 16 * t + 4 * g]);
                 const half8_t Bh = __builtin_bit_cast(half8_t, bh);
-                const half8_t Bl = __builtin_bit_cast(half8_t, bl);
+                half8_t Bl;
+                if (!kPack) {
+                    const uint4 bl = *reinterpret_cast<const uint4*>(&s_v[buf][1][r16 * kBStride + 16 * t + 4 * g]);
+                    Bl = __builtin_bit_cast(half8_t, bl);
+                }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const uint32_t e = (cb[m][t >> 2] >> (8 * (t & 3))) & 0xFFu;
                     const half8_t A = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(&s_lut[4 * e]));
                     c[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, c[m], 0, 0, 0);
-                    c[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, c[m], 0, 0, 0);
+                    if (!kPack) c[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, c[m], 0, 0, 0);
                 }
             }
-            // D's column is activation row r16: undo that row's staging scale, apply alpha_r
-            const int ec = s_e[buf][r16];
+            // D's column is activation row r16 (kPack: r16 mod 8): undo that row's staging scale,
+            // apply alpha_r
+            const int ec = s_e[buf][kPack ? (r16 & 7) : r16];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -315,7 +332,13 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
         arb ^= 1;
     }
 
-    // y[b][row] (+)= the running sums
+    // y[b][row] (+)= the running sums (kPack: lane r16 < 8 adds the lo sums of lane r16 + 8)
+    if (kPack) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[m][j] += __shfl_xor(acc[m][j], 8);
+    }
     if (r16 >= batch) return;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -359,7 +382,7 @@ static MmCapacity mm_capacity() {
         int cus = 0, dev = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pm1_mfma<XT>, kMmThreads, 0) != hipSuccess)
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pm1_mfma<XT, false>, kMmThreads, 0) != hipSuccess)
             return MmCapacity{0, 0};
         c.cus = cus;
         c.cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
@@ -442,8 +465,14 @@ hipError_t launch_step_mfma_group(const StepArgs* a, int count, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)tiles, (unsigned)kc_grid);
-    if (a[0].x_dtype == UBW_F16) hipLaunchKernelGGL(k_pm1_mfma<__half>, grid, dim3(kMmThreads), 0, s, G);
-    else hipLaunchKernelGGL(k_pm1_mfma<float>, grid, dim3(kMmThreads), 0, s, G);
+    const bool pack = G.batch <= 8;
+    if (a[0].x_dtype == UBW_F16) {
+        if (pack) hipLaunchKernelGGL((k_pm1_mfma<__half, true>), grid, dim3(kMmThreads), 0, s, G);
+        else hipLaunchKernelGGL((k_pm1_mfma<__half, false>), grid, dim3(kMmThreads), 0, s, G);
+    } else {
+        if (pack) hipLaunchKernelGGL((k_pm1_mfma<float, true>), grid, dim3(kMmThreads), 0, s, G);
+        else hipLaunchKernelGGL((k_pm1_mfma<float, false>), grid, dim3(kMmThreads), 0, s, G);
+    }
     return hipGetLastError();
 }
 
