@@ -429,11 +429,11 @@ hipError_t launch_step_mfma_group(const StepArgs* a, int count, hipStream_t s) {
     }
     if (tiles > INT32_MAX) return hipErrorInvalidValue;
     G.tile0[count] = (int)tiles;
-    // At most as many workgroups as the device holds at once (one round), split over whole
+    // At most as many workgroups as the device holds at once, split over whole
     // slices. Each workgroup of a split chunk adds 16 x 256 partial sums to y with atomics and
     // loads its own tile setup, so a chunk takes at least kMmMinSlices slices unless that would
     // leave CUs idle (8192 x 8192 at 16 rows: 76 us at about one slice per chunk, 59 us at two,
-    // 52 us at three). The GEMVs of a group share the round: each gets the same number of
+    // 52 us at three). The GEMVs of a group share those workgroups: each gets the same number of
     // workgroups per row tile (or fewer, when it has fewer slices).
     const MmCapacity mc = a[0].x_dtype == UBW_F16 ? mm_capacity<__half>() : mm_capacity<float>();
     if (mc.cap <= 0) return hipErrorInvalidConfiguration;
