@@ -59,8 +59,8 @@ typedef enum {
 enum { UBW_F32 = 0, UBW_F16 = 1 };                       /* activation dtypes */
 enum { UBW_SRC_CANON_BITS = 0, UBW_SRC_INT8_SIGNS = 1 };  /* ubw_pack_bases sources */
 
-/* Largest batch one GEMV call accepts. Batches of 7 rows or more (5 or more when the main bases
- * hold at least 2^28 weights, nb * N * K) run in one launch on the
+/* Largest batch one GEMV call accepts. Batches of 7 rows or more (5 or more when
+ * batch * nb * N * K >= 2^30) run in one launch on the
  * matrix cores (the sign bits expanded to fp16 +-1, v = alpha_c * x split into fp16 high and
  * low parts, fp32 accumulation: the same result as the tables up to fp32 summation order) when
  * the call has per-row scales and at most six bases (main + refinement); otherwise batches

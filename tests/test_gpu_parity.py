@@ -418,7 +418,8 @@ def sampled_rows(g, rows):
 
 def test_large_matrix_five_and_six_rows_sampled():
     """5 and 6 rows on the 70B gate shape (3 bases of 28672 x 8192: the matrix cores) and on
-    8192 x 8192 with 3 bases (the tables), sampled rows against the oracle."""
+    8192 x 8192 with 3 bases (tables at 5 rows, matrix cores at 6), sampled rows against the
+    oracle."""
     rng = np.random.default_rng(56)
     for name, n, k in (("gate", 28672, 8192), ("q", 8192, 8192)):
         g = make_gemv(rng, name, n, k, 3, s=410, ns=2, batch=6)

@@ -1250,7 +1250,7 @@ static hipError_t launch_step_rows(const StepArgs& a, hipStream_t s) {
 
 static bool use_mfma(const StepArgs& a) {
     if (a.tables_only || a.batch < kMfmaMinBatchLarge || !mfma_step_supported(a)) return false;
-    return a.batch >= kMfmaMinBatch || (int64_t)a.seg[0].nb * a.N * a.seg[0].Kv >= kMfmaLargeWeights;
+    return a.batch >= kMfmaMinBatch || (int64_t)a.batch * a.seg[0].nb * a.N * a.seg[0].Kv >= kMfmaLargeWork;
 }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t s) {

@@ -80,7 +80,7 @@ hipError_t launch_ternary(const int8_t* w, const float* scale, int N, int K, uin
 hipError_t launch_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, int nb, int K,
                             int g, float* lut, hipStream_t s);
 hipError_t launch_extract(const uint32_t* packed, int nb, int N, int K, int g, uint16_t* out, hipStream_t s);
-// A step: batches of kMfmaMinBatch rows or more (kMfmaMinBatchLarge for large matrices) on the
+// A step: batches of kMfmaMinBatch rows or more (kMfmaMinBatchLarge for large work) on the
 // matrix cores (unless a.tables_only or
 // the step has group scales or more than six bases), smaller ones through the tables.
 hipError_t launch_step(const StepArgs& a, hipStream_t s);
@@ -93,12 +93,13 @@ hipError_t launch_step_group(const StepArgs* a, int count, hipStream_t s);
 // while the matrix cores already win on 70B shapes (28672 x 8192, 3 bases: 92-103 us vs 87 us);
 // at 7 rows the 7B shapes are even (31 us) and the 70B gate takes 117 us on the tables vs
 // 89 us; at 8 rows the matrix cores win everywhere. So they take 7 rows and more, and 5 or 6
-// rows when the main bases hold at least kMfmaLargeWeights weights (70B gate and down at 5/6
-// rows: 91/103 us on the tables vs 86/88 us; 8192 x 8192 with 3 bases is about even there).
+// rows when rows x main weights (batch nb N K) reach kMfmaLargeWork: 70B gate and down at 5/6
+// rows 91/103 us on the tables vs 86/88 us; 8192 x 8192 with 3 bases even at 5 rows (41 us),
+// 46 us vs 42 us at 6; the 7B shapes (2 bases) stay on the tables at 6 (27-29 us vs 30 us).
 // At 2-4 rows (one table launch) the tables win on every shape (70B gate: 40-65 us vs 83 us).
 constexpr int kMfmaMinBatch = 7;
 constexpr int kMfmaMinBatchLarge = 5;
-constexpr int64_t kMfmaLargeWeights = int64_t(1) << 28;
+constexpr int64_t kMfmaLargeWork = int64_t(1) << 30;
 bool mfma_step_supported(const StepArgs& a);
 hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s);
 // Several GEMVs sharing x (same x, batch, dtype, ldx) in one matrix-core launch.
