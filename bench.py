@@ -142,6 +142,27 @@ def main():
         step(copies[i % ncopy])
     torch.cuda.synchronize()
 
+    # Every timed launch reads a copy that no launch has touched for at least COLD_BYTES of other
+    # data: one position runs on through the copies across all legs, and a COLD_BYTES write
+    # evicts the caches before each leg.
+    evict = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device=dev)
+    pos = [0]
+
+    def leg(fn):
+        evict.zero_()
+        start = pos[0]
+
+        def launch(i):
+            fn(copies[(start + i) % ncopy])
+        return launch
+
+    def timed(fn, count, isolated=False):
+        """Per-launch us: K queued launches (pipelined) or the median of single launches."""
+        launch = leg(fn)
+        us = (run_isolated(torch, launch, count) if isolated else run_queued(torch, launch, count) * 1e3 / count)
+        pos[0] += count
+        return us
+
     if args.profile_run:
         src = torch.ones(16 << 20, dtype=torch.float32, device=dev)   # 64 MiB
         dst = torch.empty_like(src)
@@ -157,14 +178,40 @@ def main():
     # sleep so the GPU runs them back to back (host launch overhead would otherwise dominate).
     # A step is one launch of the step kernel, so the time per step is also that kernel's
     # average launch duration, dispatch gap between back-to-back launches included.
-    ms_total = run_queued(torch, lambda i: step(copies[i % ncopy]), args.steps)
-    ms_per_step = ms_total / args.steps
+    ms_per_step = timed(step, args.steps) * 1e-3
     # B. main bases only (ubw_lut_gemv, one launch per call), same protocol
-    main_us = run_queued(torch, lambda i: main_only(copies[i % ncopy]), args.steps) * 1e3 / args.steps
+    main_us = timed(main_only, args.steps)
     # C. size-matched streaming read of the same weight bytes (ceiling of one read that size)
-    read_us = run_queued(torch, lambda i: read_only(copies[i % ncopy]), args.steps) * 1e3 / args.steps
-    if int(ws[0].item()) != 0:
-        raise RuntimeError("workspace error word set: a workgroup gave up waiting")
+    read_us = timed(read_only, args.steps)
+    # D. the same three, one launch at a time: each launch alone on the GPU between two events
+    # (median), i.e. dispatch, the kernel and its end, with nothing of a neighbour overlapping
+    iso = min(args.steps, 100)
+    iso_step, iso_main, iso_read = (timed(f, iso, isolated=True) for f in (step, main_only, read_only))
+    st, word = ubw.workspace_check(ws)
+    if st != ubw.UBW_OK:
+        raise RuntimeError(f"workspace reports {ubw.status_str(st)} (word {word:#x})")
+    # E. a dependent chain: call i + 1 reads call i's output as its activations (fp32 x, which
+    # the kernel reads directly), so no call can start before the previous one has finished and
+    # its output is written: the per-token latency of a chain of such layers. The chain's copies
+    # get alpha_c / 8 so that values stay finite along it (same work, same bytes).
+    for c in copies:
+        c["ac"].mul_(0.125)
+        c["ac_s"].mul_(0.125)
+    ys = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _ in range(2)]
+    ys[1].copy_(copies[0]["x"].float())
+
+    def chained(i):
+        c = copies[(chain_start + i) % ncopy]
+        ubw.lut_gemv_refined(c["packed"], c["ar"], c["ac"], c["idx"], c["packed_s"], c["ar_s"], c["ac_s"],
+                             ys[(i + 1) % 2], n, k, y=ys[i % 2], workspace=ws)
+
+    evict.zero_()
+    chain_start = pos[0]
+    chain_us = run_queued(torch, chained, args.steps) * 1e3 / args.steps
+    pos[0] += args.steps
+    st, word = ubw.workspace_check(ws)
+    if st != ubw.UBW_OK or not torch.isfinite(ys[(args.steps - 1) % 2]).all():
+        raise RuntimeError(f"dependent chain: {ubw.status_str(st)} (word {word:#x}) or non-finite output")
 
     # sanity: the last outputs are finite (parity itself is the test suite's job)
     if not torch.isfinite(copies[(args.steps - 1) % ncopy]["y"]).all():
@@ -172,6 +219,7 @@ def main():
 
     step_bytes = algorithmic_bytes(n, k, nb, batch, 2, s, ns)
     main_bytes = algorithmic_bytes(n, k, nb, batch, 2)
+    chain_bytes = algorithmic_bytes(n, k, nb, batch, 4, s, ns)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     step_mean = ms_per_step * 1e3
     achieved = step_bytes / (step_mean * 1e-6) / 1e9
@@ -227,10 +275,44 @@ def main():
             "bytes": wbytes,
             "us_per_launch": round(read_us, 3),
             "GBps": round(wbytes / (read_us * 1e-6) / 1e9, 2),
+            "us_isolated": round(iso_read, 3),
+            "GBps_isolated": round(wbytes / (iso_read * 1e-6) / 1e9, 2),
+        },
+        "isolated": {
+            "what": "median of single launches, each alone on the GPU between two events (dispatch, kernel "
+                    "and its end; no neighbouring launch overlapping), cold",
+            "launches": iso,
+            "step_us": round(iso_step, 3),
+            "step_GBps": round(step_bytes / (iso_step * 1e-6) / 1e9, 2),
+            "main_only_us": round(iso_main, 3),
+            "read_us": round(iso_read, 3),
+        },
+        "dependent_chain": {
+            "what": "K steps where step i + 1 reads step i's fp32 output as x (each waits for the previous "
+                    "one's result), weights cold",
+            "us_per_step": round(chain_us, 3),
+            "bytes_per_step": chain_bytes,
+            "GBps": round(chain_bytes / (chain_us * 1e-6) / 1e9, 2),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def run_isolated(torch, launch, count):
+    """Median time of `count` single launches in us: each is queued behind a short GPU sleep
+    (so the host's launch overhead is not counted) between two events on the launch stream and
+    synchronized before the next."""
+    times = []
+    for i in range(count):
+        torch.cuda._sleep(2_000_000)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch(i)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    return float(np.median(times))
 
 
 def run_queued(torch, launch, count):
@@ -546,6 +628,18 @@ def saliency_sweep(torch, ubw, dev):
         torch.cuda.empty_cache()
 
 
+def host_cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or the platform's processor string."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(g, step_bytes, seconds):
     """The oracle as it stands (fp64 dequantize + naive matvec, OpenMP over rows) on the host
     cores, on whole calls of the step until about `seconds` have passed."""
@@ -564,6 +658,7 @@ def cpu_baseline(g, step_bytes, seconds):
         "value": round(step_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
+        "cpu_model": host_cpu_model(),
         "kind": "oracle",
         "sample": f"{reps} full calls of the same step (4096x4096, 2 bases + 205 salient columns, batch 1), "
                   f"{dt * 1e3:.1f} ms per call",

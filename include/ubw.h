@@ -28,7 +28,9 @@
  *   - Scalars: alpha_r [nb][N] and alpha_c [nb][K] fp32, row-major; y [batch][N] fp32.
  *   - Activations x [batch][K], fp16 (UBW_F16) or fp32 (UBW_F32), row-major.
  *   - Pointers are device pointers unless a comment says otherwise. The caller allocates
- *     and owns every buffer; the library allocates nothing and keeps no global state.
+ *     and owns every buffer; the library allocates nothing. Its only process-wide state is a
+ *     per-device cache of how many workgroups of each kernel a device holds at once (filled
+ *     on first use, thread-safe).
  *   - stream is a hipStream_t (NULL = the default stream). Every call only enqueues work on
  *     it and returns; results are ready when the stream is synchronized.
  *   - Return value: UBW_OK (0) or a negative ubw_status. Arguments are validated on the host
@@ -53,7 +55,8 @@ typedef enum {
     UBW_EALIGN = -3,        /* packed / x / workspace pointer not 16-byte aligned */
     UBW_ERANGE = -4,        /* a size or index out of its allowed range */
     UBW_EHIP = -5,          /* the HIP runtime rejected a launch */
-    UBW_ESIZE = -6          /* a caller buffer is smaller than required */
+    UBW_ESIZE = -6,         /* a caller buffer is smaller than required */
+    UBW_EWAIT = -7          /* (ubw_workspace_check) a workgroup gave up waiting and wrote nothing */
 } ubw_status;
 
 enum { UBW_F32 = 0, UBW_F16 = 1 };                       /* activation dtypes */
@@ -61,10 +64,12 @@ enum { UBW_SRC_CANON_BITS = 0, UBW_SRC_INT8_SIGNS = 1 };  /* ubw_pack_bases sour
 
 /* Largest batch one GEMV call accepts. Batches of 7 rows or more (5 or more when
  * batch * nb * N * K >= 2^30) run in one launch on the
- * matrix cores (the sign bits expanded to fp16 +-1, v = alpha_c * x split into fp16 high and
- * low parts, fp32 accumulation: the same result as the tables up to fp32 summation order) when
- * the call has per-row scales and at most six bases (main + refinement); otherwise batches
- * above 4 rows run through the tables as consecutive launches of 4 rows on the call's stream. */
+ * matrix cores when the call has per-row scales and at most six bases (main + refinement): the
+ * sign bits are expanded to fp16 +-1 and v = alpha_c * x is split into fp16 high and low parts
+ * (round toward zero each), so that per element |v - hi - lo| < 2^-20 |v| + 2^-38 m, m the
+ * largest |v| of that activation row within the 256-column slice, against the tables' fp32 v
+ * (2^-24 |v|); accumulation is fp32 in both. Otherwise batches above 4 rows run through the
+ * tables as consecutive launches of 4 rows on the call's stream. */
 #define UBW_MAX_BATCH 16
 /* columns per row scale in ubw_lut_gemv_gs */
 #define UBW_GROUP_COLS 128
@@ -128,19 +133,34 @@ int ubw_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, i
 
 /*
  * Workspace bytes the GEMV calls use for this shape (64 + 256 * ceil(N / 256)). *out is a
- * host pointer.
+ * host pointer. ubw_workspace_bytes is the same call under its earlier name.
  * A workspace lets a call that overwrites y (accumulate = 0) run as ONE launch: the kernel's
- * persistent workgroups (never more than the device holds at once) combine partial sums with
- * fp32 atomics; each workgroup zeroes the rows of the row groups it owns and, once the zeroing
- * has been performed, raises their flags in the workspace; a workgroup reads a row group's
- * flag before adding into it. Without a workspace (NULL, 0 bytes) the library zero-fills y with a separate
- * launch first. Rules: zero-fill the workspace once after allocating it (the kernels leave it
- * consistent after every call, whatever the shape); a workspace serves calls on one stream at a
- * time (calls that may run concurrently need separate workspaces); word 0 becomes nonzero only
- * if a wait gave up (an internal error that should never occur), after which the workspace
- * must be zero-filled again.
+ * persistent workgroups combine partial sums with fp32 atomics; per row group of 256 (or 512)
+ * rows, the first workgroup to announce its arrival in the workspace zeroes those rows (or
+ * writes its own sums there) and then raises the row group's flag, and every other workgroup
+ * adds into the rows only after it has seen the flag. The first arriver never waits for another
+ * workgroup before raising the flag, so every call completes whatever else runs on the device.
+ * Without a workspace (NULL, 0 bytes) the library zero-fills y with a separate launch first.
+ * Rules: zero-fill the workspace once after allocating it (the kernels leave it consistent
+ * after every call, whatever the shape); a workspace serves calls on one stream at a time
+ * (calls that may run concurrently need separate workspaces).
+ * Word 0 of the workspace collects errors found on the device (read it with
+ * ubw_workspace_check): bit 0 (UBW_EWAIT) a wait gave up and that workgroup added nothing
+ * (a safety net; the protocol above makes it unreachable), bit 1 (UBW_ERANGE) a salient index
+ * outside [0, K) or not above the index before it. Calls with a workspace set these bits and
+ * never clear them. Errors: UBW_EINVAL (null, sizes, batch), UBW_EUNSUPPORTED (g != 8).
  */
+int ubw_lut_gemv_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out);
 int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out);
+
+/*
+ * Reads (and with clear != 0 then zeroes) word 0 of a GEMV workspace: waits for `stream` to
+ * finish, so it is not for use inside graph capture. *out_word (host) gets the word.
+ * Returns UBW_OK (no error recorded), UBW_EWAIT (bit 0 set: some outputs were not written),
+ * UBW_ERANGE (bit 1 set, bit 0 clear: a salient index was out of range or out of order; the
+ * offending columns contributed nothing), or UBW_EINVAL / UBW_EALIGN / UBW_EHIP for the call.
+ */
+int ubw_workspace_check(void* workspace, int clear, void* stream, uint32_t* out_word);
 
 /*
  * Main GEMV: y (= or +=) sum_k alpha_r^(k) (.) (B^(k) (alpha_c^(k) (.) x)), for every
@@ -166,13 +186,14 @@ int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alph
  * dense virtual N x s matrix; its activations x[b][idx[q]] and scales alpha_c_s[k][q] are
  * gathered while the tables are built, and the same LUT-GEMV runs over it:
  * y[b][r] += sum_{k<ns} alpha_r_s[k][r] * sum_{q<s} B_s^(k)[r][q] * alpha_c_s[k][q] * x[b][idx[q]].
- *   idx          int32 [s], each in [0, K) (order free; ascending is the convention)
+ *   idx          int32 [s], strictly ascending, each in [0, K)
  *   packed_s     from ubw_pack_bases(ns, N, s, g=8) of the refinement bases [ns][N][s]
  *   alpha_r_s    fp32 [ns][N];  alpha_c_s fp32 [ns][s]
  *   K            columns of x (the activation row length)
- * Indices are not validated on the device (the page's VCM carries no metadata checks): an
- * index outside [0, K) is clamped to K - 1, so it never reads outside x but gives a wrong
- * result; ubw_check_indices validates them when the caller wants that.
+ * The kernels check idx on the device as they gather: a position q whose idx[q] lies outside
+ * [0, K), or is not above idx[q - 1], reads nothing and contributes nothing, and sets bit 1 of
+ * the workspace's word 0 (UBW_ERANGE from ubw_workspace_check). Without a workspace nothing
+ * records it; ubw_check_indices checks a host copy of idx.
  * Errors: as ubw_lut_gemv; s < 1 is UBW_EINVAL.
  */
 int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_s,
@@ -319,8 +340,9 @@ int ubw_hessian_saliency(float* H, int64_t K, float damp, const float* W, int64_
                          void* stream);
 
 /*
- * Host-side check of a salient index list: every idx[q] in [0, K) and strictly ascending.
- * idx is a HOST pointer. Returns UBW_OK or UBW_ERANGE (UBW_EINVAL for null / s < 1).
+ * Host-side check of a salient index list: every idx[q] in [0, K) and strictly ascending (the
+ * rule the kernels check on the device). idx is a HOST pointer. Returns UBW_OK or UBW_ERANGE
+ * (UBW_EINVAL for null / s < 1).
  */
 int ubw_check_indices(const int32_t* idx_host, int64_t s, int64_t K);
 
@@ -335,12 +357,13 @@ int ubw_extract_patterns(const uint32_t* packed, int nb, int64_t N, int64_t K, i
 /*
  * Test and tuning export: ubw_lut_gemv (mode = 0), ubw_vcm_gather_refine (mode = 1) or the
  * main bases of ubw_lut_gemv_gs (mode = 2: alpha_r is then its fp16 alpha_rg) with an
- * explicit launch geometry, always through the tables (at every batch). The kernel walks a list of units (a unit: rows_per_group tiles of
- * 256 rows x two (256-column slice, base) items) split into equal contiguous ranges over
- * `workgroups` persistent workgroups (0 = the default: as many as the device holds at once, or
- * one per CU at batch 1 when the units fit in two per CU; larger values are capped to the
- * device's capacity). With a workspace and equal ranges, the launch may add one workgroup per
- * row group that only zeroes y. rows_per_group is 1, 2 or 4 for batch 1 and 1 or 2 above
+ * explicit launch geometry, always through the tables (at every batch). The kernel walks a list
+ * of units (a unit: rows_per_group tiles of 256 rows x two (256-column slice, base) items) split
+ * into equal contiguous ranges over `workgroups` persistent workgroups (0 = the default: as many
+ * as the device holds at once, or one per CU at batch 1 when the units fit in two per CU; larger
+ * values are capped to the number of units only, so a launch may hold more workgroups than the
+ * device runs at once). With a workspace and equal ranges, the launch may add one workgroup per
+ * row group that takes part in the zeroing only. rows_per_group is 1, 2 or 4 for batch 1 and 1 or 2 above
  * (UBW_ERANGE otherwise). Results equal the default geometry's up to fp32 summation
  * order. For modes 0 and 2, idx is ignored and Kv = K; for mode 1, Kv = s. workspace as
  * ubw_lut_gemv. A mode outside 0..2 is UBW_ERANGE.

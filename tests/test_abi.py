@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert ubw.status_str(st).startswith("UBW_") or st == 0
     assert "unknown" in ubw.status_str(-99)
 
@@ -60,8 +60,20 @@ def test_workspace_bytes():
     assert ubw.workspace_bytes(2, 4096, 4096, 8, 1) == 4 * (16 + 64 * 16)
     assert ubw.workspace_bytes(1, 1, 1, 8, 1) == 4 * (16 + 64)
     sz = ctypes.c_size_t()
-    assert ubw.lib().ubw_workspace_bytes(2, 4096, 4096, 8, 17, ctypes.byref(sz)) == EINVAL
-    assert ubw.lib().ubw_workspace_bytes(2, 4096, 4096, 4, 1, ctypes.byref(sz)) == EUNSUP
+    L = ubw.lib()
+    for fn in (L.ubw_lut_gemv_workspace_bytes, L.ubw_workspace_bytes):
+        assert fn(2, 4096, 4096, 8, 1, ctypes.byref(sz)) == 0 and sz.value == 4 * (16 + 64 * 16)
+        assert fn(2, 4096, 4096, 8, 17, ctypes.byref(sz)) == EINVAL
+        assert fn(2, 4096, 4096, 4, 1, ctypes.byref(sz)) == EUNSUP
+        assert fn(2, 4096, 4096, 8, 1, None) == EINVAL
+
+
+def test_workspace_check_rejects():
+    word = ctypes.c_uint32()
+    L = ubw.lib()
+    assert L.ubw_workspace_check(None, 0, None, ctypes.byref(word)) == EINVAL
+    assert L.ubw_workspace_check(FAKE, 0, None, None) == EINVAL
+    assert L.ubw_workspace_check(MISALIGNED, 1, None, ctypes.byref(word)) == EALIGN
 
 
 def gemv_args(**kw):

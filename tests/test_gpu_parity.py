@@ -11,8 +11,8 @@ import pytest
 
 import oracle
 import ultra_bit_weight_uint32_amd as ubw
-from workloads import (single_gemv_256x512, ternary_stack_256x768, attn_proj_7b, mlp_7b, decoder_layer_70b, draw_bits, make_gemv, make_integer_gemv,
-                       words_per_row)
+from workloads import (Gemv, single_gemv_256x512, ternary_stack_256x768, attn_proj_7b, mlp_7b, decoder_layer_70b,
+                       draw_bits, make_gemv, make_integer_gemv, words_per_row)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -74,7 +74,8 @@ def gpu_gemv(g, packed=None, refine=True, y=None, accumulate=False, mode="fused_
             ubw.vcm_gather_refine(dev(g.idx), ps, dev(g.alpha_r_s), dev(g.alpha_c_s), x, g.n, g.k, y, workspace=ws)
     out = host(y).astype(np.float64)
     if ws is not None:
-        assert host(ws)[0] == 0, "a workgroup gave up waiting for its row group's flag"
+        word = int(host(ws)[0])
+        assert word == 0, f"workspace error word {word:#x} (bit 0: a wait gave up, bit 1: a salient index)"
     return out
 
 
@@ -305,19 +306,110 @@ def test_vcm_every_column_salient_doubles():
     assert np.array_equal(host(y), 2 * y1)
 
 
-def test_vcm_permutation_invariant():
-    rng = np.random.default_rng(23)
+def drop_positions(g, positions):
+    """The same problem with the refinement columns at `positions` contributing nothing (their
+    alpha_c_s set to 0; the index list itself is left alone)."""
+    h = Gemv(**{f: getattr(g, f) for f in g.__dataclass_fields__})
+    h.alpha_c_s = g.alpha_c_s.copy()
+    h.alpha_c_s[:, list(positions)] = 0.0
+    return h
+
+
+@pytest.mark.parametrize("batch", [1, 3, 9])
+def test_vcm_index_checks(batch):
+    """Salient indices are checked on the device: an index outside [0, K) or not above the one
+    before it is reported in workspace word 0 (UBW_ERANGE) and its column contributes nothing;
+    a valid list reports nothing. Batch 9 runs on the matrix cores, 1 and 3 on the tables."""
+    rng = np.random.default_rng(23 + batch)
     n, k, s = 260, 900, 90
-    g = make_integer_gemv(rng, n, k, 1, s=s, ns=2, batch=1)
-    base = gpu_gemv(g)
-    perm = rng.permutation(s)
-    by = g.bits_s.view(np.uint8).reshape(2, n, -1)
-    b01 = np.unpackbits(by, axis=2, bitorder="little")[:, :, :s][:, :, perm]
-    b01 = np.concatenate([b01, np.zeros((2, n, (-s) % 32), np.uint8)], axis=2)
-    g.bits_s = np.packbits(b01, axis=2, bitorder="little").view(np.uint32).reshape(2, n, -1)
-    g.idx = g.idx[perm].copy()
-    g.alpha_c_s = g.alpha_c_s[:, perm].copy()
-    assert np.array_equal(gpu_gemv(g), base)
+    g = make_integer_gemv(rng, n, k, 1, s=s, ns=2, batch=batch)
+    ok_ws = ubw.workspace(n, DEV)
+    want = oracle_gemv(g)
+    assert np.array_equal(gpu_gemv(g, ws=ok_ws), want)
+    assert ubw.workspace_check(ok_ws) == (ubw.UBW_OK, 0)
+    cases = [
+        ({0: -1}, [0]),                                 # below 0
+        ({s - 1: k}, [s - 1]),                          # at K
+        ({s - 1: 2**31 - 1}, [s - 1]),                  # far beyond K
+        ({40: int(g.idx[39])}, [40]),                   # repeats the one before
+        ({40: int(g.idx[39]) - 1 if g.idx[39] > 0 else 0, 41: int(g.idx[41])}, [40]),  # goes down
+    ]
+    for change, dropped in cases:
+        h = Gemv(**{f: getattr(g, f) for f in g.__dataclass_fields__})
+        h.idx = g.idx.copy()
+        for q, v in change.items():
+            h.idx[q] = v
+        if any(h.idx[q + 1] <= h.idx[q] for q in dropped if q + 1 < s):
+            continue  # the change also breaks its successor: covered by the other cases
+        for mode in ("fused_ws", "two_calls_ws"):
+            ws = ubw.workspace(n, DEV)
+            x = dev(h.x)
+            if mode == "fused_ws":
+                y = ubw.lut_gemv_refined(pack(h.bits, k), dev(h.alpha_r), dev(h.alpha_c), dev(h.idx), pack(h.bits_s, s),
+                                         dev(h.alpha_r_s), dev(h.alpha_c_s), x, n, k, workspace=ws)
+            else:
+                y = ubw.lut_gemv(pack(h.bits, k), dev(h.alpha_r), dev(h.alpha_c), x, n, k, workspace=ws)
+                ubw.vcm_gather_refine(dev(h.idx), pack(h.bits_s, s), dev(h.alpha_r_s), dev(h.alpha_c_s), x, n, k, y,
+                                      workspace=ws)
+            st, word = ubw.workspace_check(ws, clear=True)
+            assert st == ubw.UBW_ERANGE and word == 2, (change, mode, st, word)
+            assert ubw.workspace_check(ws) == (ubw.UBW_OK, 0)
+            assert np.array_equal(host(y).astype(np.float64), oracle_gemv(drop_positions(g, dropped))), (change, mode)
+
+
+def test_progress_beyond_device_capacity():
+    """y = result with more workgroups than the device holds at once (1024 single-unit
+    workgroups for 16 row groups): a workgroup only ever waits for the first arriver of its row
+    group, which is already running, so the launch completes and every result is exact."""
+    rng = np.random.default_rng(24)
+    n, k = 4096, 16384
+    g = make_integer_gemv(rng, n, k, 2, batch=1)
+    packed = pack(g.bits, k)
+    ws = ubw.workspace(n, DEV)
+    want = oracle_gemv(g)
+    for wgs in (100000, 700, 513):
+        y = torch.full((1, n), float("nan"), device=DEV)
+        ubw.lut_gemv_geometry(packed, dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y, rows_per_group=1,
+                              workgroups=wgs, workspace=ws)
+        assert np.array_equal(host(y).astype(np.float64), want), wgs
+        assert ubw.workspace_check(ws) == (ubw.UBW_OK, 0), wgs
+
+
+def test_concurrent_streams_separate_workspaces():
+    """Two streams, each with its own workspace, issue full-device y = result launches at the same
+    time: the 4096 x 4096 step (2 bases + 205 salient columns) and a 70B gate (28672 x 8192,
+    3 bases + 1434 salient columns); integer-valued inputs, so every output of every launch must
+    equal the oracle exactly."""
+    rng = np.random.default_rng(25)
+    gs = [make_integer_gemv(rng, 4096, 4096, 2, s=205, ns=2, batch=1),
+          make_integer_gemv(rng, 28672, 8192, 3, s=1434, ns=2, batch=1)]
+    wants = [oracle_gemv(g) for g in gs]
+    args = []
+    for g in gs:
+        args.append(dict(packed=pack(g.bits, g.k), ar=dev(g.alpha_r), ac=dev(g.alpha_c), idx=dev(g.idx),
+                         ps=pack(g.bits_s, g.s), ars=dev(g.alpha_r_s), acs=dev(g.alpha_c_s), x=dev(g.x),
+                         ws=ubw.workspace(g.n, DEV)))
+    reps = 60
+    outs = [[torch.full((1, g.n), float("nan"), device=DEV) for _ in range(reps)] for g in gs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(20_000_000)  # both streams start together once this ends
+    gate = torch.cuda.Event()
+    gate.record()
+    for st in streams:
+        st.wait_event(gate)
+    for r in range(reps):
+        for i, (g, a) in enumerate(zip(gs, args)):
+            with torch.cuda.stream(streams[i]):
+                ubw.lut_gemv_refined(a["packed"], a["ar"], a["ac"], a["idx"], a["ps"], a["ars"], a["acs"], a["x"],
+                                     g.n, g.k, y=outs[i][r], workspace=a["ws"])
+    torch.cuda.synchronize()
+    for i, g in enumerate(gs):
+        with torch.cuda.stream(streams[i]):
+            assert ubw.workspace_check(args[i]["ws"]) == (ubw.UBW_OK, 0), g.n
+        got = torch.cat(outs[i]).cpu().numpy().astype(np.float64)
+        bad = np.flatnonzero(np.any(got != wants[i], axis=1))
+        assert bad.size == 0, f"{g.n} x {g.k}: launches {bad[:10].tolist()} differ from the oracle"
 
 
 @pytest.mark.parametrize("batch", [1, 3])
@@ -907,3 +999,84 @@ def test_matrix_core_and_tables_agree_and_seven_bases_fall_back():
         ubw.lut_gemv_geometry(pack(g.bits_s, g.s), dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), n, g.s, y,
                               idx=dev(g.idx), k=k, accumulate=True, rows_per_group=1)
         assert np.array_equal(host(y).astype(np.float64), ref), (nb, ns)
+
+
+def split_bound(g, x):
+    """Per output, sum over bases of |alpha_r| (2^-20 sum_j |v_j| + K 2^-38 max_j |v_j|), v the
+    fp32 product alpha_c * x of each activation row: the most the matrix cores' fp16 hi + lo
+    representation of v can move a result away from the tables' (include/ubw.h, UBW_MAX_BATCH)."""
+    xb = x.astype(np.float32)
+    out = np.zeros((x.shape[0], g.n))
+    for kk in range(g.nb):
+        v = np.abs((g.alpha_c[kk][None, :] * xb).astype(np.float64))
+        per_row = 2.0 ** -20 * v.sum(axis=1) + g.k * 2.0 ** -38 * v.max(axis=1)
+        out += per_row[:, None] * np.abs(g.alpha_r[kk].astype(np.float64))[None, :]
+    return out
+
+
+def tables_reference(g, x):
+    """The same GEMV through the tables at any batch (the geometry export), main bases only."""
+    y = torch.zeros((x.shape[0], g.n), device=DEV)
+    ubw.lut_gemv_geometry(pack(g.bits, g.k), dev(g.alpha_r), dev(g.alpha_c), dev(x), g.n, g.k, y, rows_per_group=1)
+    return host(y).astype(np.float64)
+
+
+def test_matrix_core_split_bound_one_hot():
+    """16 rows on the matrix cores against the tables, each activation row one-hot at its own
+    column with a full-precision alpha_c: every output is then alpha_r * (+-v) of one column, exact
+    on the tables (fp32 v), so the difference is the hi/lo split's own error, which must stay
+    within |alpha_r| (2^-20 |v| + 2^-38 |v|) per base plus the fp32 rounding of the products."""
+    rng = np.random.default_rng(26)
+    n, k, nb = 512, 1024, 2
+    g = make_gemv(rng, "onehot", n, k, nb, batch=16)
+    cols = rng.choice(k, 16, replace=False)
+    x = np.zeros((16, k), np.float16)
+    x[np.arange(16), cols] = (rng.uniform(0.5, 4.0, 16) * rng.choice([-1, 1], 16)).astype(np.float16)
+    g.x = x
+    y_mm = host(ubw.lut_gemv(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(x), n, k)).astype(np.float64)
+    y_tab = tables_reference(g, x)
+    prod = sum(np.abs(g.alpha_r[kk].astype(np.float64))[None, :] *
+               np.abs((g.alpha_c[kk] * x.astype(np.float32)).astype(np.float64)).max(axis=1)[:, None]
+               for kk in range(nb))
+    bound = (2.0 ** -20 + 2.0 ** -38) * prod + 4 * 2.0 ** -24 * prod
+    diff = np.abs(y_mm - y_tab)
+    assert np.all(diff <= bound), float(np.max(diff / bound))
+    assert max_rel_err(y_mm, oracle_gemv(g)) <= TOL
+
+
+@pytest.mark.parametrize("n,k,nb", [(11008, 4096, 2), (4096, 11008, 2)])
+def test_matrix_core_vs_tables_16_rows(n, k, nb):
+    """7B MLP shapes at 16 rows, every output: the matrix-core result stays within the split
+    bound of the tables' result (the two paths' fp32 summation orders differ by far less on these
+    inputs) and within the 1e-3 bar of the oracle."""
+    rng = np.random.default_rng(27 + n)
+    g = make_gemv(rng, "mlp16", n, k, nb, batch=16)
+    y_mm = host(ubw.lut_gemv(pack(g.bits, k), dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k)).astype(np.float64)
+    y_tab = tables_reference(g, g.x)
+    assert np.all(np.abs(y_mm - y_tab) <= split_bound(g, g.x))
+    assert max_rel_err(y_mm, oracle_gemv(g)) <= TOL
+
+
+@pytest.mark.parametrize("n,k,batch", [(9 * 256 + 37, 1500, 1), (23 * 256, 777, 1), (10 * 256, 2048, 3),
+                                       (17 * 256 - 5, 600, 4)])
+def test_xcd_local_row_groups_integer_exact(n, k, batch):
+    """y = result with 8 or more row groups runs with each row group on one XCD (its zeroing done
+    by the workgroup holding its first unit): every split over 8 .. 100000 workgroups, ragged row
+    groups per XCD, the refinement alone and main + refinement, NaN garbage overwritten, exact."""
+    rng = np.random.default_rng(n + k + batch)
+    g = make_integer_gemv(rng, n, k, 2, s=max(1, k // 20), ns=2, batch=batch)
+    packed, ps = pack(g.bits, k), pack(g.bits_s, g.s)
+    ws = ubw.workspace(n, DEV)
+    main, full = oracle_gemv(g, refine=False), oracle_gemv(g)
+    for wgs in (8, 9, 15, 64, 0, 100000):
+        y = torch.full((batch, n), float("nan"), device=DEV)
+        ubw.lut_gemv_geometry(packed, dev(g.alpha_r), dev(g.alpha_c), dev(g.x), n, k, y, rows_per_group=1,
+                              workgroups=wgs, workspace=ws)
+        assert np.array_equal(host(y).astype(np.float64), main), ("main", wgs)
+        y = torch.full((batch, n), float("nan"), device=DEV)
+        ubw.lut_gemv_geometry(ps, dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), n, g.s, y, idx=dev(g.idx), k=k,
+                              rows_per_group=1, workgroups=wgs, workspace=ws)
+        assert np.array_equal(host(y).astype(np.float64), full - main), ("refinement", wgs)
+        assert ubw.workspace_check(ws) == (ubw.UBW_OK, 0), wgs
+    y = torch.full((batch, n), float("nan"), device=DEV)
+    assert np.array_equal(gpu_gemv(g, y=y, ws=ws), full)

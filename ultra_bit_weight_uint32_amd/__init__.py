@@ -18,6 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBPATH = os.path.join(_HERE, "libubw.so")
 
 UBW_OK = 0
+UBW_ERANGE = -4
+UBW_EWAIT = -7
 UBW_F32, UBW_F16 = 0, 1
 UBW_SRC_CANON_BITS, UBW_SRC_INT8_SIGNS = 0, 1
 MAX_BATCH = 16
@@ -26,7 +28,8 @@ MAX_GROUP = 8
 # every symbol include/ubw.h declares
 EXPORTS = (
     "ubw_status_str", "ubw_version", "ubw_packed_words", "ubw_pack_bases", "ubw_ternary_encode",
-    "ubw_build_lut", "ubw_workspace_bytes", "ubw_lut_gemv", "ubw_vcm_gather_refine", "ubw_lut_gemv_refined",
+    "ubw_build_lut", "ubw_lut_gemv_workspace_bytes", "ubw_workspace_bytes", "ubw_workspace_check",
+    "ubw_lut_gemv", "ubw_vcm_gather_refine", "ubw_lut_gemv_refined",
     "ubw_check_indices", "ubw_extract_patterns", "ubw_lut_gemv_geometry", "ubw_bench_stream_read",
     "ubw_lut_gemv_multi", "ubw_lut_gemv_gs", "ubw_fit_workspace_bytes", "ubw_fit_bases",
     "ubw_gram", "ubw_saliency_workspace_bytes", "ubw_hessian_saliency",
@@ -68,7 +71,9 @@ def lib():
         "ubw_pack_bases": ([P, I, I, I64, I64, I, P, P], I),
         "ubw_ternary_encode": ([P, P, I64, I64, I, P, P, P, P], I),
         "ubw_build_lut": ([P, I, I, P, I, I64, I, P, P], I),
+        "ubw_lut_gemv_workspace_bytes": ([I, I64, I64, I, I, ctypes.POINTER(SZ)], I),
         "ubw_workspace_bytes": ([I, I64, I64, I, I, ctypes.POINTER(SZ)], I),
+        "ubw_workspace_check": ([P, I, P, ctypes.POINTER(ctypes.c_uint32)], I),
         "ubw_lut_gemv": ([P, P, P, I, I64, I64, I, P, I, I, P, I, P, SZ, P], I),
         "ubw_vcm_gather_refine": ([P, I64, P, P, P, I, I64, I64, I, P, I, I, P, P, SZ, P], I),
         "ubw_check_indices": ([P, I64, I64], I),
@@ -154,10 +159,26 @@ def packed_words(nb: int, n: int, k: int, g: int = 8) -> int:
     return out.value
 
 
-def workspace_bytes(nb: int, n: int, k: int, g: int = 8, batch: int = 1) -> int:
+def lut_gemv_workspace_bytes(nb: int, n: int, k: int, g: int = 8, batch: int = 1) -> int:
     out = ctypes.c_size_t(0)
-    _check("ubw_workspace_bytes", lib().ubw_workspace_bytes(nb, n, k, g, batch, ctypes.byref(out)))
+    _check("ubw_lut_gemv_workspace_bytes", lib().ubw_lut_gemv_workspace_bytes(nb, n, k, g, batch, ctypes.byref(out)))
     return out.value
+
+
+workspace_bytes = lut_gemv_workspace_bytes
+
+
+def workspace_check(workspace, clear: bool = False):
+    """Word 0 of a GEMV workspace after the current stream's work has finished: returns
+    (status, word), status being UBW_OK, UBW_EWAIT (bit 0: a wait gave up, outputs not written)
+    or UBW_ERANGE (bit 1: a salient index out of range or out of order). clear=True zeroes the
+    word afterwards."""
+    word = ctypes.c_uint32(0)
+    st = lib().ubw_workspace_check(_dev(workspace, "workspace", None), 1 if clear else 0, _stream(),
+                                   ctypes.byref(word))
+    if st not in (UBW_OK, UBW_EWAIT, UBW_ERANGE):
+        raise UbwError("ubw_workspace_check", st)
+    return st, word.value
 
 
 def workspace(n: int, device="cuda"):

@@ -11,7 +11,7 @@ using namespace ubw;
 
 namespace {
 
-constexpr int kVersion = 6;
+constexpr int kVersion = 7;
 constexpr int kMaxFitIters = 10000;
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -106,6 +106,7 @@ const char* ubw_status_str(int status) {
         case UBW_ERANGE: return "UBW_ERANGE: index out of range or not ascending";
         case UBW_EHIP: return "UBW_EHIP: HIP runtime error";
         case UBW_ESIZE: return "UBW_ESIZE: buffer too small";
+        case UBW_EWAIT: return "UBW_EWAIT: a workgroup gave up waiting for a row group's zeroing (outputs not written)";
         default: return "unknown ubw status";
     }
 }
@@ -147,10 +148,34 @@ int ubw_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, i
     return hip_status(launch_build_lut(x, x_dtype, batch, alpha_c, nb, (int)K, g, lut, as_stream(stream)));
 }
 
-int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out) {
+int ubw_lut_gemv_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out) {
     if (!out || nb < 1 || !fits_int(N) || !fits_int(K) || batch < 1 || batch > UBW_MAX_BATCH) return UBW_EINVAL;
     if (g != 8) return UBW_EUNSUPPORTED;
     *out = (size_t)step_workspace_words(N) * 4;
+    return UBW_OK;
+}
+
+int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out) {
+    return ubw_lut_gemv_workspace_bytes(nb, N, K, g, batch, out);
+}
+
+int ubw_workspace_check(void* workspace, int clear, void* stream, uint32_t* out_word) {
+    if (!workspace || !out_word) return UBW_EINVAL;
+    if (!aligned16(workspace)) return UBW_EALIGN;
+    hipStream_t st = as_stream(stream);
+    uint32_t word = 0;
+    if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return UBW_EHIP;
+    *out_word = word;
+    if (clear && word != 0) {
+        const uint32_t zero = 0;
+        if (hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, st) != hipSuccess ||
+            hipStreamSynchronize(st) != hipSuccess)
+            return UBW_EHIP;
+    }
+    if (word & kWsErrWait) return UBW_EWAIT;
+    if (word & kWsErrIndex) return UBW_ERANGE;
     return UBW_OK;
 }
 

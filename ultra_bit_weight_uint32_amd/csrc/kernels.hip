@@ -25,6 +25,7 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstddef>
 #include <type_traits>
 
@@ -400,12 +401,34 @@ __global__ void k_extract4(const uint32_t* __restrict__ packed, int nb, int N, i
 // cross-lane swap when flushing. The data of the next three units are in flight while a unit
 // is processed (three register slots, reloaded in place).
 //
-// y = result in one launch (kModeFirst): at its start workgroup g zeroes the rows of every
-// row group rg with rg mod G == g, and raises that row group's flag once the zeroing has been
-// performed (at its first staging barrier); a workgroup reads the flag of a row group before
-// adding into it. Zeroing depends on nothing and the grid never exceeds what the device holds
-// at once, so every wait ends. Per row group, 256 bytes of workspace: word 0 =
-// (generation << 12) | arrivals, word 32 = flag (launches that zeroed the row group).
+// y = result in one launch (kModeFirst, with a workspace). Per row group, 256 bytes of
+// workspace: word 0 counts arrivals, (generation << 12) | units announced in this launch, and
+// word 32 (the flag) counts the launches that initialized the row group's rows of y; between
+// launches both hold the same count. A workgroup announces its units of a row group with one
+// atomic add when it starts on them, and adds into y only after it has seen the flag raised for
+// this launch (one past the generation its add returned), unless it initialized the rows
+// itself; the participant whose add brings the arrivals to the row group's total resets the
+// field and advances the generation. Two ways to initialize (zero) the rows:
+//  * XCD-local mode (8 or more row groups and workgroups): the dispatcher deals a launch's
+//    workgroups out to the eight XCDs in turn (workgroup g runs on XCD g mod 8) and allocates
+//    each XCD's share in ID order. Row group rg is worked on only by workgroups on XCD rg mod 8,
+//    and zeroed by workgroup rg, which has no units, runs on that XCD and has a lower ID than
+//    every workgroup that adds into it: whenever one of those waits, workgroup rg has been
+//    allocated, and it zeroes the rows with atomic exchanges, waits for them and raises the
+//    flag without waiting for anything else. No zeroing waits for an atomic's answer first.
+//  * First-arriver mode (otherwise, e.g. grouped launches): the value the add returns says
+//    whether the workgroup arrived first, and the first arriver initializes the rows. A
+//    candidate (an arriver without units, or a run that starts among the row group's first
+//    units) makes its add before its loads and looks at the answer right away: if first, wave 0
+//    zeroes the rows, waits for the exchanges and raises the flag. Any other workgroup looks at
+//    the answer only at its flush and, if it did arrive first, writes its own partial sums there
+//    with exchanges (every row of the row group) and then raises the flag. The first arriver is
+//    running (it made the add) and raises the flag without waiting for any other workgroup;
+//    every waiter arrived after it.
+// Either way nothing depends on how many workgroups the device holds at once, so launches on
+// other streams (with their own workspaces) cannot stall the protocol. A bounded spin still
+// guards each wait: if it ever ran out, the workgroup would set bit 0 of workspace word 0 and
+// add nothing.
 
 enum { kModeStore = 0, kModeAtomic = 2, kModeFirst = 3 };
 constexpr int kSpinLimit = 1 << 20;
@@ -437,10 +460,12 @@ struct StepParams {
     int US[2];        // units per row group per segment
     int Urg;          // units per row group, both segments
     int U;            // units in the whole list (< 2^31)
-    int G;            // workgroups
-    int Gu;           // workgroups with units (the first Gu); the others only zero y
+    int G;            // workgroups: Zn arrivers without units (IDs 0 .. Zn - 1), then Gu with units
+    int Gu;           // workgroups with units
+    int Zn;           // arrivers without units, one per row group (0 or NRG)
+    int Arr;          // arrivals that complete a row group: Urg, plus 1 when Zn > 0
     int mode;
-    int Q, R;         // U = Q Gu + R: workgroup g < Gu takes Q units, plus one if g < R
+    int xmode;        // 1: XCD-local row groups with static zeroing (see step_body), 0: first arriver
     FastDiv dUS[2];   // division by US[si]
     FastDiv dNb[2];   // division by seg[si].nb
 };
@@ -458,7 +483,7 @@ struct Unit {
     XT xv[BMAX];       // staging: activations of the staged column (0 for rows >= batch)
     uint4 xb;          // XL: this thread's 16 bytes of the activation block
     uint32_t xc;       // XL: idx of the staged column (read at staging, so nothing waits for it here)
-    bool cv;           // XL: the staged column exists
+    uint32_t xp;       // XL: idx of the column before it (for the ascending-order check)
 };
 
 // A unit within its segment's part of the list: row group, unit within the row group, and the
@@ -542,6 +567,7 @@ struct LaneC {
     uint32_t hsel;    // lookup item within the unit (half of the wave)
     uint32_t wl;      // byte offset of this lane's row in its item's tile, item 2 q + h relative to 2 q
     uint32_t rho;     // tile row
+    int rgo, rgs;     // row group rgo + rgs * rg for a cursor's rg (this workgroup's row groups)
 };
 
 template <int SI, bool XL, bool GS, typename XT, int RPL, int BMAX>
@@ -561,14 +587,22 @@ __device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const Step
     const bool its_ok = 2 * cu.q + (int)lcn.sd < nitems;
     const uint32_t colBase = (uint32_t)sks * kSliceCols;
     const bool cvalid = its_ok && colBase + lcn.colL < (uint32_t)sg.Kv;
-    // idx of the staged column; with XL it is loaded straight into the unit (a copy of a value
-    // still in flight would wait for it)
-    uint32_t raw = 0;
+    // idx of the staged column and of the one before it (for the checks); with XL they are loaded
+    // straight into the unit and checked at staging (a copy of a value still in flight would wait
+    // for it), otherwise checked below, where the gather waits for them anyway
+    const uint32_t col = colBase + lcn.colL;
+    uint32_t raw = 0, rawp = 0;
     if constexpr (SI == 1) {
         const Rsrc r_idx = make_rsrc(sg.idx, valid ? (uint32_t)sg.Kv * 4u : 0u);
-        const int ioff = (int)(cvalid ? (colBase + lcn.colL) * 4u : kOob);
-        if constexpr (XL) U.xc = __builtin_amdgcn_raw_buffer_load_b32(r_idx, ioff, 0, 0);
-        else raw = __builtin_amdgcn_raw_buffer_load_b32(r_idx, ioff, 0, 0);
+        const int ioff = (int)(cvalid ? col * 4u : kOob);
+        const int poff = (int)(cvalid && col > 0 ? col * 4u - 4u : kOob);
+        if constexpr (XL) {
+            U.xc = __builtin_amdgcn_raw_buffer_load_b32(r_idx, ioff, 0, 0);
+            U.xp = __builtin_amdgcn_raw_buffer_load_b32(r_idx, poff, 0, 0);
+        } else {
+            raw = __builtin_amdgcn_raw_buffer_load_b32(r_idx, ioff, 0, 0);
+            rawp = __builtin_amdgcn_raw_buffer_load_b32(r_idx, poff, 0, 0);
+        }
     }
     const uint32_t acBase = ((uint32_t)sk * (uint32_t)sg.Kv + colBase) * 4u;
     U.ac = buf_f32(make_rsrc(sg.alpha_c, valid ? (uint32_t)sg.nb * (uint32_t)sg.Kv * 4u : 0u),
@@ -579,7 +613,6 @@ __device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const Step
             buf_x(r_x, cvalid ? ((uint32_t)b * ldx + colBase) * xs + lcn.colL * xs : kOob, U.xv[b]);
     } else if constexpr (XL) {
         U.xb = buf_u128(r_x, 16u * (uint32_t)tid);  // before the weights, like x in the main segment
-        U.cv = cvalid;
     }
     // lookup role: item 2 q + h for tile row rho
     const bool lval = 2 * cu.q + (int)lcn.hsel < nitems;
@@ -595,7 +628,7 @@ __device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const Step
         make_rsrc(sg.alpha_r, valid ? (uint32_t)sg.nb * (gsc ? (uint32_t)P.KT[0] : 1u) * (uint32_t)a.N * 4u : 0u);
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
-        const int rt = cu.rg * RPL + j;
+        const int rt = (lcn.rgo + lcn.rgs * cu.rg) * RPL + j;
         const Rsrc r_w = make_rsrc(sg.packed + (int64_t)rt * nitems * kTileWords, valid && rt < P.NT ? slab : 0u);
         U.w[j][0] = buf_u128(r_w, woff);
         U.w[j][1] = buf_u128(r_w, lval ? woff + kTileRows * 16u : kOob);
@@ -603,19 +636,15 @@ __device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const Step
         U.ar[j] = buf_f32(r_ar, lval && row < (uint32_t)a.N ? arBase + row * 4u : kOob);
     }
     if constexpr (SI == 1 && !XL) {
-        const uint32_t xc = raw < ldx ? raw : ldx - 1u;  // in range by contract
+        // VCM: the index must lie in [0, K) and exceed the one before it (ascending, distinct); a
+        // column that breaks this reads nothing (x = 0, so it contributes nothing) and sets bit 1
+        // of workspace word 0
+        const bool bad = valid && cvalid && (raw >= ldx || (col > 0 && (int)rawp >= (int)raw));
+        if (bad && a.ws != nullptr) atomicOr(a.ws, kWsErrIndex);
+        const bool use = cvalid && !bad;
 #pragma unroll
-        for (int b = 0; b < BMAX; ++b) buf_x(r_x, cvalid ? ((uint32_t)b * ldx + xc) * xs : kOob, U.xv[b]);
+        for (int b = 0; b < BMAX; ++b) buf_x(r_x, use ? ((uint32_t)b * ldx + raw) * xs : kOob, U.xv[b]);
     }
-}
-
-// First unit of workgroup g's range: the first R workgroups take Q + 1 units, the rest of the
-// first Gu take Q, and the workgroups past Gu none. (The first workgroups start first; with
-// one per CU and two units on some, measured on 4096 x 4096 with 5% salient columns: longer
-// ranges first 6.12 us, in the middle 6.36 us, last 7.02 us.)
-__device__ __forceinline__ uint32_t range_start(const StepParams& P, uint32_t g) {
-    const uint32_t x = g * (uint32_t)P.Q + (g < (uint32_t)P.R ? g : (uint32_t)P.R);
-    return x < (uint32_t)P.U ? x : (uint32_t)P.U;  // from g = Gu on: Gu Q + R = U
 }
 
 // The body of a step: workgroup g of the P.G that work on the GEMV described by P.
@@ -656,53 +685,87 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) lc[i] += 0x80808080u * (uint32_t)h;  // half h's tables: +128 bytes
 
-    const uint32_t x0 = range_start(P, g);
-    const uint32_t x1 = range_start(P, g + 1);
-    const uint32_t Um = (uint32_t)P.NRG * (uint32_t)P.US[0];  // units of segment 0
-
-    // y = result in one launch: workgroup g zeroes the rows of the row groups rg = g, g + G, ...
-    // with atomic exchanges and raises their flags once every exchange has been performed. It
-    // does so right after requesting its first unit's data, so the wait for the exchanges
-    // overlaps that request and covers nothing else.
+    // y = result protocol (kModeFirst; see the comment above kModeStore)
     const bool first_mode = P.mode == kModeFirst;
-    // Row group rg is zeroed by workgroup (rg + off) mod G. With workgroups that have no units
-    // (G > Gu) those do it (off = Gu), so that no workgroup with units waits for the exchanges;
-    // otherwise, with off = NRG (when G >= 2 NRG), the zeroing workgroups are not the first ones,
-    // which the device places on CUs that also receive the workgroups beyond one per CU.
-    const int zoff = P.G > P.Gu ? P.Gu : (2 * P.NRG <= P.G ? P.NRG : 0);
-    const int zrg0 = g >= zoff ? g - zoff : g - zoff + P.G;  // first row group this workgroup zeroes
-    bool zpend = first_mode && zrg0 < P.NRG;
-    auto rg_word = [&](int rg) { return a.ws + kWsHeaderWords + kWsRowGroupWords * rg; };
-    auto zero_owned = [&]() {
-        zpend = false;
-        for (int rg = zrg0; rg < P.NRG; rg += P.G) {
-            float zr[RPL][BMAX];
-#pragma unroll
-            for (int j = 0; j < RPL; ++j) {
-                const int rt = rg * RPL + j;
-                const int row = rt * kTileRows + tid;
-                const bool rv = tid < kTileRows && rt < P.NT && row < a.N;
-#pragma unroll
-                for (int b = 0; b < BMAX; ++b) {
-                    zr[j][b] = 0.f;
-                    if (rv && b < a.batch)
-                        zr[j][b] = __hip_atomic_exchange(a.y + (int64_t)b * a.N + row, 0.f, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-            // wait for every returned value (each exchange has then been performed)
-#pragma unroll
-            for (int j = 0; j < RPL; ++j)
-#pragma unroll
-                for (int b = 0; b < BMAX; ++b) asm volatile("" ::"v"(zr[j][b]));
-            __syncthreads();
-            // A flag counts the launches that have zeroed its row group, as the arrival
-            // counter's generation field counts the launches whose units have all arrived:
-            // between launches the two are equal, so the increment makes the flag generation + 1.
-            if (tid == 0)
-                __hip_atomic_fetch_add(rg_word(rg) + kWsFlagOffset, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    auto rg_word = [&](int grg) { return a.ws + kWsHeaderWords + kWsRowGroupWords * grg; };
+    __shared__ uint32_t s_fm;  // flush mode from thread 0: bit 0 add nothing, bit 1 initialize y
+    // The flag of row group grg: the count of launches that initialized its rows.
+    auto read_flag = [&](int grg) -> uint32_t {
+        return __hip_atomic_load(rg_word(grg) + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
+    auto raise_flag = [&](int grg) {
+        __hip_atomic_fetch_add(rg_word(grg) + kWsFlagOffset, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // Wave 0 of a row group's zeroing workgroup: y = 0 on every row of row group grg (all
+    // activation rows) with atomic exchanges, wait until all have returned (each has then been
+    // performed), raise the flag.
+    auto zero_rows = [&](int grg) {
+        uint32_t sink = 0;
+#pragma unroll
+        for (int j = 0; j < RPL; ++j) {
+            const int rt = grg * RPL + j;
+#pragma unroll
+            for (int q = 0; q < kTileRows / 64; ++q) {
+                const int row = rt * kTileRows + 64 * q + L;
+                const bool rv = rt < P.NT && row < a.N;
+#pragma unroll
+                for (int b = 0; b < BMAX; ++b)
+                    if (rv && b < a.batch)
+                        sink |= __float_as_uint(__hip_atomic_exchange(a.y + (int64_t)b * a.N + row, 0.f,
+                                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            }
+        }
+        asm volatile("" ::"v"(sink));
+        if (L == 0) raise_flag(grg);
+    };
+
+    // The first Zn workgroups have no units. XCD-local mode: workgroup g < NRG zeroes row group g
+    // at once and raises its flag (it runs on XCD g mod 8, with every workgroup that adds into row
+    // group g, and has a lower ID than all of them). First-arriver mode: it announces one arrival
+    // at row group g, zeroes its rows if first, and completes the row group if last.
+    if (g < P.Zn) {
+        if (wv == 0 && g < P.NRG) {
+            if (P.xmode) {
+                zero_rows(g);
+            } else {
+                uint32_t arr = 0;
+                if (L == 0) arr = atomicAdd(rg_word(g), 1u);
+                arr = __builtin_amdgcn_readfirstlane(arr);
+                if ((arr & kArrMask) == 0) zero_rows(g);
+                if (L == 0 && (arr & kArrMask) + 1u == (uint32_t)P.Arr)
+                    atomicAdd(rg_word(g), (1u << kArrBits) - (uint32_t)P.Arr);
+            }
+        }
+        return;
+    }
+
+    // The row groups this workgroup works on and its range of units. XCD-local mode: workgroup g
+    // runs on XCD g mod 8 (the dispatcher deals a launch's workgroups out to the eight XCDs in
+    // turn) and works only on the row groups rg = g mod 8, g mod 8 + 8, ..., as rank g / 8 of that
+    // XCD's workgroups, over a unit list of those row groups alone; otherwise on every row group
+    // as rank g - Zn. Either way the list holds the main units row group by row group, then the
+    // refinement units, and rank r takes an equal contiguous range (the first ones one unit more).
+    // A cursor's rg counts the listed row groups; it is row group rgo + rgs * rg of the matrix.
+    int rank, Gx, NRGx;
+    if (P.xmode) {  // Zn is a multiple of 8: unit workgroup g - Zn is on the XCD of g
+        lcn.rgo = g & 7;
+        lcn.rgs = 8;
+        rank = (g - P.Zn) >> 3;
+        Gx = (P.Gu - lcn.rgo + 7) >> 3;
+        NRGx = (P.NRG - lcn.rgo + 7) >> 3;
+    } else {
+        lcn.rgo = 0;
+        lcn.rgs = 1;
+        rank = g - P.Zn;
+        Gx = P.Gu;
+        NRGx = P.NRG;
+    }
+    auto grg = [&](int rg) { return lcn.rgo + lcn.rgs * rg; };
+    const uint32_t Ux = (uint32_t)NRGx * (uint32_t)P.Urg;
+    const uint32_t Qx = Ux / (uint32_t)Gx, Rx = Ux - Qx * (uint32_t)Gx;
+    const uint32_t x0 = (uint32_t)rank * Qx + ((uint32_t)rank < Rx ? (uint32_t)rank : Rx);
+    const uint32_t x1 = x0 + Qx + ((uint32_t)rank < Rx ? 1u : 0u);
+    const uint32_t Um = (uint32_t)NRGx * (uint32_t)P.US[0];  // units of segment 0 in the list
 
     float acc[RPL][BMAX];
     auto clear_acc = [&]() {
@@ -713,54 +776,79 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
     };
     clear_acc();
 
-    // Row-group bookkeeping (thread 0): the arrival counter's value returned on entry, the units
-    // this workgroup adds to it, the flag as read on entry and, if that read did not find it
-    // raised, as read again before the last lookups of the run (kept apart so that a flush
-    // after a successful first read does not wait for the loads issued after it).
+    // Row-group bookkeeping (thread 0, except `zeroed`, which wave 0 sets): the arrival counter's
+    // value returned on entry, the units this workgroup adds to it, the flag as read on entry and,
+    // if that read did not find it raised, as read again before the last lookups of the run (kept
+    // apart so that a flush after a successful first read does not wait for the loads issued after
+    // it), and whether this workgroup has zeroed the row group's rows (first-arriver mode).
     uint32_t arrived = 0, units_in = 0, seen = 0, seen_late = 0;
-    bool late = false;
+    bool late = false, zeroed = false;
     auto want = [&]() { return ((arrived >> kArrBits) + 1) & kGenMask; };
-    // Entering row group rg with n of its units to process: add n to its counter's arrival
-    // field and take a first look at its flag. Both are requested before the loads that follow,
-    // so using their values never waits for those. Over a launch the arrivals of a row group
-    // add up to its unit count Urg; the flush that completes them resets the field.
+    // whether this workgroup adds into row group rg without waiting for its flag (it initializes it)
+    auto no_wait = [&](int) { return !P.xmode && (arrived & kArrMask) == 0; };
+    // Entering row group rg with n of its units to process: add n to its arrival field and take a
+    // first look at its flag.
     auto enter = [&](int rg, uint32_t n) {
+        zeroed = false;
         if (first_mode && tid == 0) {
             units_in = n;
-            arrived = atomicAdd(rg_word(rg), n);
-            seen = __hip_atomic_load(rg_word(rg) + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            arrived = atomicAdd(rg_word(grg(rg)), n);
+            seen = read_flag(grg(rg));
+        }
+    };
+    // First-arriver mode, after an entry at the start of a run (its add the oldest memory
+    // operation of the run): if this workgroup arrived first, wave 0 zeroes the rows now.
+    auto zero_if_first = [&](int rg) {
+        if (first_mode && wv == 0) {
+            const uint32_t arr = __builtin_amdgcn_readfirstlane(arrived);
+            if ((arr & kArrMask) == 0) {
+                zero_rows(grg(rg));
+                zeroed = true;
+            }
         }
     };
 
     // Add this workgroup's partial sums of row group rg into y.
     auto flush = [&](int rg) {
+        uint32_t fm = 0;
+        const int gr = grg(rg);
         if (first_mode) {
             if (tid == 0) {
-                const uint32_t wnt = want();
-                uint32_t cur = seen;
-                if (late) {
-                    asm volatile("");  // keeps this a branch: only this path waits for seen_late
-                    cur = seen_late;
-                }
-                int n = 0;
-                while ((cur & kGenMask) != wnt) {
-                    if (++n > kSpinLimit) {  // cannot happen while the owner runs; never hang
-                        atomicOr(a.ws, 1u);
-                        break;
+                uint32_t m = 0;
+                if (no_wait(rg)) {
+                    if (!P.xmode && !zeroed) m = 2;  // arrived first mid-run: initialize y with these sums
+                } else {
+                    const uint32_t wnt = want();
+                    uint32_t cur = seen;
+                    if (late) {
+                        asm volatile("");  // keeps this a branch: only this path waits for seen_late
+                        cur = seen_late;
                     }
-                    __builtin_amdgcn_s_sleep(2);
-                    cur = __hip_atomic_load(rg_word(rg) + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    int n = 0;
+                    while ((cur & kGenMask) != wnt) {
+                        if (++n > kSpinLimit) {  // the zeroer raises it; never hang regardless
+                            atomicOr(a.ws, kWsErrWait);
+                            m = 1;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                        cur = read_flag(gr);
+                    }
                 }
                 late = false;
-                const uint32_t total = (uint32_t)P.Urg;
+                const uint32_t total = (uint32_t)P.Arr;
                 if ((arrived & kArrMask) + units_in == total)  // completes it: arrivals 0, next generation
-                    atomicAdd(rg_word(rg), (1u << kArrBits) - total);
+                    atomicAdd(rg_word(gr), (1u << kArrBits) - total);
+                s_fm = m;
             }
             __syncthreads();
+            fm = __builtin_amdgcn_readfirstlane(s_fm);  // uniform: the branches below are scalar
         }
+        if (fm & 1u) return;  // a wait gave up: add nothing (workspace word 0 says so)
+        uint32_t sink = 0;
 #pragma unroll
         for (int j = 0; j < RPL; ++j) {
-            const int rt = rg * RPL + j;
+            const int rt = gr * RPL + j;
             const int row = rt * kTileRows + rho;
             const bool rv = rt < P.NT && row < a.N;
 #pragma unroll
@@ -771,10 +859,18 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
                 const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
                 if (h == 0 && rv) {
                     float* dst = a.y + (int64_t)b * a.N + row;
-                    if (P.mode == kModeStore) *dst = total;
+                    if (fm & 2u)
+                        sink |= __float_as_uint(
+                            __hip_atomic_exchange(dst, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                    else if (P.mode == kModeStore) *dst = total;
                     else atomicAdd(dst, total);
                 }
             }
+        }
+        if (fm & 2u) {  // every row of the row group written: raise the flag once all have returned
+            asm volatile("" ::"v"(sink));
+            __syncthreads();
+            if (tid == 0) raise_flag(gr);
         }
     };
 
@@ -793,8 +889,8 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         __syncthreads();
         // before the lookups that end a row group, look at its flag again if the look on entry
         // did not find it raised (the read then overlaps the lookups)
-        if (first_mode && last && tid == 0 && b == 0 && (seen & kGenMask) != want()) {
-            seen_late = __hip_atomic_load(rg_word(rg) + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (first_mode && last && tid == 0 && b == 0 && !no_wait(rg) && (seen & kGenMask) != want()) {
+            seen_late = read_flag(grg(rg));
             late = true;
         }
         if constexpr (decltype(gs_c)::value) {
@@ -824,16 +920,26 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         const bool mine = 2 * cu.q + h < nitems;  // this half has an item in this unit
         // scaled activations of both items: v = alpha_c * x (LUT-BSF folds alpha_c here)
         if constexpr (SI == 1 && XL) {
+            // VCM: the staged column's index must lie in [0, K) and exceed the one before it
+            // (ascending, distinct); a column that breaks this contributes nothing and sets bit 1
+            // of workspace word 0
+            const uint32_t ldx = (uint32_t)a.ldx;
+            int sks, sk;
+            item_of(cu, (int)lcn.sd, a.seg[1].nb, sks, sk);
+            const uint32_t col = (uint32_t)sks * kSliceCols + lcn.colL;
+            const bool cvalid = 2 * cu.q + (int)lcn.sd < nitems && col < (uint32_t)a.seg[1].Kv;
+            const bool bad = cvalid && (U.xc >= ldx || (col > 0 && (int)U.xp >= (int)U.xc));
+            if (bad && a.ws != nullptr) atomicOr(a.ws, kWsErrIndex);
+            const bool use = cvalid && !bad;
             // the activation block into the table area (free until the build below), then the
             // gather through idx from there
             lds_u32x4* blk = (lds_u32x4*)(tab + 4 * tid);
             *blk = u32x4{U.xb.x, U.xb.y, U.xb.z, U.xb.w};
             __syncthreads();
-            const uint32_t ldx = (uint32_t)a.ldx;
-            const uint32_t xc = U.xc < ldx ? U.xc : ldx - 1u;  // in range by contract
+            const uint32_t xc = use ? U.xc : 0u;
 #pragma unroll
             for (int b = 0; b < BMAX; ++b)
-                if (b < a.batch) sv[b * 512 + tid] = U.cv ? U.ac * lds_x<XT>(tb, (uint32_t)b * ldx + xc) : 0.f;
+                if (b < a.batch) sv[b * 512 + tid] = use ? U.ac * lds_x<XT>(tb, (uint32_t)b * ldx + xc) : 0.f;
         } else {
 #pragma unroll
             for (int b = 0; b < BMAX; ++b)
@@ -859,7 +965,8 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
     // The run of segment SI's units in [x0, x1). Three register slots, each reloaded in place
     // three units ahead (no copies between slots, which would wait on loads still in flight);
     // loads past the run are issued with valid = false and read nothing, so every path issues
-    // the same loads. An owner zeroes its row groups right after requesting its first unit.
+    // the same loads. The run's first arrival is made before its loads, so that a first arriver
+    // learns it (and zeroes) without waiting for them.
     auto run = [&](auto si_c) {
         constexpr int SI = decltype(si_c)::value;
         const uint32_t base = SI ? Um : 0u;
@@ -877,14 +984,22 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             return hi - x < left ? hi - x : left;
         };
         Unit<XT, RPL, BMAX, XL> s0, s1, s2;
+        // The candidate zeroer of the row group this run starts in is a run that starts among the
+        // row group's first Q + 1 units of this segment (none when arrivers without units go
+        // first): it announces its arrival before its loads and looks at the answer as soon as
+        // it returns. Every other workgroup announces after its first unit's loads (so that the
+        // candidate's add usually comes first) and looks only at its flush, by when the answer
+        // is long back; if it did arrive first after all, it initializes the rows there.
+        const bool cand = first_mode && !P.xmode && P.Zn == 0 && (uint32_t)pcur.q <= Qx;
+        if (cand) enter(pcur.rg, run_units(lo, pcur));
         load_unit<SI, XL, GS>(s0, P, lcur, true, lcn, tid);
         advance(lcur, US, nb);
-        if (zpend) zero_owned();
-        enter(pcur.rg, run_units(lo, pcur));
+        if (!cand) enter(pcur.rg, run_units(lo, pcur));
         load_unit<SI, XL, GS>(s1, P, lcur, lo + 1 < hi, lcn, tid);
         advance(lcur, US, nb);
         load_unit<SI, XL, GS>(s2, P, lcur, lo + 2 < hi, lcn, tid);
         advance(lcur, US, nb);
+        if (cand) zero_if_first(pcur.rg);
         auto step = [&](const Unit<XT, RPL, BMAX, XL>& U, uint32_t x) {
             const bool last = x + 1 == hi || pcur.q + 1 == US;
             process(U, nitems, pcur, last, si_c);
@@ -905,16 +1020,19 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
     };
     run(std::integral_constant<int, 0>{});
     if (P.US[1] > 0) run(std::integral_constant<int, 1>{});
-    if (zpend) zero_owned();  // a workgroup without units (the host never launches one)
 }
 
 
 // Occupancy: the second argument is a minimum of waves per SIMD (2 lets the compiler use up to
 // 256 VGPRs); two workgroups per CU need at most 128, which the instances with one or two row
-// tiles and batch up to 4 stay within. (Asking for 4 waves per SIMD instead makes the compiler
-// issue the table lookups in smaller batches, which costs more than it gains.)
+// tiles and batch up to 4 stay within on their own, except two row tiles at four activation rows
+// (per-row scales), which sits at the edge and is held to four waves per SIMD explicitly. (Asking for 4 waves per
+// SIMD everywhere makes the compiler issue the table lookups in smaller batches, which costs
+// more than it gains.)
+template <int RPL, int BMAX, bool GS>
+constexpr int kMinWaves = (RPL == 2 && BMAX == 4 && !GS) ? 4 : 2;
 template <typename XT, int RPL, int BMAX, bool XL, bool GS>
-__global__ __launch_bounds__(kStepThreads, 2) void k_gemv8(StepParams P) {
+__global__ __launch_bounds__(kStepThreads, (kMinWaves<RPL, BMAX, GS>)) void k_gemv8(StepParams P) {
     step_body<XT, RPL, BMAX, XL, GS>(P, (int)blockIdx.x);
 }
 
@@ -927,7 +1045,7 @@ struct GroupParams {
 };
 
 template <typename XT, int RPL, int BMAX, bool XL>
-__global__ __launch_bounds__(kStepThreads, 2) void k_gemv8_group(GroupParams GP) {
+__global__ __launch_bounds__(kStepThreads, (kMinWaves<RPL, BMAX, false>)) void k_gemv8_group(GroupParams GP) {
     const int b = (int)blockIdx.x;
     int i = 0;
     while (i + 1 < GP.count && b >= GP.start[i + 1]) ++i;
@@ -1012,27 +1130,34 @@ hipError_t launch_extract(const uint32_t* packed, int nb, int N, int K, int g, u
     return hipGetLastError();
 }
 
-// Workgroups of a kernel instance that the device can hold at once (occupancy x CUs), cached.
+// Workgroups of a kernel instance that the current device can hold at once (occupancy x CUs),
+// cached per device (thread-safe: each entry is written once with the value every thread
+// computes; devices numbered kMaxDevices or above are queried on every call).
 template <typename Kernel>
-static int64_t capacity_of(Kernel k, int64_t& cache) {
-    if (cache < 0) {  // benign race: every thread computes the same value
-        int dev = 0, cus = 0, per_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kStepThreads, 0) != hipSuccess)
-            return 0;
-        cache = (int64_t)cus * per_cu;
+static int64_t capacity_of(Kernel k, std::atomic<int64_t>* cache) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached) {
+        const int64_t c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
     }
-    return cache;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kStepThreads, 0) != hipSuccess)
+        return 0;
+    const int64_t c = (int64_t)cus * per_cu;
+    if (cached) cache[dev].store(c, std::memory_order_relaxed);
+    return c;
 }
 template <typename XT, int RPL, int BMAX, bool XL, bool GS>
 static int64_t resident_capacity() {
-    static int64_t cap = -1;
+    static std::atomic<int64_t> cap[kMaxDevices];
     return capacity_of(k_gemv8<XT, RPL, BMAX, XL, GS>, cap);
 }
 template <typename XT, int RPL, int BMAX, bool XL>
 static int64_t resident_capacity_group() {
-    static int64_t cap = -1;
+    static std::atomic<int64_t> cap[kMaxDevices];
     return capacity_of(k_gemv8_group<XT, RPL, BMAX, XL>, cap);
 }
 
@@ -1049,30 +1174,43 @@ static int64_t default_workgroups(int64_t U, int64_t cap, int batch) {
 }
 
 // Split of P's units over Gu workgroups and the final output mode; zero-fills y first when the
-// single-launch protocol cannot be used (no workspace, or too many units per row group). With
-// the single-launch protocol, every workgroup taking the same number of units (R = 0) and room
-// on the device (Gu + NRG <= cap), NRG more workgroups without units zero y, one row group
-// each: the exchanges' round trip then delays no workgroup with units (measured on 4096 x 4096,
-// 256 units: 5.84 -> 5.36 us). With R > 0 the zeroing workgroups (from NRG on) are ones with
-// the shorter ranges, which finish before the longer ones anyway, and extra workgroups would
-// only crowd the CUs of the longer ones (4096 x 4096 with 5% salient columns, 272 units:
-// 6.12 us without, 6.29 us with).
-static hipError_t finish_params(StepParams& P, int64_t Gu, int64_t cap, hipStream_t s) {
+// single-launch protocol cannot be used (no workspace, or too many arrivals per row group for
+// the counter's field).
+// The single-launch protocol runs in XCD-local mode (static zeroing by NRG workgroups without
+// units at the lowest IDs; see step_body) when allowed and every one of the eight XCDs gets
+// workgroups and row groups (Gu >= 8, NRG >= 8). Otherwise it runs in first-arriver mode,
+// where with equal ranges (R = 0) and room on the device
+// (Gu + NRG <= cap) NRG arrivers without units go first (lowest IDs), one per row group: they
+// usually arrive first and zero, so no workgroup with units waits for the exchanges' round trip
+// (measured on 4096 x 4096, 256 units, with such workgroups as zeroing owners: 5.84 -> 5.36 us).
+// With R > 0 such workgroups would crowd the CUs of the longer ranges (4096 x 4096 with 5%
+// salient columns, 272 units: 6.12 us without, 6.29 us with).
+constexpr int kXcds = 8;  // XCDs of an MI355X; workgroup g runs on XCD g mod 8
+
+static hipError_t finish_params(StepParams& P, int64_t Gu, int64_t cap, bool allow_xcd, hipStream_t s) {
     P.Gu = (int)Gu;
-    P.G = (int)Gu;
-    P.Q = P.U / P.Gu;
-    P.R = P.U - P.Q * P.Gu;
+    P.Zn = 0;
+    P.xmode = 0;
+    const int64_t R = P.U % Gu;
     // every workgroup holds exactly one whole row group (one segment only: a refinement
     // segment's units of a row group sit in another part of the list): plain stores
     const bool whole_rows = P.Gu == P.NRG && P.US[1] == 0;
     if (P.mode == kModeFirst && whole_rows) P.mode = kModeStore;
-    // the arrival field counts a row group's units (Urg) and must not overflow into the generation
+    // the arrival field counts a row group's arrivals (Urg, plus one) and must not overflow into
+    // the generation
     if (P.mode == kModeFirst && (P.a.ws == nullptr || P.Urg + 1 > (int)kArrMask)) {
         hipError_t e = launch_fill_zero(P.a.y, (int64_t)P.a.batch * P.a.N, s);
         if (e != hipSuccess) return e;
         P.mode = kModeAtomic;
     }
-    if (P.mode == kModeFirst && P.R == 0 && Gu + P.NRG <= cap) P.G = (int)(Gu + P.NRG);
+    if (P.mode == kModeFirst && allow_xcd && Gu >= kXcds && P.NRG >= kXcds) {
+        P.xmode = 1;
+        P.Zn = (int)ceil_div(P.NRG, kXcds) * kXcds;  // keeps unit workgroup g - Zn on the XCD of g
+    } else if (P.mode == kModeFirst && R == 0 && Gu + P.NRG <= cap) {
+        P.Zn = P.NRG;
+    }
+    P.Arr = P.Urg + (P.Zn > 0 && !P.xmode ? 1 : 0);
+    P.G = P.Zn + P.Gu;
     return hipSuccess;
 }
 
@@ -1080,11 +1218,11 @@ template <typename XT, int RPL, int BMAX, bool XL, bool GS>
 static hipError_t launch_step_t(StepParams P, hipStream_t s) {
     const int64_t cap = resident_capacity<XT, RPL, BMAX, XL, GS>();
     if (cap <= 0) return hipErrorInvalidConfiguration;
-    // Never more workgroups than the device holds at once: the flag waits rely on it.
+    // Persistent workgroups: by default no more than the device holds at once (an explicit
+    // geometry may ask for more; the flag waits do not depend on it).
     int64_t G = P.a.workgroups > 0 ? P.a.workgroups : default_workgroups(P.U, cap, P.a.batch);
-    G = G < cap ? G : cap;
     G = G < P.U ? G : P.U;
-    hipError_t e = finish_params(P, G, cap, s);
+    hipError_t e = finish_params(P, G, cap, true, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_gemv8<XT, RPL, BMAX, XL, GS>), dim3((unsigned)P.G), dim3(kStepThreads), 0, s, P);
     return hipGetLastError();
@@ -1119,7 +1257,7 @@ static hipError_t launch_group_t(GroupParams GP, hipStream_t s) {
     }
     GP.start[0] = 0;
     for (int i = 0; i < GP.count; ++i) {
-        hipError_t e = finish_params(GP.p[i], Gi[i], 0, s);
+        hipError_t e = finish_params(GP.p[i], Gi[i], 0, false, s);
         if (e != hipSuccess) return e;
         GP.start[i + 1] = GP.start[i] + (int)Gi[i];
     }

@@ -7,12 +7,15 @@
 // B^(k) V^(k) (V = the rows' v side by side) is a dense contraction whose cost does not grow with
 // the rows up to the matrix instruction's width. Here the sign bits are expanded to fp16 +-1
 // (exact) and multiplied on v_mfma_f32_16x16x32_f16 against V split into fp16 high and low
-// parts (v = hi + lo to 2^-20 relative), accumulating in fp32: the result matches the
-// table path's fp32 arithmetic up to summation order. Each activation row of a staged slice is
-// scaled by a power of two (exact) that puts its largest |v| in [2^14, 2^15), so no value
-// overflows fp16 and small ones keep their precision; the MFMA result of the slice is scaled
-// back before it is added to the running sums. Main bases and the salient refinement (columns
-// gathered through idx) go through the same loop.
+// parts, accumulating in fp32. Each activation row of a staged slice is scaled by a power of two
+// 2^e (exact) that puts its largest |v| in [2^14, 2^15), so no value overflows fp16; the MFMA
+// result of the slice is scaled back before it is added to the running sums. Precision of the
+// split, per element (hi = v rounded toward zero to fp16, lo = the exact fp32 remainder v - hi
+// rounded the same way): |v - hi - lo| < 2^-20 |v| + 2^-24 2^e <= 2^-20 |v| + 2^-38 m, where m
+// is the largest |v| of the activation row in the slice (the 2^-24 term covers fp16's
+// subnormal spacing). The tables use v itself in fp32 (2^-24 |v|), so the two paths agree to
+// that bound per element plus their different fp32 summation orders. Main bases and the salient
+// refinement (columns gathered through idx) go through the same loop.
 //
 // GEMVs that share x run in one launch: grid x covers their row tiles one GEMV after the other
 // (so the small k and v projections fill the CUs next to q), grid y the column chunks, each GEMV
@@ -43,6 +46,8 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <atomic>
 
 #include "ubw_internal.h"
 
@@ -75,6 +80,8 @@ struct MmParams {
     int ST;      // slices over both segments (seg[0].KT + seg[1].KT)
     int KC;      // column chunks (grid y at most this GEMV's KC; workgroups beyond it exit)
     int atomic;  // 1: add into y with atomics, 0: store
+    uint32_t* err;  // the GEMV's workspace (word 0: bit 1 set for a salient index out of range or
+                    // out of order), or nullptr
 };
 
 // GEMVs sharing x in one launch: grid x covers their row tiles one GEMV after the other.
@@ -190,7 +197,9 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
         // (refinement) idx of the staged columns. Every load is issued (clamped to a valid address,
         // the value dropped later) before any is used.
         uint4 p0[4], p1[4];
-        uint32_t xi[16], xw[16], aw[16];  // idx (refinement), raw x bits (main), alpha_c bits
+        // idx (refinement), raw x bits (main; for the refinement: idx of the column before each
+        // even element, for the ascending-order check), alpha_c bits
+        uint32_t xi[16], xw[16], aw[16];
         const Rsrc r_ac = rsrc(acr, (uint32_t)sg.Kv * 4u);
         // this row tile's slab of the segment (all slices and bases): below 2 GiB (checked)
         const Rsrc r_w = rsrc(sg.packed + (int64_t)rt * nitems * kTileWords, (uint32_t)nitems * kTileWords * 4u);
@@ -217,7 +226,8 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
                 const uint32_t d = 32u * (uint32_t)(i >> 1) + (uint32_t)(i & 1);
                 aw[i] = ld32(r_ac, 4u * col0 + 4u * d);
                 xi[i] = ld32(r_idx, 4u * col0 + 4u * d);
-                xw[i] = ldx_raw(r_xd, xrow + col0 + d, (XT*)nullptr);
+                if (si) xw[i] = (i & 1) == 0 && col0 + d > 0 ? ld32(r_idx, 4u * (col0 + d - 1u)) : 0u;
+                else xw[i] = ldx_raw(r_xd, xrow + col0 + d, (XT*)nullptr);
             }
         };
         for (int ks = lo; ks < hi; ++ks) {
@@ -226,11 +236,21 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
             {
                 float xv[16];
                 if (si) {  // the gather through idx (the loads wait here, where they are used anyway)
+                    // VCM: each column's index must lie in [0, K) and exceed the one before it
+                    // (ascending, distinct); a column that breaks this reads nothing, contributes
+                    // nothing and sets bit 1 of the workspace's word 0
+                    const int colb = ks * kSliceCols + 2 * cg;
+                    bool bad_any = false;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {  // in range by contract
-                        const int c = xi[i] < (uint64_t)ldx ? (int)xi[i] : (int)ldx - 1;
-                        xv[i] = x_from_raw(ldx_raw(r_xg, xrow + (uint32_t)c, (XT*)nullptr), (XT*)nullptr);
+                    for (int i = 0; i < 16; ++i) {
+                        const int col = colb + 32 * (i >> 1) + (i & 1);
+                        const uint32_t prev = (i & 1) ? xi[i - 1] : xw[i];
+                        const bool bad = col < sg.Kv && (xi[i] >= (uint64_t)ldx || (col > 0 && (int)prev >= (int)xi[i]));
+                        bad_any = bad_any || bad;
+                        const uint32_t off = bad || col >= sg.Kv ? xrow : xrow + xi[i];  // valid; dropped
+                        xv[i] = bad ? 0.f : x_from_raw(ldx_raw(r_xg, off, (XT*)nullptr), (XT*)nullptr);
                     }
+                    if (bad_any && P.err != nullptr) atomicOr(P.err, kWsErrIndex);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) xv[i] = x_from_raw(xw[i], (XT*)nullptr);
@@ -370,24 +390,29 @@ __global__ void k_mm_zero(const MmZero Z) {
 
 }  // namespace
 
-// Workgroups of the instance the device holds at once (CUs x occupancy) and the CU count,
-// queried once per process (benign race: every thread computes the same values).
+// Workgroups of the instance the current device holds at once (CUs x occupancy) and its CU
+// count, cached per device (thread-safe: each entry is written once with the value every thread
+// computes; devices numbered kMaxDevices or above are queried on every call).
 struct MmCapacity {
     int64_t cap, cus;
 };
 template <typename XT>
 static MmCapacity mm_capacity() {
-    static MmCapacity c{-1, -1};
-    if (c.cap < 0) {
-        int cus = 0, dev = 0, per_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+    static std::atomic<int64_t> cache[kMaxDevices];  // cus << 32 | workgroups per CU
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MmCapacity{0, 0};
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    int64_t v = cached ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (v <= 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pm1_mfma<XT, false>, kMmThreads, 0) != hipSuccess)
             return MmCapacity{0, 0};
-        c.cus = cus;
-        c.cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+        v = ((int64_t)cus << 32) | (per_cu > 0 ? per_cu : 1);
+        if (cached) cache[dev].store(v, std::memory_order_relaxed);
     }
-    return c;
+    const int64_t cus = v >> 32;
+    return MmCapacity{cus * (v & 0xFFFFFFFF), cus};
 }
 
 bool mfma_step_supported(const StepArgs& a) {
@@ -420,6 +445,7 @@ hipError_t launch_step_mfma_group(const StepArgs* a, int count, hipStream_t s) {
             }
         }
         P.y = a[i].y;
+        P.err = a[i].ws;
         P.N = a[i].N;
         P.NT = (int)ceil_div(a[i].N, kTileRows);
         P.ST = P.seg[0].KT + P.seg[1].KT;

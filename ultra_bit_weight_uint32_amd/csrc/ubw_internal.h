@@ -32,6 +32,7 @@ constexpr int kTileWords = kTileRows * kSliceWords;  // 2048 words = 8 KiB per b
 constexpr int kThreads = 256;
 constexpr int kMaxGroup = UBW_MAX_GROUP;  // GEMVs per grouped launch
 constexpr int kBatchChunk = 4;          // activation rows per launch (larger batches: several)
+constexpr int kMaxDevices = 64;         // devices whose launch capacities are cached
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -65,9 +66,13 @@ struct StepArgs {
     int tables_only;        // 1: the table kernels at every batch (explicit geometry)
 };
 
-// Workspace of the single-launch y = result mode: a 16-word header (word 0: error flag), then
-// 64 words (256 bytes) per row group (at most one per 256-row tile): the arrival counter at
-// word 0 and the zeroing flag at word 32, on separate cache lines.
+// Workspace of the GEMV calls: a 16-word header, then 64 words (256 bytes) per row group (at
+// most one per 256-row tile) for the single-launch y = result mode: the arrival counter at word
+// 0 and the zeroing flag at word 32, on separate cache lines. Header word 0 collects errors the
+// kernels find: kWsErrWait (a wait for a row group's zeroing gave up; that workgroup added
+// nothing) and kWsErrIndex (a salient index outside [0, K) or not above the one before it).
+constexpr uint32_t kWsErrWait = 1u;
+constexpr uint32_t kWsErrIndex = 2u;
 constexpr int kWsHeaderWords = 16;
 constexpr int kWsRowGroupWords = 64;
 constexpr int kWsFlagOffset = 32;
