@@ -154,8 +154,9 @@ int ubw_lut_gemv_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch,
 int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out);
 
 /*
- * Reads (and with clear != 0 then zeroes) word 0 of a GEMV workspace: waits for `stream` to
- * finish, so it is not for use inside graph capture. *out_word (host) gets the word.
+ * Reads (and with clear != 0 then zeroes) word 0 of a GEMV workspace, or with workspace == NULL
+ * of the static workspace of ubw_lut_gemv_refined_noalloc on the current device: waits for
+ * `stream` to finish, so it is not for use inside graph capture. *out_word (host) gets the word.
  * Returns UBW_OK (no error recorded), UBW_EWAIT (bit 0 set: some outputs were not written),
  * UBW_ERANGE (bit 1 set, bit 0 clear: a salient index was out of range or out of order; the
  * offending columns contributed nothing), or UBW_EINVAL / UBW_EALIGN / UBW_EHIP for the call.
@@ -213,6 +214,25 @@ int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const flo
                          const float* alpha_r_s, const float* alpha_c_s, int ns, int64_t N,
                          int64_t K, int g, const void* x, int x_dtype, int batch, float* y,
                          int accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * ubw_lut_gemv_refined for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid it. The workspace
+ * is a static array inside the library, one per device (65,600 bytes, held until the process
+ * ends), so y = result stays one launch and the call allocates nothing. Arguments and results as
+ * ubw_lut_gemv_refined, without workspace and ws_bytes.
+ *   N            at most 65536 rows (UBW_ERANGE above)
+ * The first call on a device looks up the array's device address (hipGetSymbolAddress, with that
+ * device current), so make it before any graph capture. All calls on one device share the one
+ * array: calls that may overlap on a GPU (other streams, other threads) race and must not be
+ * issued. Its error word is read (and cleared) with ubw_workspace_check(NULL, ...).
+ * Errors: as ubw_lut_gemv_refined, plus UBW_ERANGE (N), UBW_EHIP (the address lookup failed).
+ */
+int ubw_lut_gemv_refined_noalloc(const uint32_t* packed, const float* alpha_r, const float* alpha_c,
+                                 int nb, const int32_t* idx, int64_t s, const uint32_t* packed_s,
+                                 const float* alpha_r_s, const float* alpha_c_s, int ns, int64_t N,
+                                 int64_t K, int g, const void* x, int x_dtype, int batch, float* y,
+                                 int accumulate, void* stream);
 
 /*
  * Group-scale variant: the row scale of the main bases varies along the row, one value per

@@ -71,9 +71,26 @@ def test_workspace_bytes():
 def test_workspace_check_rejects():
     word = ctypes.c_uint32()
     L = ubw.lib()
-    assert L.ubw_workspace_check(None, 0, None, ctypes.byref(word)) == EINVAL
     assert L.ubw_workspace_check(FAKE, 0, None, None) == EINVAL
+    assert L.ubw_workspace_check(None, 0, None, None) == EINVAL
     assert L.ubw_workspace_check(MISALIGNED, 1, None, ctypes.byref(word)) == EALIGN
+
+
+def noalloc_args(**kw):
+    a = dict(packed=FAKE, alpha_r=FAKE, alpha_c=FAKE, nb=2, idx=FAKE, s=10, packed_s=FAKE, alpha_r_s=FAKE,
+             alpha_c_s=FAKE, ns=1, N=4096, K=4096, g=8, x=FAKE, x_dtype=1, batch=1, y=FAKE, accumulate=0, stream=None)
+    a.update(kw)
+    return ubw.lib().ubw_lut_gemv_refined_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=65537), ERANGE), (dict(N=1 << 20), ERANGE), (dict(idx=None), EINVAL), (dict(packed=None), EINVAL),
+    (dict(g=4), EUNSUP), (dict(batch=17), EINVAL), (dict(packed_s=MISALIGNED), EALIGN), (dict(ns=0), EINVAL),
+])
+def test_noalloc_rejects_before_touching_the_device(kw, status):
+    """Every argument check of the allocation-free entry point runs on the host before the static
+    workspace is looked up (no GPU is needed for these)."""
+    assert noalloc_args(**kw) == status
 
 
 def gemv_args(**kw):

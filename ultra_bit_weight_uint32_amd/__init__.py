@@ -29,7 +29,7 @@ MAX_GROUP = 8
 EXPORTS = (
     "ubw_status_str", "ubw_version", "ubw_packed_words", "ubw_pack_bases", "ubw_ternary_encode",
     "ubw_build_lut", "ubw_lut_gemv_workspace_bytes", "ubw_workspace_bytes", "ubw_workspace_check",
-    "ubw_lut_gemv", "ubw_vcm_gather_refine", "ubw_lut_gemv_refined",
+    "ubw_lut_gemv", "ubw_vcm_gather_refine", "ubw_lut_gemv_refined", "ubw_lut_gemv_refined_noalloc",
     "ubw_check_indices", "ubw_extract_patterns", "ubw_lut_gemv_geometry", "ubw_bench_stream_read",
     "ubw_lut_gemv_multi", "ubw_lut_gemv_gs", "ubw_fit_workspace_bytes", "ubw_fit_bases",
     "ubw_gram", "ubw_saliency_workspace_bytes", "ubw_hessian_saliency",
@@ -79,6 +79,7 @@ def lib():
         "ubw_check_indices": ([P, I64, I64], I),
         "ubw_extract_patterns": ([P, I, I64, I64, I, P, P], I),
         "ubw_lut_gemv_refined": ([P, P, P, I, P, I64, P, P, P, I, I64, I64, I, P, I, I, P, I, P, SZ, P], I),
+        "ubw_lut_gemv_refined_noalloc": ([P, P, P, I, P, I64, P, P, P, I, I64, I64, I, P, I, I, P, I, P], I),
         "ubw_lut_gemv_geometry": ([P, P, P, I, I64, I64, P, I64, P, I, I, P, I, I, I, I, P, SZ, P], I),
         "ubw_bench_stream_read": ([P, I64, P, P], I),
         "ubw_lut_gemv_multi": ([ctypes.POINTER(GemvDesc), I, I64, I, P, I, I, I, P], I),
@@ -169,13 +170,13 @@ workspace_bytes = lut_gemv_workspace_bytes
 
 
 def workspace_check(workspace, clear: bool = False):
-    """Word 0 of a GEMV workspace after the current stream's work has finished: returns
-    (status, word), status being UBW_OK, UBW_EWAIT (bit 0: a wait gave up, outputs not written)
-    or UBW_ERANGE (bit 1: a salient index out of range or out of order). clear=True zeroes the
-    word afterwards."""
+    """Word 0 of a GEMV workspace (None: the static workspace of lut_gemv_refined_noalloc on the
+    current device) after the current stream's work has finished: returns (status, word), status
+    being UBW_OK, UBW_EWAIT (bit 0: a wait gave up, outputs not written) or UBW_ERANGE (bit 1: a
+    salient index out of range or out of order). clear=True zeroes the word afterwards."""
     word = ctypes.c_uint32(0)
-    st = lib().ubw_workspace_check(_dev(workspace, "workspace", None), 1 if clear else 0, _stream(),
-                                   ctypes.byref(word))
+    wp = None if workspace is None else _dev(workspace, "workspace", None)
+    st = lib().ubw_workspace_check(wp, 1 if clear else 0, _stream(), ctypes.byref(word))
     if st not in (UBW_OK, UBW_EWAIT, UBW_ERANGE):
         raise UbwError("ubw_workspace_check", st)
     return st, word.value
@@ -325,6 +326,33 @@ def lut_gemv_refined(packed, alpha_r, alpha_c, idx, packed_s, alpha_r_s, alpha_c
                                       _dev(alpha_c_s, "alpha_c_s", F32), ns, n, k, g, _dev(x, "x", None),
                                       _xdtype(x), batch, _dev(y, "y", F32), 1 if accumulate else 0, ws, wsb,
                                       _stream()))
+    return y
+
+
+def lut_gemv_refined_noalloc(packed, alpha_r, alpha_c, idx, packed_s, alpha_r_s, alpha_c_s, x, n: int, k: int, y,
+                             g: int = 8, accumulate: bool = False):
+    """lut_gemv_refined with the library's static workspace (allocates nothing; y is required,
+    n <= 65536). Returns y."""
+    torch = _torch()
+    x = _as_2d(x)
+    batch = x.shape[0]
+    nb, ns, s = alpha_r.shape[0], alpha_r_s.shape[0], idx.shape[0]
+    if x.shape[1] != k or tuple(alpha_r.shape) != (nb, n) or tuple(alpha_c.shape) != (nb, k):
+        raise ValueError("shape mismatch between x, alpha_r, alpha_c and (n, k)")
+    if tuple(alpha_r_s.shape) != (ns, n) or tuple(alpha_c_s.shape) != (ns, s):
+        raise ValueError("shape mismatch between idx, alpha_r_s, alpha_c_s and n")
+    if packed.numel() < packed_words(nb, n, k, g) or packed_s.numel() < packed_words(ns, n, s, g):
+        raise ValueError("packed buffer smaller than packed_words()")
+    if tuple(y.shape) != (batch, n):
+        raise ValueError(f"y must be [{batch}, {n}]")
+    F32 = (torch.float32,)
+    _check("ubw_lut_gemv_refined_noalloc",
+           lib().ubw_lut_gemv_refined_noalloc(_dev(packed, "packed", _words_dtypes()), _dev(alpha_r, "alpha_r", F32),
+                                              _dev(alpha_c, "alpha_c", F32), nb, _dev(idx, "idx", (torch.int32,)), s,
+                                              _dev(packed_s, "packed_s", _words_dtypes()),
+                                              _dev(alpha_r_s, "alpha_r_s", F32), _dev(alpha_c_s, "alpha_c_s", F32), ns,
+                                              n, k, g, _dev(x, "x", None), _xdtype(x), batch, _dev(y, "y", F32),
+                                              1 if accumulate else 0, _stream()))
     return y
 
 

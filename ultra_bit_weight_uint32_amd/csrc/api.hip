@@ -160,7 +160,12 @@ int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* 
 }
 
 int ubw_workspace_check(void* workspace, int clear, void* stream, uint32_t* out_word) {
-    if (!workspace || !out_word) return UBW_EINVAL;
+    if (!out_word) return UBW_EINVAL;
+    if (!workspace) {  // the static workspace of ubw_lut_gemv_refined_noalloc on the current device
+        uint32_t* p = nullptr;
+        if (scratch_address(&p) != hipSuccess) return UBW_EHIP;
+        workspace = p;
+    }
     if (!aligned16(workspace)) return UBW_EALIGN;
     hipStream_t st = as_stream(stream);
     uint32_t word = 0;
@@ -229,6 +234,24 @@ int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const flo
     a.seg[1] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
     a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(K, nb) + units_of(s, ns), batch);
     return run_step(a, stream);
+}
+
+int ubw_lut_gemv_refined_noalloc(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb,
+                                 const int32_t* idx, int64_t s, const uint32_t* packed_s, const float* alpha_r_s,
+                                 const float* alpha_c_s, int ns, int64_t N, int64_t K, int g, const void* x,
+                                 int x_dtype, int batch, float* y, int accumulate, void* stream) {
+    // every check that needs no device first, so that rejected calls touch nothing
+    int st = validate_gemv_common(packed, alpha_r, alpha_c, nb, N, K, x, x_dtype, batch, y);
+    if (st != UBW_OK) return st;
+    if (!idx) return UBW_EINVAL;
+    if ((st = validate_gemv_common(packed_s, alpha_r_s, alpha_c_s, ns, N, s, x, x_dtype, batch, y)) != UBW_OK)
+        return st;
+    if (g != 8) return UBW_EUNSUPPORTED;
+    if (N > kScratchMaxRows) return UBW_ERANGE;
+    uint32_t* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return UBW_EHIP;
+    return ubw_lut_gemv_refined(packed, alpha_r, alpha_c, nb, idx, s, packed_s, alpha_r_s, alpha_c_s, ns, N, K, g, x,
+                                x_dtype, batch, y, accumulate, ws, (size_t)kScratchWords * 4, stream);
 }
 
 int ubw_lut_gemv_gs(const uint32_t* packed, const uint16_t* alpha_rg, const float* alpha_c, int nb, int gsize,

@@ -1053,6 +1053,30 @@ __global__ __launch_bounds__(kStepThreads, (kMinWaves<RPL, BMAX, false>)) void k
 }
 
 // ---------------------------------------------------------------------------------------
+// The GEMV workspace of ubw_lut_gemv_refined_noalloc, for callers that cannot allocate: one
+// static array per device, zero when the code object is loaded and kept consistent by every
+// call (the counters of at most kScratchRowGroups row groups; header word 0 the error word).
+// Host code reaches it only through the device address that scratch_address() looks up once per
+// device.
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+hipError_t scratch_address(uint32_t** out) {
+    static std::atomic<uint32_t*> addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    uint32_t* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {  // first call on this device (which is current): look the array up
+        e = hipGetSymbolAddress(reinterpret_cast<void**>(&p), HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------------------
 // Streaming read with the GEMV's access shape (measurement helper).
 
 __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ p, int64_t n16, uint32_t* out) {

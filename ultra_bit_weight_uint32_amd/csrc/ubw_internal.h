@@ -78,6 +78,13 @@ constexpr int kWsRowGroupWords = 64;
 constexpr int kWsFlagOffset = 32;
 inline int64_t step_workspace_words(int64_t N) { return kWsHeaderWords + kWsRowGroupWords * ceil_div(N, kTileRows); }
 
+// The static workspace of ubw_lut_gemv_refined_noalloc: the counters of up to 256 row groups
+// (N <= 65536 rows), 65,600 bytes per device; scratch_address() gives this device's copy.
+constexpr int kScratchRowGroups = 256;
+constexpr int64_t kScratchMaxRows = (int64_t)kScratchRowGroups * kTileRows;
+constexpr int kScratchWords = kWsHeaderWords + kWsRowGroupWords * kScratchRowGroups;
+hipError_t scratch_address(uint32_t** out);
+
 hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t s);
 hipError_t launch_pack(const void* src, int src_fmt, int nb, int N, int K, uint32_t* dst, hipStream_t s);
 hipError_t launch_ternary(const int8_t* w, const float* scale, int N, int K, uint32_t* packed,
