@@ -148,7 +148,9 @@ int ubw_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, i
  * ubw_workspace_check): bit 0 (UBW_EWAIT) a wait gave up and that workgroup added nothing
  * (a safety net; the protocol above makes it unreachable), bit 1 (UBW_ERANGE) a salient index
  * outside [0, K) or not above the index before it. Calls with a workspace set these bits and
- * never clear them. Errors: UBW_EINVAL (null, sizes, batch), UBW_EUNSUPPORTED (g != 8).
+ * never clear them. At g = 4 (whole rows per workgroup, no cross-workgroup sums) only the
+ * 16-word header is used: *out = 64.
+ * Errors: UBW_EINVAL (null, sizes, batch), UBW_EUNSUPPORTED (g not 4 or 8).
  */
 int ubw_lut_gemv_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out);
 int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out);
@@ -165,17 +167,26 @@ int ubw_workspace_check(void* workspace, int clear, void* stream, uint32_t* out_
 
 /*
  * Main GEMV: y (= or +=) sum_k alpha_r^(k) (.) (B^(k) (alpha_c^(k) (.) x)), for every
- * activation row. Tables are built per 256-column slice in LDS (LUT-BSF), pattern indices
- * are read from the packed words with byte-permute operations, and alpha_r is applied to
- * each row's partial sum; slices of one row are combined with fp32 atomics, so the
- * summation order (not the result beyond rounding) varies between runs.
- *   packed       from ubw_pack_bases(nb, N, K, g=8)
+ * activation row, with tables of g columns (LUT-BSF; section "2. Kernel innovation").
+ *   g = 8: tables of 256 entries per 8 columns, built per 256-column slice in LDS; pattern
+ *          indices are read from the packed words with byte-permute operations and alpha_r is
+ *          applied to each row's partial sum; slices of one row are combined with fp32 atomics,
+ *          so the summation order (not the result beyond rounding) varies between runs.
+ *   g = 4: tables of 16 entries per 4 columns for the whole row in LDS (16 bytes per column and
+ *          base); a workgroup owns 16 complete rows and writes each output once with a plain
+ *          store (fixed summation order, no workspace needed). The tables and the fp32 copy of
+ *          x must fit 156 KiB: main nb in {1, 2, 4} with nb * K <= 8192 (nb = 1: K up to ~6000),
+ *          refinement ns in {1, 2, 4} with ns * ceil(s / 256) in {1, 2, 4}; other shapes are
+ *          UBW_EUNSUPPORTED (never switched to g = 8).
+ *   Both widths read the same packed layout.
+ *   packed       from ubw_pack_bases(nb, N, K, g)
  *   accumulate   0: y = result; 1: y += result
  *   workspace    ubw_workspace_bytes() bytes, or NULL with ws_bytes == 0 (see there)
  * Errors: UBW_EINVAL (null, nb < 1, N < 1, K < 1, batch not in [1, UBW_MAX_BATCH], workspace
- *         NULL with ws_bytes != 0), UBW_EUNSUPPORTED (g != 8, dtype, or an operand of 2 GiB or
- *         more: the kernel addresses each operand with 32-bit offsets), UBW_EALIGN (packed or
- *         workspace), UBW_ESIZE (ws_bytes too small), UBW_EHIP.
+ *         NULL with ws_bytes != 0), UBW_EUNSUPPORTED (g not 4 or 8, a g = 4 shape that does
+ *         not fit, dtype, or an operand of 2 GiB or more: the kernels address each operand
+ *         with 32-bit offsets), UBW_EALIGN (packed or workspace), UBW_ESIZE (ws_bytes too
+ *         small), UBW_EHIP.
  */
 int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb,
                  int64_t N, int64_t K, int g, const void* x, int x_dtype, int batch,
@@ -188,7 +199,7 @@ int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alph
  * gathered while the tables are built, and the same LUT-GEMV runs over it:
  * y[b][r] += sum_{k<ns} alpha_r_s[k][r] * sum_{q<s} B_s^(k)[r][q] * alpha_c_s[k][q] * x[b][idx[q]].
  *   idx          int32 [s], strictly ascending, each in [0, K)
- *   packed_s     from ubw_pack_bases(ns, N, s, g=8) of the refinement bases [ns][N][s]
+ *   packed_s     from ubw_pack_bases(ns, N, s, g) of the refinement bases [ns][N][s]
  *   alpha_r_s    fp32 [ns][N];  alpha_c_s fp32 [ns][s]
  *   K            columns of x (the activation row length)
  * The kernels check idx on the device as they gather: a position q whose idx[q] lies outside
@@ -221,7 +232,8 @@ int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const flo
  * is a static array inside the library, one per device (65,600 bytes, held until the process
  * ends), so y = result stays one launch and the call allocates nothing. Arguments and results as
  * ubw_lut_gemv_refined, without workspace and ws_bytes.
- *   N            at most 65536 rows (UBW_ERANGE above)
+ *   N            at most 65536 rows at g = 8 (UBW_ERANGE above); g = 4 uses only the array's
+ *                error word and takes any N
  * The first call on a device looks up the array's device address (hipGetSymbolAddress, with that
  * device current), so make it before any graph capture. All calls on one device share the one
  * array: calls that may overlap on a GPU (other streams, other threads) race and must not be
@@ -289,9 +301,9 @@ typedef struct ubw_gemv_desc {
  * overlapping outputs. Section "2. Kernel innovation" (unified kernel execution) carried over
  * to GEMVs that share x.
  *   descs        HOST array of count descriptors, 1 <= count <= UBW_MAX_GROUP
- *   K, g, x, x_dtype, batch, accumulate   shared by all, as ubw_lut_gemv
+ *   K, g, x, x_dtype, batch, accumulate   shared by all, as ubw_lut_gemv (g = 8 only)
  * Errors: UBW_EINVAL (count out of range, null descs, or any desc invalid as in the single
- *         calls), otherwise as ubw_lut_gemv.
+ *         calls), UBW_EUNSUPPORTED (g != 8), otherwise as ubw_lut_gemv.
  */
 int ubw_lut_gemv_multi(const ubw_gemv_desc* descs, int count, int64_t K, int g, const void* x,
                        int x_dtype, int batch, int accumulate, void* stream);

@@ -64,7 +64,8 @@ def test_workspace_bytes():
     for fn in (L.ubw_lut_gemv_workspace_bytes, L.ubw_workspace_bytes):
         assert fn(2, 4096, 4096, 8, 1, ctypes.byref(sz)) == 0 and sz.value == 4 * (16 + 64 * 16)
         assert fn(2, 4096, 4096, 8, 17, ctypes.byref(sz)) == EINVAL
-        assert fn(2, 4096, 4096, 4, 1, ctypes.byref(sz)) == EUNSUP
+        assert fn(2, 4096, 4096, 4, 1, ctypes.byref(sz)) == 0 and sz.value == 4 * 16  # g = 4: header only
+        assert fn(2, 4096, 4096, 5, 1, ctypes.byref(sz)) == EUNSUP
         assert fn(2, 4096, 4096, 8, 1, None) == EINVAL
 
 
@@ -85,7 +86,8 @@ def noalloc_args(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(N=65537), ERANGE), (dict(N=1 << 20), ERANGE), (dict(idx=None), EINVAL), (dict(packed=None), EINVAL),
-    (dict(g=4), EUNSUP), (dict(batch=17), EINVAL), (dict(packed_s=MISALIGNED), EALIGN), (dict(ns=0), EINVAL),
+    (dict(g=2), EUNSUP), (dict(batch=17), EINVAL), (dict(packed_s=MISALIGNED), EALIGN), (dict(ns=0), EINVAL),
+    (dict(g=4, K=40000), EUNSUP), (dict(g=4, s=600), EUNSUP), (dict(g=4, nb=3), EUNSUP),
 ])
 def test_noalloc_rejects_before_touching_the_device(kw, status):
     """Every argument check of the allocation-free entry point runs on the host before the static
@@ -104,8 +106,12 @@ def gemv_args(**kw):
     (dict(packed=None), EINVAL), (dict(alpha_r=None), EINVAL), (dict(alpha_c=None), EINVAL),
     (dict(x=None), EINVAL), (dict(y=None), EINVAL), (dict(nb=0), EINVAL), (dict(N=0), EINVAL),
     (dict(K=0), EINVAL), (dict(N=-5), EINVAL), (dict(batch=0), EINVAL), (dict(batch=17), EINVAL),
-    (dict(x_dtype=7), EUNSUP), (dict(g=4), EUNSUP), (dict(g=5), EUNSUP), (dict(packed=MISALIGNED), EALIGN),
+    (dict(x_dtype=7), EUNSUP), (dict(g=2), EUNSUP), (dict(g=5), EUNSUP), (dict(packed=MISALIGNED), EALIGN),
     (dict(ws=None, wsb=8), EINVAL), (dict(ws=MISALIGNED, wsb=4096), EALIGN), (dict(ws=FAKE, wsb=8), ESIZE),
+    # group width 4: tables of the whole row in LDS (K = 40000 does not fit), 1, 2 or 4 bases,
+    # a workspace of at least the 16 header words
+    (dict(g=4, K=40000), EUNSUP), (dict(g=4, K=8192, nb=1), EUNSUP), (dict(g=4, nb=3), EUNSUP),
+    (dict(g=4, ws=FAKE, wsb=32), ESIZE),
 ])
 def test_lut_gemv_rejects(kw, status):
     assert gemv_args(**kw) == status
@@ -113,7 +119,8 @@ def test_lut_gemv_rejects(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(idx=None), EINVAL), (dict(s=0), EINVAL), (dict(packed_s=None), EINVAL), (dict(ns=0), EINVAL),
-    (dict(K=0), EINVAL), (dict(g=4), EUNSUP), (dict(batch=0), EINVAL), (dict(packed_s=MISALIGNED), EALIGN),
+    (dict(K=0), EINVAL), (dict(g=2), EUNSUP), (dict(batch=0), EINVAL), (dict(packed_s=MISALIGNED), EALIGN),
+    (dict(g=4, s=600), EUNSUP), (dict(g=4, ns=3), EUNSUP),
 ])
 def test_vcm_rejects(kw, status):
     a = dict(idx=FAKE, s=10, packed_s=FAKE, alpha_r_s=FAKE, alpha_c_s=FAKE, ns=2, N=64, K=64, g=8, x=FAKE,
@@ -144,7 +151,8 @@ def test_refined_rejects():
     args = dict(packed=FAKE, ar=FAKE, ac=FAKE, nb=2, idx=FAKE, s=10, packed_s=FAKE, ar_s=FAKE, ac_s=FAKE, ns=2,
                 N=64, K=64, g=8, x=FAKE, x_dtype=1, batch=1, y=FAKE, acc=0, ws=None, wsb=0, stream=None)
     for kw, status in [(dict(idx=None), EINVAL), (dict(s=0), EINVAL), (dict(ns=0), EINVAL), (dict(nb=0), EINVAL),
-                       (dict(packed_s=MISALIGNED), EALIGN), (dict(g=4), EUNSUP), (dict(ws=FAKE, wsb=4), ESIZE),
+                       (dict(packed_s=MISALIGNED), EALIGN), (dict(g=2), EUNSUP), (dict(ws=FAKE, wsb=4), ESIZE),
+                       (dict(g=4, s=600), EUNSUP), (dict(g=4, K=40000), EUNSUP),
                        (dict(batch=17), EINVAL)]:
         a = dict(args)
         a.update(kw)

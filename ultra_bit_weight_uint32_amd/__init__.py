@@ -18,8 +18,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBPATH = os.path.join(_HERE, "libubw.so")
 
 UBW_OK = 0
+UBW_EINVAL, UBW_EUNSUPPORTED, UBW_EALIGN = -1, -2, -3
 UBW_ERANGE = -4
-UBW_EWAIT = -7
+UBW_EHIP, UBW_ESIZE, UBW_EWAIT = -5, -6, -7
 UBW_F32, UBW_F16 = 0, 1
 UBW_SRC_CANON_BITS, UBW_SRC_INT8_SIGNS = 0, 1
 MAX_BATCH = 16

@@ -11,7 +11,7 @@ using namespace ubw;
 
 namespace {
 
-constexpr int kVersion = 7;
+constexpr int kVersion = 8;
 constexpr int kMaxFitIters = 10000;
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -93,6 +93,28 @@ int run_step(StepArgs& a, void* stream) {
     return hip_status(launch_step(a, as_stream(stream)));
 }
 
+// Group width 4 runs the whole-row kernel, which needs no counters: a workspace, when given,
+// only receives the error bits in its header (16 words). Group width 8 needs the counters of
+// every row group for its single-launch y = result mode.
+int check_workspace_g(void* ws, size_t ws_bytes, int64_t N, int g, uint32_t** out) {
+    if (g != 4) return check_workspace(ws, ws_bytes, N, out);
+    *out = nullptr;
+    if (ws == nullptr) return ws_bytes == 0 ? UBW_OK : UBW_EINVAL;
+    if (!aligned16(ws)) return UBW_EALIGN;
+    if (ws_bytes < (size_t)kWsHeaderWords * 4) return UBW_ESIZE;
+    *out = static_cast<uint32_t*>(ws);
+    return UBW_OK;
+}
+
+// A step at group width g (4 or 8, checked by the caller). Shapes whose group-4 tables do not
+// fit one workgroup's LDS are refused at g = 4 (UBW_EUNSUPPORTED): the caller chooses g, so
+// nothing silently switches width.
+int run_step_g(StepArgs& a, int g, void* stream) {
+    if (g != 4) return run_step(a, stream);
+    if (!rows4_supported(a)) return UBW_EUNSUPPORTED;
+    return hip_status(launch_rows4(a, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -150,8 +172,8 @@ int ubw_build_lut(const void* x, int x_dtype, int batch, const float* alpha_c, i
 
 int ubw_lut_gemv_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* out) {
     if (!out || nb < 1 || !fits_int(N) || !fits_int(K) || batch < 1 || batch > UBW_MAX_BATCH) return UBW_EINVAL;
-    if (g != 8) return UBW_EUNSUPPORTED;
-    *out = (size_t)step_workspace_words(N) * 4;
+    if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
+    *out = g == 4 ? (size_t)kWsHeaderWords * 4 : (size_t)step_workspace_words(N) * 4;
     return UBW_OK;
 }
 
@@ -189,14 +211,14 @@ int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alph
                  void* workspace, size_t ws_bytes, void* stream) {
     int st = validate_gemv_common(packed, alpha_r, alpha_c, nb, N, K, x, x_dtype, batch, y);
     if (st != UBW_OK) return st;
-    if (g != 8) return UBW_EUNSUPPORTED;
+    if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
     uint32_t* ws = nullptr;
-    if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
+    if ((st = check_workspace_g(workspace, ws_bytes, N, g, &ws)) != UBW_OK) return st;
     StepArgs a = make_step(N, x, x_dtype, K, batch, y, accumulate, ws);
     a.nseg = 1;
     a.seg[0] = make_segment(packed, alpha_r, alpha_c, nullptr, nb, K);
     a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(K, nb), batch);
-    return run_step(a, stream);
+    return run_step_g(a, g, stream);
 }
 
 int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_s, const float* alpha_r_s,
@@ -206,14 +228,14 @@ int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_
     int st = validate_gemv_common(packed_s, alpha_r_s, alpha_c_s, ns, N, s, x, x_dtype, batch, y);
     if (st != UBW_OK) return st;
     if (!fits_int(K)) return UBW_EINVAL;
-    if (g != 8) return UBW_EUNSUPPORTED;
+    if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
     uint32_t* ws = nullptr;
-    if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
+    if ((st = check_workspace_g(workspace, ws_bytes, N, g, &ws)) != UBW_OK) return st;
     StepArgs a = make_step(N, x, x_dtype, K, batch, y, 1, ws);
     a.nseg = 2;
     a.seg[1] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
     a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(s, ns), batch);
-    return run_step(a, stream);
+    return run_step_g(a, g, stream);
 }
 
 int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb,
@@ -225,15 +247,15 @@ int ubw_lut_gemv_refined(const uint32_t* packed, const float* alpha_r, const flo
     if (!idx) return UBW_EINVAL;
     if ((st = validate_gemv_common(packed_s, alpha_r_s, alpha_c_s, ns, N, s, x, x_dtype, batch, y)) != UBW_OK)
         return st;
-    if (g != 8) return UBW_EUNSUPPORTED;
+    if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
     uint32_t* ws = nullptr;
-    if ((st = check_workspace(workspace, ws_bytes, N, &ws)) != UBW_OK) return st;
+    if ((st = check_workspace_g(workspace, ws_bytes, N, g, &ws)) != UBW_OK) return st;
     StepArgs a = make_step(N, x, x_dtype, K, batch, y, accumulate, ws);
     a.nseg = 2;
     a.seg[0] = make_segment(packed, alpha_r, alpha_c, nullptr, nb, K);
     a.seg[1] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
     a.rows_per_group = choose_rows(ceil_div(N, kTileRows), units_of(K, nb) + units_of(s, ns), batch);
-    return run_step(a, stream);
+    return run_step_g(a, g, stream);
 }
 
 int ubw_lut_gemv_refined_noalloc(const uint32_t* packed, const float* alpha_r, const float* alpha_c, int nb,
@@ -246,8 +268,15 @@ int ubw_lut_gemv_refined_noalloc(const uint32_t* packed, const float* alpha_r, c
     if (!idx) return UBW_EINVAL;
     if ((st = validate_gemv_common(packed_s, alpha_r_s, alpha_c_s, ns, N, s, x, x_dtype, batch, y)) != UBW_OK)
         return st;
-    if (g != 8) return UBW_EUNSUPPORTED;
-    if (N > kScratchMaxRows) return UBW_ERANGE;
+    if (g != 8 && g != 4) return UBW_EUNSUPPORTED;
+    if (g == 8 && N > kScratchMaxRows) return UBW_ERANGE;  // g = 4 uses the header only
+    if (g == 4) {
+        StepArgs a = make_step(N, x, x_dtype, K, batch, y, accumulate, nullptr);
+        a.nseg = 2;
+        a.seg[0] = make_segment(packed, alpha_r, alpha_c, nullptr, nb, K);
+        a.seg[1] = make_segment(packed_s, alpha_r_s, alpha_c_s, idx, ns, s);
+        if (!rows4_supported(a)) return UBW_EUNSUPPORTED;
+    }
     uint32_t* ws = nullptr;
     if (scratch_address(&ws) != hipSuccess) return UBW_EHIP;
     return ubw_lut_gemv_refined(packed, alpha_r, alpha_c, nb, idx, s, packed_s, alpha_r_s, alpha_c_s, ns, N, K, g, x,

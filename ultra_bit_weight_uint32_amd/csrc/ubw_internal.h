@@ -118,6 +118,13 @@ hipError_t launch_step_mfma(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_mfma_group(const StepArgs* a, int count, hipStream_t s);
 // Whether every buffer of a step is small enough for the kernel's 32-bit buffer offsets.
 bool step_buffers_fit(const StepArgs& a);
+// Group width 4 (rows4.hip): 16 whole rows per workgroup with all of a row's tables in LDS, one
+// plain store per output. Needs main and refinement with 1, 2 or 4 bases, a refinement of at
+// whose ns x tiles is 1, 2 or 4 (32 chunks of 8, 16 or 32 columns), and the
+// tables + fp32 activations within 156 KiB of LDS (2 bases: K <= 4096 with a refinement of at
+// most 256 columns in 2 bases or 512 in 1); a.ws only takes error bits.
+bool rows4_supported(const StepArgs& a);
+hipError_t launch_rows4(const StepArgs& a, hipStream_t s);
 
 // Hessian-guided saliency (saliency.hip).
 hipError_t launch_gram(const void* x, int T, int K, float scale, float* H, hipStream_t s);
