@@ -188,10 +188,14 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
         }
     };
 
-    // ---- every load offset first (no load in flight yet), then the loads in the order they
-    // are needed: x (staging), alpha_c and the refinement's indices and scales (table builds),
-    // alpha_r and the weights (lookups); a wait for one of them leaves the later ones in flight
-    //
+    // ---- loads, in the order they are needed: x (staging; first, so that every wave has it in
+    // flight before the address arithmetic), alpha_c and the refinement's indices and scales
+    // (table builds), alpha_r and the weights (lookups); a wait for one of them leaves the later
+    // ones in flight. (Offsets use 24-bit multiplies: a 32 x 32 multiply-add may be compiled to a
+    // 64-bit one whose unused high input is any register, possibly one a load is still to write,
+    // which forces an early wait.)
+    prefetch(0);
+
     // main build role: thread t < 8 G0 builds the tables of group gi = t / 8 of chunks 4 qd ..
     // 4 qd + 3, qd = t % 8: the 8 lanes of each LDS pass write 8 different bank quadruples. Per
     // chunk: alpha_c of the group's 4 columns and the LDS address of their staged x (the zero pad
@@ -199,40 +203,54 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
     const int gi = tid >> 3, qd = tid & 7;
     const bool mb = S0.nb > 0 && gi < S0.G;
     const uint32_t xpad = P.xs_off + 4u * xpos(P.K4, P.xsh);
-    uint32_t ao[4][4], xa[4];
+    uint4 acm[4];
+    uint32_t xa[4];
+    {
+        const Rsrc r = rsrc4(S0.alpha_c, (uint32_t)S0.nb * (uint32_t)S0.Kv * 4u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int cb = 4 * qd + j, kb = cb >> S0.lcpb;
-        const int col = (cb & (S0.cpb - 1)) * S0.C + 4 * gi;
-        const bool in = mb && col < S0.Kv;
-        const uint32_t o = ((uint32_t)kb * (uint32_t)S0.Kv + (uint32_t)col) * 4u;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) ao[j][t] = in && col + t < S0.Kv ? o + 4u * (uint32_t)t : kR4Oob;
-        xa[j] = in ? P.xs_off + 4u * xpos((uint32_t)col, P.xsh) : xpad;
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t cb = (uint32_t)(4 * qd + j), kb = cb >> S0.lcpb;
+            const uint32_t col = __umul24(cb & (uint32_t)(S0.cpb - 1), (uint32_t)S0.C) + 4u * (uint32_t)gi;
+            const bool in = mb && col < (uint32_t)S0.Kv;
+            const uint32_t o = (__umul24(kb, (uint32_t)S0.Kv) + col) * 4u;
+            if constexpr (AV) {  // K a multiple of 4 and alpha_c 16-byte aligned: one load per group
+                acm[j] = ld128(r, in ? o : kR4Oob);
+            } else {
+                acm[j].x = ld32(r, in ? o : kR4Oob);
+                acm[j].y = ld32(r, in && col + 1u < (uint32_t)S0.Kv ? o + 4u : kR4Oob);
+                acm[j].z = ld32(r, in && col + 2u < (uint32_t)S0.Kv ? o + 8u : kR4Oob);
+                acm[j].w = ld32(r, in && col + 3u < (uint32_t)S0.Kv ? o + 12u : kR4Oob);
+            }
+            xa[j] = in ? P.xs_off + 4u * xpos(col, P.xsh) : xpad;
+        }
     }
-    // refinement build role: thread 511 - t, t < 8 G1 (the last wave), builds group gj = t / 8 of
-    // chunks 4 qe .. 4 qe + 3, qe = t % 8; per chunk its 4 virtual columns' idx, the idx before
-    // the first (order check) and alpha_c_s
+    // refinement build role: one table per thread, on the last waves: thread 511 - t, t < 32 G1,
+    // builds the table of group gj = t / 32 of chunk ce = t % 32 from its 4 virtual columns (their
+    // idx, the idx before the first for the order check, and alpha_c_s)
     const int tr = kR4Threads - 1 - tid;
-    const int gj = tr >> 3, qe = tr & 7;
+    const int ce = tr & 31, gj = tr >> 5;
     const bool rb = S1.nb > 0 && gj < S1.G;
-    uint32_t ix[4][4], ixp[4], acs[4][4];
-    uint32_t io[4][4], so[4][4], po[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int cb = 4 * qe + j, kb = cb >> S1.lcpb;
-        const int q0 = (cb & (S1.cpb - 1)) * S1.C + 4 * gj;
+    uint32_t ix[4] = {0u, 0u, 0u, 0u}, acs[4] = {0u, 0u, 0u, 0u}, ixp = 0u;
+    const uint32_t q0 = __umul24((uint32_t)ce & (uint32_t)(S1.cpb - 1), (uint32_t)S1.C) + 4u * (uint32_t)gj;
+    if (rb) {  // the last waves only (the others skip this)
+        const Rsrc ri = rsrc4(S1.idx, (uint32_t)S1.Kv * 4u);
+        const Rsrc ra = rsrc4(S1.alpha_c, (uint32_t)S1.nb * (uint32_t)S1.Kv * 4u);
+        const uint32_t sb = __umul24((uint32_t)ce >> S1.lcpb, (uint32_t)S1.Kv);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int q = q0 + t;
-            io[j][t] = rb && q < S1.Kv ? 4u * (uint32_t)q : kR4Oob;
-            so[j][t] = rb && q < S1.Kv ? ((uint32_t)kb * (uint32_t)S1.Kv + (uint32_t)q) * 4u : kR4Oob;
+            const uint32_t q = q0 + (uint32_t)t;
+            ix[t] = ld32(ri, q < (uint32_t)S1.Kv ? 4u * q : kR4Oob);
+            acs[t] = ld32(ra, q < (uint32_t)S1.Kv ? 4u * (sb + q) : kR4Oob);
         }
-        po[j] = rb && q0 > 0 && q0 <= S1.Kv ? 4u * (uint32_t)(q0 - 1) : kR4Oob;
+        ixp = ld32(ri, q0 > 0u && q0 <= (uint32_t)S1.Kv ? 4u * (q0 - 1u) : kR4Oob);
     }
     // alpha_r of the lane's chunks
-    const uint32_t aro0 = S0.nb > 0 && row < P.N ? ((uint32_t)k0_of(lane, S0) * (uint32_t)P.N + (uint32_t)row) * 4u : kR4Oob;
-    const uint32_t aro1 = S1.nb > 0 && row < P.N ? ((uint32_t)k0_of(lane, S1) * (uint32_t)P.N + (uint32_t)row) * 4u : kR4Oob;
+    const uint32_t aro0 =
+        S0.nb > 0 && row < P.N ? (__umul24((uint32_t)k0_of(lane, S0), (uint32_t)P.N) + (uint32_t)row) * 4u : kR4Oob;
+    const uint32_t aro1 =
+        S1.nb > 0 && row < P.N ? (__umul24((uint32_t)k0_of(lane, S1), (uint32_t)P.N) + (uint32_t)row) * 4u : kR4Oob;
+    const float ar0 = __uint_as_float(ld32(rsrc4(S0.alpha_r, (uint32_t)S0.nb * (uint32_t)P.N * 4u), aro0));
+    const float ar1 = __uint_as_float(ld32(rsrc4(S1.alpha_r, (uint32_t)S1.nb * (uint32_t)P.N * 4u), aro1));
     // main chunk: base k0, columns [cib0 C, cib0 C + C), canonical words [w0, w0 + CW) of the row.
     // The lane loads the stored slots that hold them (canonical word w of a slice is slot w ^ a):
     // MW = min(CW, 8) words per slice, element m of a slice's load holding the chunk's word m ^ am
@@ -240,8 +258,9 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
     constexpr int MW = CW < 8 ? CW : 8;
     constexpr int NS = CW / MW;
     const int am = a & (MW - 1);
-    uint32_t wo[NS][2];
+    uint32_t wm[CW];
     {
+        const Rsrc r = rsrc4(S0.packed, (uint32_t)S0.nb * (uint32_t)P.NT * (uint32_t)S0.KT * kTileWords * 4u);
         const int k0 = k0_of(lane, S0);
         const int w0 = (S0.nb > 0 ? lane & (S0.cpb - 1) : 0) * CW;  // first canonical word of the chunk
 #pragma unroll
@@ -250,113 +269,57 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
             const bool ok = S0.nb > 0 && row < P.N && ks < S0.KT;
             const uint32_t o = ok ? slice_off(S0, row, ks, k0) : 0u;
             if constexpr (MW == 8) {  // both 16-byte halves of the slice
-                wo[j][0] = ok ? o : kR4Oob;
-                wo[j][1] = ok ? o + (uint32_t)kTileRows * 16u : kR4Oob;
+                const uint4 h0 = ld128(r, ok ? o : kR4Oob);
+                const uint4 h1 = ld128(r, ok ? o + (uint32_t)kTileRows * 16u : kR4Oob);
+                wm[8 * j + 0] = h0.x; wm[8 * j + 1] = h0.y; wm[8 * j + 2] = h0.z; wm[8 * j + 3] = h0.w;
+                wm[8 * j + 4] = h1.x; wm[8 * j + 5] = h1.y; wm[8 * j + 6] = h1.z; wm[8 * j + 7] = h1.w;
             } else {  // the MW slots of the chunk's words: an aligned run inside one half
                 const int slot = ((w0 & 7) ^ a) & ~(MW - 1);
-                wo[j][0] = ok ? o + (uint32_t)(slot >> 2) * (uint32_t)kTileRows * 16u + 4u * (uint32_t)(slot & 3) : kR4Oob;
-                wo[j][1] = kR4Oob;
+                const uint32_t oo =
+                    ok ? o + (uint32_t)(slot >> 2) * (uint32_t)kTileRows * 16u + 4u * (uint32_t)(slot & 3) : kR4Oob;
+                if constexpr (MW == 4) {
+                    const uint4 h = ld128(r, oo);
+                    wm[0] = h.x; wm[1] = h.y; wm[2] = h.z; wm[3] = h.w;
+                } else if constexpr (MW == 2) {
+                    const uint2 h = ld64(r, oo);
+                    wm[0] = h.x; wm[1] = h.y;
+                } else {
+                    wm[0] = ld32(r, oo);
+                }
             }
         }
     }
     // refinement chunk: base k1, virtual columns [c1, c1 + Cs) inside canonical word wi of slice
     // ks (Cs <= 32 and divides 32): one stored slot, wi ^ a
     const int c1 = (S1.nb > 0 ? lane & (S1.cpb - 1) : 0) * S1.C;  // first virtual column of the chunk
-    uint32_t wro;
+    uint32_t Wr0;
     {
         const int ks = c1 >> 8, slot = ((c1 & 255) >> 5) ^ a;
         const bool ok = S1.nb > 0 && row < P.N && ks < S1.KT;
-        wro = ok ? slice_off(S1, row, ks, k0_of(lane, S1)) + (uint32_t)(slot >> 2) * (uint32_t)kTileRows * 16u +
-                       4u * (uint32_t)(slot & 3)
-                 : kR4Oob;
+        Wr0 = ld32(rsrc4(S1.packed, (uint32_t)S1.nb * (uint32_t)P.NT * (uint32_t)S1.KT * kTileWords * 4u),
+                   ok ? slice_off(S1, row, ks, k0_of(lane, S1)) + (uint32_t)(slot >> 2) * (uint32_t)kTileRows * 16u +
+                            4u * (uint32_t)(slot & 3)
+                      : kR4Oob);
     }
-    // (the offsets are computed here, before any load: none of them may need a register that a
-    // load in flight is still to write)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(ao[j][t]), "+v"(io[j][t]), "+v"(so[j][t]));
-        asm volatile("" : "+v"(po[j]), "+v"(xa[j]));
-    }
-#pragma unroll
-    for (int j = 0; j < NS; ++j) asm volatile("" : "+v"(wo[j][0]), "+v"(wo[j][1]));
-    asm volatile("" : "+v"(wro));
-
-    prefetch(0);
-    uint4 acm[4];
-    {
-        const Rsrc r = rsrc4(S0.alpha_c, (uint32_t)S0.nb * (uint32_t)S0.Kv * 4u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (AV) {  // K a multiple of 4 and alpha_c 16-byte aligned: one load per group
-                acm[j] = ld128(r, ao[j][0]);
-            } else {
-                acm[j].x = ld32(r, ao[j][0]);
-                acm[j].y = ld32(r, ao[j][1]);
-                acm[j].z = ld32(r, ao[j][2]);
-                acm[j].w = ld32(r, ao[j][3]);
-            }
-        }
-    }
-    if (rb) {
-        const Rsrc ri = rsrc4(S1.idx, (uint32_t)S1.Kv * 4u);
-        const Rsrc ra = rsrc4(S1.alpha_c, (uint32_t)S1.nb * (uint32_t)S1.Kv * 4u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                ix[j][t] = ld32(ri, io[j][t]);
-                acs[j][t] = ld32(ra, so[j][t]);
-            }
-            ixp[j] = ld32(ri, po[j]);
-        }
-    }
-    const float ar0 = __uint_as_float(ld32(rsrc4(S0.alpha_r, (uint32_t)S0.nb * (uint32_t)P.N * 4u), aro0));
-    const float ar1 = __uint_as_float(ld32(rsrc4(S1.alpha_r, (uint32_t)S1.nb * (uint32_t)P.N * 4u), aro1));
-    uint32_t wm[CW];
-    {
-        const Rsrc r = rsrc4(S0.packed, (uint32_t)S0.nb * (uint32_t)P.NT * (uint32_t)S0.KT * kTileWords * 4u);
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            if constexpr (MW == 8) {
-                const uint4 h0 = ld128(r, wo[j][0]);
-                const uint4 h1 = ld128(r, wo[j][1]);
-                wm[8 * j + 0] = h0.x; wm[8 * j + 1] = h0.y; wm[8 * j + 2] = h0.z; wm[8 * j + 3] = h0.w;
-                wm[8 * j + 4] = h1.x; wm[8 * j + 5] = h1.y; wm[8 * j + 6] = h1.z; wm[8 * j + 7] = h1.w;
-            } else if constexpr (MW == 4) {
-                const uint4 h = ld128(r, wo[j][0]);
-                wm[0] = h.x; wm[1] = h.y; wm[2] = h.z; wm[3] = h.w;
-            } else if constexpr (MW == 2) {
-                const uint2 h = ld64(r, wo[j][0]);
-                wm[0] = h.x; wm[1] = h.y;
-            } else {
-                wm[0] = ld32(r, wo[j][0]);
-            }
-        }
-    }
-    const uint32_t Wr0 = ld32(rsrc4(S1.packed, (uint32_t)S1.nb * (uint32_t)P.NT * (uint32_t)S1.KT * kTileWords * 4u), wro);
 
     // ---- index checks (the weights stay in flight): an index outside [0, K) or not above the one
     // before it is reported and its column reads the zero pad with alpha_c_s = 0 (it adds
     // nothing); so do the padding columns
+    uint32_t ia[4] = {xpad, xpad, xpad, xpad};  // LDS addresses of the table's 4 staged activations
     if (rb) {
         bool bad_idx = false;
+        uint32_t prev = ixp;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int q0 = ((4 * qe + j) & (S1.cpb - 1)) * S1.C + 4 * gj;
-            uint32_t prev = ixp[j];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int q = q0 + t;
-                const uint32_t xi = ix[j][t];
-                const bool live = q < S1.Kv;
-                const bool bad = live && (xi >= ldx || (q > 0 && (int)prev >= (int)xi));
-                bad_idx = bad_idx || bad;
-                const bool use = live && !bad;
-                ix[j][t] = use ? P.xs_off + 4u * xpos(xi, P.xsh) : xpad;
-                acs[j][t] = use ? acs[j][t] : 0u;
-                prev = xi;
-            }
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t q = q0 + (uint32_t)t;
+            const uint32_t xi = ix[t];
+            const bool live = q < (uint32_t)S1.Kv;
+            const bool bad = live && (xi >= ldx || (q > 0u && (int)prev >= (int)xi));
+            bad_idx = bad_idx || bad;
+            const bool use = live && !bad;
+            ia[t] = use ? P.xs_off + 4u * xpos(xi, P.xsh) : xpad;
+            acs[t] = use ? acs[t] : 0u;
+            prev = xi;
         }
         if (bad_idx && P.err != nullptr) atomicOr(P.err, kWsErrIndex);
     }
@@ -387,21 +350,15 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
                 *reinterpret_cast<float4*>(s_lds + S0.tab + 4u * ((uint32_t)(e * S0.G + gi) * 32u + 4u * (uint32_t)qd)) =
                     make_float4(T[0][e], T[1][e], T[2][e], T[3][e]);
         }
-        // ---- build: refinement tables (v = alpha_c_s x[idx])
+        // ---- build: refinement tables (v = alpha_c_s x[idx]), one per thread
         if (rb) {
-            float T[4][16];
+            float v[4], T[16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float v[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    v[t] = __uint_as_float(acs[j][t]) * *reinterpret_cast<const float*>(s_lds + ix[j][t]);
-                lut4(v, T[j]);
-            }
+            for (int t = 0; t < 4; ++t) v[t] = __uint_as_float(acs[t]) * *reinterpret_cast<const float*>(s_lds + ia[t]);
+            lut4(v, T);
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-                *reinterpret_cast<float4*>(s_lds + S1.tab + 4u * ((uint32_t)(e * S1.G + gj) * 32u + 4u * (uint32_t)qe)) =
-                    make_float4(T[0][e], T[1][e], T[2][e], T[3][e]);
+                *reinterpret_cast<float*>(s_lds + S1.tab + 4u * ((uint32_t)(e * S1.G + gj) * 32u + (uint32_t)ce)) = T[e];
         }
         __syncthreads();
         // ---- lookups: main chunk (G0 = 8 CW groups), then the refinement chunk (G1 groups).
