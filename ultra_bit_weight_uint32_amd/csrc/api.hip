@@ -15,13 +15,11 @@ constexpr int kVersion = 8;
 constexpr int kMaxFitIters = 10000;
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-inline bool fits_int(int64_t v) { return v >= 1 && v <= INT_MAX / 2; }
+using plan::aligned16;
+using plan::fits_int;
 inline int hip_status(hipError_t e) { return e == hipSuccess ? UBW_OK : UBW_EHIP; }
 
-int64_t packed_words_of(int nb, int64_t N, int64_t K) {
-    return (int64_t)nb * ceil_div(N, kTileRows) * ceil_div(K, kSliceCols) * kTileWords;
-}
+int64_t packed_words_of(int nb, int64_t N, int64_t K) { return plan::packed_words(nb, N, K); }
 
 // Rows per unit: 2 row tiles when the list still holds at least 768 units (enough to keep every
 // workgroup busy; the tables, built once per unit and activation row, then serve 512 rows),
@@ -39,24 +37,18 @@ int64_t units_of(int64_t Kv, int nb) { return ceil_div(ceil_div(Kv, kSliceCols) 
 
 int validate_gemv_common(const void* packed, const void* ar, const float* ac, int nb, int64_t N, int64_t Kv,
                          const void* x, int x_dtype, int batch, const float* y) {
-    if (!packed || !ar || !ac || !x || !y) return UBW_EINVAL;
-    if (nb < 1 || nb > 64 || !fits_int(N) || !fits_int(Kv)) return UBW_EINVAL;
-    if (batch < 1 || batch > UBW_MAX_BATCH) return UBW_EINVAL;
-    if (x_dtype != UBW_F16 && x_dtype != UBW_F32) return UBW_EUNSUPPORTED;
-    if (!aligned16(packed)) return UBW_EALIGN;
-    return UBW_OK;
+    return plan::check_gemv_common(packed, ar, ac, nb, N, Kv, x, x_dtype, batch, y);
 }
 
-// Workspace check: NULL with 0 bytes means "none" (the y = result mode then zero-fills y with
-// a separate launch); otherwise it must hold the counters for N rows.
-int check_workspace(void* ws, size_t ws_bytes, int64_t N, uint32_t** out) {
+// Workspace check at group width g (plan.h): NULL with 0 bytes means "none" (the y = result mode
+// then zero-fills y with a separate launch at g = 8).
+int check_workspace_g(void* ws, size_t ws_bytes, int64_t N, int g, uint32_t** out) {
     *out = nullptr;
-    if (ws == nullptr) return ws_bytes == 0 ? UBW_OK : UBW_EINVAL;
-    if (!aligned16(ws)) return UBW_EALIGN;
-    if (ws_bytes < (size_t)step_workspace_words(N) * 4) return UBW_ESIZE;
-    *out = static_cast<uint32_t*>(ws);
-    return UBW_OK;
+    const int st = plan::check_workspace(ws, ws_bytes, N, g);
+    if (st == UBW_OK) *out = static_cast<uint32_t*>(ws);
+    return st;
 }
+int check_workspace(void* ws, size_t ws_bytes, int64_t N, uint32_t** out) { return check_workspace_g(ws, ws_bytes, N, 8, out); }
 
 Segment make_segment(const uint32_t* packed, const void* ar, const float* ac, const int32_t* idx, int nb,
                      int64_t Kv) {
@@ -91,19 +83,6 @@ StepArgs make_step(int64_t N, const void* x, int x_dtype, int64_t K, int batch, 
 int run_step(StepArgs& a, void* stream) {
     if (!step_buffers_fit(a)) return UBW_EUNSUPPORTED;
     return hip_status(launch_step(a, as_stream(stream)));
-}
-
-// Group width 4 runs the whole-row kernel, which needs no counters: a workspace, when given,
-// only receives the error bits in its header (16 words). Group width 8 needs the counters of
-// every row group for its single-launch y = result mode.
-int check_workspace_g(void* ws, size_t ws_bytes, int64_t N, int g, uint32_t** out) {
-    if (g != 4) return check_workspace(ws, ws_bytes, N, out);
-    *out = nullptr;
-    if (ws == nullptr) return ws_bytes == 0 ? UBW_OK : UBW_EINVAL;
-    if (!aligned16(ws)) return UBW_EALIGN;
-    if (ws_bytes < (size_t)kWsHeaderWords * 4) return UBW_ESIZE;
-    *out = static_cast<uint32_t*>(ws);
-    return UBW_OK;
 }
 
 // A step at group width g (4 or 8, checked by the caller). Shapes whose group-4 tables do not

@@ -437,20 +437,10 @@ constexpr uint32_t kArrBits = 12;
 constexpr uint32_t kArrMask = (1u << kArrBits) - 1u;
 constexpr uint32_t kGenMask = (1u << (32 - kArrBits)) - 1u;
 
-// Division by a divisor fixed for the launch: q = (n * m) >> sh for 0 <= n < 2^31, with
-// sh = 31 + ceil(log2 d) and m = ceil(2^sh / d) (the rounding error stays below 1 / d).
-struct FastDiv {
-    uint32_t m, sh;
-};
-__host__ __device__ inline FastDiv fast_div(uint32_t d) {
-    uint32_t l = 0;
-    while ((1ull << l) < d) ++l;
-    const uint64_t p = 1ull << (31 + l);
-    return FastDiv{(uint32_t)((p + d - 1) / d), 31 + l};
-}
-__device__ __forceinline__ uint32_t div_by(uint32_t n, FastDiv f) {
-    return (uint32_t)(((uint64_t)n * f.m) >> f.sh);
-}
+// Division by a divisor fixed for the launch (plan.h).
+using plan::FastDiv;
+using plan::div_by;
+using plan::fast_div;
 
 struct StepParams {
     StepArgs a;
@@ -746,25 +736,13 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
     // as rank g - Zn. Either way the list holds the main units row group by row group, then the
     // refinement units, and rank r takes an equal contiguous range (the first ones one unit more).
     // A cursor's rg counts the listed row groups; it is row group rgo + rgs * rg of the matrix.
-    int rank, Gx, NRGx;
-    if (P.xmode) {  // Zn is a multiple of 8: unit workgroup g - Zn is on the XCD of g
-        lcn.rgo = g & 7;
-        lcn.rgs = 8;
-        rank = (g - P.Zn) >> 3;
-        Gx = (P.Gu - lcn.rgo + 7) >> 3;
-        NRGx = (P.NRG - lcn.rgo + 7) >> 3;
-    } else {
-        lcn.rgo = 0;
-        lcn.rgs = 1;
-        rank = g - P.Zn;
-        Gx = P.Gu;
-        NRGx = P.NRG;
-    }
+    const plan::WgRange wr = plan::wg_range(g, P.Zn, P.Gu, P.NRG, P.Urg, P.xmode != 0);
+    lcn.rgo = wr.rgo;
+    lcn.rgs = wr.rgs;
+    const int NRGx = wr.NRGx;
     auto grg = [&](int rg) { return lcn.rgo + lcn.rgs * rg; };
-    const uint32_t Ux = (uint32_t)NRGx * (uint32_t)P.Urg;
-    const uint32_t Qx = Ux / (uint32_t)Gx, Rx = Ux - Qx * (uint32_t)Gx;
-    const uint32_t x0 = (uint32_t)rank * Qx + ((uint32_t)rank < Rx ? (uint32_t)rank : Rx);
-    const uint32_t x1 = x0 + Qx + ((uint32_t)rank < Rx ? 1u : 0u);
+    const uint32_t Qx = (uint32_t)NRGx * (uint32_t)P.Urg / (uint32_t)wr.Gx;
+    const uint32_t x0 = wr.x0, x1 = wr.x1;
     const uint32_t Um = (uint32_t)NRGx * (uint32_t)P.US[0];  // units of segment 0 in the list
 
     float acc[RPL][BMAX];
@@ -1185,17 +1163,7 @@ static int64_t resident_capacity_group() {
     return capacity_of(k_gemv8_group<XT, RPL, BMAX, XL>, cap);
 }
 
-// Workgroups with units for U units when the device holds cap at once (two per CU): one per
-// CU at batch 1 when the units fit in two per CU. A second workgroup on a CU runs behind the
-// first (the CU issues the older waves' instructions first), so with one unit each the doubled
-// CUs finish last; one workgroup per CU taking two units where needed ends sooner (measured,
-// batch 1, K = 4096: 272 units 6.36 -> 6.24 us, 384 units 6.53 -> 6.44, 512 units
-// 7.16 -> 6.61). With more units, or a larger batch, two workgroups per CU hide more latency.
-static int64_t default_workgroups(int64_t U, int64_t cap, int batch) {
-    const int64_t cus = cap / 2;
-    if (batch == 1 && U > cus && U <= cap) return cus;
-    return cap;
-}
+using plan::default_workgroups;
 
 // Split of P's units over Gu workgroups and the final output mode; zero-fills y first when the
 // single-launch protocol cannot be used (no workspace, or too many arrivals per row group for

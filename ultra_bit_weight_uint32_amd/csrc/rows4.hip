@@ -68,7 +68,9 @@ struct R4Params {
     uint32_t* err;           // workspace word 0 for index errors, or nullptr
     uint32_t xs_off;         // byte offset of the fp32 staging of x in LDS
     uint32_t K4;             // K rounded up to a multiple of 4
-    uint32_t xsh;            // staging: column c at float xpos(c) = c + 4 (c >> xsh)
+    uint32_t xsh;            // staging: column c at float c + 4 (c >> xsh): 4 padding floats after every
+                             // 4 main chunks of columns, so that the 8 lanes of an LDS pass of the
+                             // main build (8 chunk quadruples, 4 chunks apart) read different banks
     int xvec;                // 1: 16-byte aligned x rows (16-byte loads), 0: one element per load
 };
 
@@ -94,15 +96,14 @@ __device__ __forceinline__ uint4 ld128(Rsrc r, uint32_t off) {
 // time where rows are not 16-byte aligned.
 template <typename XT> constexpr uint32_t kVecCols = 16u / (uint32_t)sizeof(XT);
 __device__ __forceinline__ float h2f(uint32_t h) { return __half2float(__ushort_as_half((unsigned short)h)); }
-__device__ __forceinline__ uint32_t xpos(uint32_t c, uint32_t sh);
 template <typename XT> __device__ __forceinline__ void stage_vec(float* xs, uint32_t c0, uint32_t sh, const uint4& v);
 template <> __device__ __forceinline__ void stage_vec<__half>(float* xs, uint32_t c0, uint32_t sh, const uint4& v) {
-    *reinterpret_cast<float4*>(&xs[xpos(c0, sh)]) = make_float4(h2f(v.x & 0xFFFFu), h2f(v.x >> 16), h2f(v.y & 0xFFFFu), h2f(v.y >> 16));
-    *reinterpret_cast<float4*>(&xs[xpos(c0 + 4u, sh)]) =
+    *reinterpret_cast<float4*>(&xs[plan::r4_xpos(c0, sh)]) = make_float4(h2f(v.x & 0xFFFFu), h2f(v.x >> 16), h2f(v.y & 0xFFFFu), h2f(v.y >> 16));
+    *reinterpret_cast<float4*>(&xs[plan::r4_xpos(c0 + 4u, sh)]) =
         make_float4(h2f(v.z & 0xFFFFu), h2f(v.z >> 16), h2f(v.w & 0xFFFFu), h2f(v.w >> 16));
 }
 template <> __device__ __forceinline__ void stage_vec<float>(float* xs, uint32_t c0, uint32_t sh, const uint4& v) {
-    *reinterpret_cast<float4*>(&xs[xpos(c0, sh)]) =
+    *reinterpret_cast<float4*>(&xs[plan::r4_xpos(c0, sh)]) =
         make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 template <typename XT> __device__ __forceinline__ float x_at(Rsrc r, uint32_t off);
@@ -124,10 +125,6 @@ __device__ __forceinline__ void lut4(const float v[4], float T[16]) {
     for (int q = 0; q < 8; ++q) T[8 + q] = T[q] + u3;
 }
 
-// Staging position of activation column c: 4 padding floats after every 2^sh columns (2^sh =
-// 4 main chunks), so that the 8 lanes of an LDS pass of the main build, which read the columns
-// of 8 chunk quadruples (4 chunks apart), fall on different banks.
-__device__ __forceinline__ uint32_t xpos(uint32_t c, uint32_t sh) { return c + 4u * (c >> sh); }
 
 // Base of lane c's chunk (32 / nb chunks per base), 0 for an empty segment.
 __device__ __forceinline__ int k0_of(int c, const R4Seg& sg) { return sg.nb > 0 ? c >> sg.lcpb : 0; }
@@ -184,7 +181,7 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
                 stage_vec<XT>(xs, kVecCols<XT> * v, P.xsh, ld128(rx, (uint32_t)b * xrow + 16u * v));
         } else {
             for (uint32_t i = (uint32_t)tid; i < ldx; i += kR4Threads)
-                xs[xpos(i, P.xsh)] = x_at<XT>(rx, (uint32_t)b * xrow + (uint32_t)sizeof(XT) * i);
+                xs[plan::r4_xpos(i, P.xsh)] = x_at<XT>(rx, (uint32_t)b * xrow + (uint32_t)sizeof(XT) * i);
         }
     };
 
@@ -202,7 +199,7 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
     // for columns >= K, whose alpha_c reads as 0 too)
     const int gi = tid >> 3, qd = tid & 7;
     const bool mb = S0.nb > 0 && gi < S0.G;
-    const uint32_t xpad = P.xs_off + 4u * xpos(P.K4, P.xsh);
+    const uint32_t xpad = P.xs_off + 4u * plan::r4_xpos(P.K4, P.xsh);
     uint4 acm[4];
     uint32_t xa[4];
     {
@@ -221,7 +218,7 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
                 acm[j].z = ld32(r, in && col + 2u < (uint32_t)S0.Kv ? o + 8u : kR4Oob);
                 acm[j].w = ld32(r, in && col + 3u < (uint32_t)S0.Kv ? o + 12u : kR4Oob);
             }
-            xa[j] = in ? P.xs_off + 4u * xpos(col, P.xsh) : xpad;
+            xa[j] = in ? P.xs_off + 4u * plan::r4_xpos(col, P.xsh) : xpad;
         }
     }
     // refinement build role: one table per thread, on the last waves: thread 511 - t, t < 32 G1,
@@ -317,7 +314,7 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
             const bool bad = live && (xi >= ldx || (q > 0u && (int)prev >= (int)xi));
             bad_idx = bad_idx || bad;
             const bool use = live && !bad;
-            ia[t] = use ? P.xs_off + 4u * xpos(xi, P.xsh) : xpad;
+            ia[t] = use ? P.xs_off + 4u * plan::r4_xpos(xi, P.xsh) : xpad;
             acs[t] = use ? acs[t] : 0u;
             prev = xi;
         }
@@ -325,7 +322,7 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
     }
     // the zero pad: every position after column K - 1 (ordered by the first barrier below)
     {
-        const uint32_t zlo = xpos(ldx - 1u, P.xsh) + 1u, zhi = xpos(P.K4, P.xsh) + 4u;
+        const uint32_t zlo = plan::r4_xpos(ldx - 1u, P.xsh) + 1u, zhi = plan::r4_xpos(P.K4, P.xsh) + 4u;
         if ((uint32_t)tid < zhi - zlo) xs[zlo + (uint32_t)tid] = 0.f;
     }
 
@@ -414,8 +411,7 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
     }
 }
 
-// Chunking of one segment: 32 chunks per row, 32 / nb per base, C columns each (a multiple of
-// 4); false when the segment cannot be cut that way.
+// A segment's chunking (plan.h) with its buffers; false when it cannot be cut that way.
 bool chunk_segment(const Segment& sg, int cw_main, bool refinement, R4Seg& out) {
     out = R4Seg{};
     out.packed = sg.packed;
@@ -424,43 +420,13 @@ bool chunk_segment(const Segment& sg, int cw_main, bool refinement, R4Seg& out) 
     out.idx = sg.idx;
     out.nb = sg.nb;
     out.Kv = sg.Kv;
-    if (sg.nb == 0) return true;
-    if (sg.nb != 1 && sg.nb != 2 && sg.nb != 4) return false;
-    out.KT = (int)ceil_div(sg.Kv, kSliceCols);
-    out.cpb = 32 / sg.nb;
-    out.lcpb = sg.nb == 1 ? 5 : sg.nb == 2 ? 4 : 3;
-    if (!refinement) {
-        out.C = 32 * cw_main;
-    } else {
-        // the refinement's virtual columns padded to its tiles: 32 chunks of Cs columns, one
-        // word at most (a chunk stays within one 32-column word)
-        const int64_t cs = (int64_t)sg.nb * out.KT * kSliceCols / 32;
-        if (cs > 32 || cs % 4 != 0 || 32 % cs != 0) return false;
-        out.C = (int)cs;
-    }
-    out.G = out.C / 4;
-    return (int64_t)out.cpb * out.C >= sg.Kv;
-}
-
-// Staging padding: 4 floats after every 4 C main columns (C a power of two), none without a
-// main segment; the staging holds the padded K4 columns and 4 zeros.
-uint32_t staging_shift(int C) {
-    if (C == 0) return 31;
-    uint32_t sh = 0;
-    while ((1 << sh) < 4 * C) ++sh;
-    return sh;
-}
-int64_t staging_floats(int64_t K, int C) {
-    const int64_t K4 = ceil_div(K, 4) * 4;
-    return K4 + 4 * (K4 >> staging_shift(C)) + 4;
-}
-
-// Words per main chunk for K columns and nb bases: the smallest power of two >= nb K / 1024.
-int main_chunk_words(int nb, int64_t K) {
-    const int64_t need = ceil_div((int64_t)nb * K, 1024);
-    int cw = 1;
-    while (cw < need) cw *= 2;
-    return cw;
+    const plan::R4Chunk c = plan::r4_chunk(sg.nb, sg.Kv, refinement, cw_main);
+    out.KT = c.KT;
+    out.cpb = c.cpb;
+    out.lcpb = c.lcpb;
+    out.C = c.C;
+    out.G = c.G;
+    return c.ok;
 }
 
 }  // namespace
@@ -471,20 +437,17 @@ bool rows4_supported(const StepArgs& a) {
     const Segment& m = a.nseg >= 1 ? a.seg[0] : empty;
     const Segment& r = a.nseg >= 2 ? a.seg[1] : empty;
     if (m.nb == 0 && r.nb == 0) return false;
-    const int cw = m.nb > 0 ? main_chunk_words(m.nb, m.Kv) : 1;
+    const int cw = m.nb > 0 ? plan::r4_main_chunk_words(m.nb, m.Kv) : 1;
     if (cw > 8) return false;
-    R4Seg s0, s1;
-    if (!chunk_segment(m, cw, false, s0) || !chunk_segment(r, cw, true, s1)) return false;
-    const uint64_t lds = 512ull * (uint64_t)(s0.nb ? s0.C : 0) + 512ull * (uint64_t)(s1.nb ? s1.C : 0) +
-                         4ull * ((uint64_t)staging_floats(a.ldx, s0.nb ? s0.C : 0));
-    return lds <= kR4LdsBytes;
+    const plan::R4Chunk c0 = plan::r4_chunk(m.nb, m.Kv, false, cw), c1 = plan::r4_chunk(r.nb, r.Kv, true, cw);
+    return c0.ok && c1.ok && plan::r4_lds_bytes(c0, c1, a.ldx) <= (int64_t)kR4LdsBytes;
 }
 
 hipError_t launch_rows4(const StepArgs& a, hipStream_t s) {
     if (!rows4_supported(a)) return hipErrorInvalidValue;
     R4Params P{};
     const Segment empty{};
-    const int cw = a.seg[0].nb > 0 && a.nseg >= 1 ? main_chunk_words(a.seg[0].nb, a.seg[0].Kv) : 1;
+    const int cw = a.seg[0].nb > 0 && a.nseg >= 1 ? plan::r4_main_chunk_words(a.seg[0].nb, a.seg[0].Kv) : 1;
     chunk_segment(a.nseg >= 1 ? a.seg[0] : empty, cw, false, P.seg[0]);
     chunk_segment(a.nseg >= 2 ? a.seg[1] : empty, cw, true, P.seg[1]);
     uint32_t off = 0;
@@ -492,7 +455,7 @@ hipError_t launch_rows4(const StepArgs& a, hipStream_t s) {
     if (P.seg[1].nb) { P.seg[1].tab = off; off += 512u * (uint32_t)P.seg[1].C; }
     P.xs_off = off;
     P.K4 = (uint32_t)(ceil_div(a.ldx, 4) * 4);
-    P.xsh = staging_shift(P.seg[0].nb ? P.seg[0].C : 0);
+    P.xsh = plan::r4_staging_shift(P.seg[0].C);
     const int64_t xsz = a.x_dtype == UBW_F16 ? 2 : 4;
     P.xvec = (a.ldx * xsz) % 16 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15u) == 0;
     const bool av = P.seg[0].Kv % 4 == 0 && (reinterpret_cast<uintptr_t>(P.seg[0].alpha_c) & 15u) == 0;

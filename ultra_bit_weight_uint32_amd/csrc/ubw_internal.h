@@ -22,6 +22,7 @@
 #include <stdint.h>
 
 #include "../../include/ubw.h"
+#include "plan.h"
 
 namespace ubw {
 
@@ -73,10 +74,10 @@ struct StepArgs {
 // nothing) and kWsErrIndex (a salient index outside [0, K) or not above the one before it).
 constexpr uint32_t kWsErrWait = 1u;
 constexpr uint32_t kWsErrIndex = 2u;
-constexpr int kWsHeaderWords = 16;
-constexpr int kWsRowGroupWords = 64;
+constexpr int kWsHeaderWords = plan::kWsHeaderWords;
+constexpr int kWsRowGroupWords = plan::kWsRowGroupWords;
 constexpr int kWsFlagOffset = 32;
-inline int64_t step_workspace_words(int64_t N) { return kWsHeaderWords + kWsRowGroupWords * ceil_div(N, kTileRows); }
+inline int64_t step_workspace_words(int64_t N) { return plan::workspace_words(N); }
 
 // The static workspace of ubw_lut_gemv_refined_noalloc: the counters of up to 256 row groups
 // (N <= 65536 rows), 65,600 bytes per device; scratch_address() gives this device's copy.
