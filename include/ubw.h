@@ -160,8 +160,8 @@ int ubw_workspace_bytes(int nb, int64_t N, int64_t K, int g, int batch, size_t* 
  * of the static workspace of ubw_lut_gemv_refined_noalloc on the current device: waits for
  * `stream` to finish, so it is not for use inside graph capture. *out_word (host) gets the word.
  * Returns UBW_OK (no error recorded), UBW_EWAIT (bit 0 set: some outputs were not written),
- * UBW_ERANGE (bit 1 set, bit 0 clear: a salient index was out of range or out of order; the
- * offending columns contributed nothing), or UBW_EINVAL / UBW_EALIGN / UBW_EHIP for the call.
+ * UBW_ERANGE (bit 1 set, bit 0 clear: a salient index was out of range or out of order; see
+ * ubw_vcm_gather_refine), or UBW_EINVAL / UBW_EALIGN / UBW_EHIP for the call.
  */
 int ubw_workspace_check(void* workspace, int clear, void* stream, uint32_t* out_word);
 
@@ -202,10 +202,11 @@ int ubw_lut_gemv(const uint32_t* packed, const float* alpha_r, const float* alph
  *   packed_s     from ubw_pack_bases(ns, N, s, g) of the refinement bases [ns][N][s]
  *   alpha_r_s    fp32 [ns][N];  alpha_c_s fp32 [ns][s]
  *   K            columns of x (the activation row length)
- * The kernels check idx on the device as they gather: a position q whose idx[q] lies outside
- * [0, K), or is not above idx[q - 1], reads nothing and contributes nothing, and sets bit 1 of
- * the workspace's word 0 (UBW_ERANGE from ubw_workspace_check). Without a workspace nothing
- * records it; ubw_check_indices checks a host copy of idx.
+ * The kernels check idx on the device: a position q whose idx[q] lies outside [0, K), or is not
+ * above idx[q - 1], sets bit 1 of the workspace's word 0 (UBW_ERANGE from ubw_workspace_check).
+ * A position outside [0, K) reads nothing and contributes nothing; one out of order still adds
+ * its term of the sum above (which is defined for any order). Without a workspace nothing
+ * records the fault; ubw_check_indices checks a host copy of idx.
  * Errors: as ubw_lut_gemv; s < 1 is UBW_EINVAL.
  */
 int ubw_vcm_gather_refine(const int32_t* idx, int64_t s, const uint32_t* packed_s,

@@ -13,7 +13,7 @@ import oracle
 import ultra_bit_weight_uint32_amd as ubw
 from workloads import Gemv, make_gemv, make_integer_gemv
 
-from test_gpu_parity import DEV, TOL, dev, drop_positions, host, max_rel_err, oracle_gemv, pack
+from test_gpu_parity import DEV, TOL, dev, drop_positions, host, index_fault_cases, max_rel_err, oracle_gemv, pack
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -111,22 +111,19 @@ def test_g4_headline_full_output_b1_and_b16():
 @pytest.mark.parametrize("batch", [1, 4])
 def test_g4_index_checks(batch):
     """Salient indices checked on the device at g = 4: outside [0, K) or not above the one before
-    it sets bit 1 of the workspace header and that column adds nothing."""
+    it sets bit 1 of the workspace header; a column outside [0, K) adds nothing, one out of order
+    still adds its term."""
     rng = np.random.default_rng(35 + batch)
     n, k, s = 260, 900, 90
     g = make_integer_gemv(rng, n, k, 1, s=s, ns=2, batch=batch)
-    cases = [({0: -1}, [0]), ({s - 1: k}, [s - 1]), ({s - 1: 2**31 - 1}, [s - 1]), ({40: int(g.idx[39])}, [40])]
-    for change, dropped in cases:
-        h = Gemv(**{f: getattr(g, f) for f in g.__dataclass_fields__})
-        h.idx = g.idx.copy()
-        for q, v in change.items():
-            h.idx[q] = v
+    for change, dropped, h in index_fault_cases(g, k, s):
         for mode in ("fused", "two_calls"):
             ws = torch.zeros(16, dtype=torch.int32, device=DEV)
             got = run4(h, mode=mode, ws=ws)
             st, word = ubw.workspace_check(ws, clear=True)
             assert st == ubw.UBW_ERANGE and word == 2, (change, mode, st, word)
-            assert np.array_equal(got, oracle_gemv(drop_positions(g, dropped))), (change, mode)
+            want = oracle_gemv(drop_positions(g, dropped)) if dropped else oracle_gemv(h)
+            assert np.array_equal(got, want), (change, mode)
 
 
 def test_g4_noalloc_matches_refined():

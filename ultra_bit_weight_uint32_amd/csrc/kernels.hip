@@ -626,12 +626,12 @@ __device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const Step
         U.ar[j] = buf_f32(r_ar, lval && row < (uint32_t)a.N ? arBase + row * 4u : kOob);
     }
     if constexpr (SI == 1 && !XL) {
-        // VCM: the index must lie in [0, K) and exceed the one before it (ascending, distinct); a
-        // column that breaks this reads nothing (x = 0, so it contributes nothing) and sets bit 1
-        // of workspace word 0
+        // VCM: the index must lie in [0, K) and exceed the one before it (ascending, distinct);
+        // either fault sets bit 1 of workspace word 0, and a column outside [0, K) reads nothing
+        // (x = 0, so it contributes nothing; one out of order still adds x[idx])
         const bool bad = valid && cvalid && (raw >= ldx || (col > 0 && (int)rawp >= (int)raw));
         if (bad && a.ws != nullptr) atomicOr(a.ws, kWsErrIndex);
-        const bool use = cvalid && !bad;
+        const bool use = cvalid && raw < ldx;
 #pragma unroll
         for (int b = 0; b < BMAX; ++b) buf_x(r_x, use ? ((uint32_t)b * ldx + raw) * xs : kOob, U.xv[b]);
     }
@@ -899,8 +899,8 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         // scaled activations of both items: v = alpha_c * x (LUT-BSF folds alpha_c here)
         if constexpr (SI == 1 && XL) {
             // VCM: the staged column's index must lie in [0, K) and exceed the one before it
-            // (ascending, distinct); a column that breaks this contributes nothing and sets bit 1
-            // of workspace word 0
+            // (ascending, distinct); either fault sets bit 1 of workspace word 0, and a column
+            // outside [0, K) contributes nothing (one out of order still adds x[idx])
             const uint32_t ldx = (uint32_t)a.ldx;
             int sks, sk;
             item_of(cu, (int)lcn.sd, a.seg[1].nb, sks, sk);
@@ -908,7 +908,7 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             const bool cvalid = 2 * cu.q + (int)lcn.sd < nitems && col < (uint32_t)a.seg[1].Kv;
             const bool bad = cvalid && (U.xc >= ldx || (col > 0 && (int)U.xp >= (int)U.xc));
             if (bad && a.ws != nullptr) atomicOr(a.ws, kWsErrIndex);
-            const bool use = cvalid && !bad;
+            const bool use = cvalid && U.xc < ldx;
             // the activation block into the table area (free until the build below), then the
             // gather through idx from there
             lds_u32x4* blk = (lds_u32x4*)(tab + 4 * tid);

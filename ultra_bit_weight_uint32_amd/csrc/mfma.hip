@@ -115,6 +115,10 @@ __device__ __forceinline__ uint32_t ldx_raw(Rsrc r, uint32_t i, float*) { return
 __device__ __forceinline__ uint32_t ldx_raw(Rsrc r, uint32_t i, __half*) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)(2u * i), 0, 0);
 }
+// An element index whose byte offset lies beyond every activation buffer (below 2 GiB): the
+// buffer load returns 0 for it.
+__device__ __forceinline__ uint32_t x_oob(float*) { return 0x3FFFFFFFu; }
+__device__ __forceinline__ uint32_t x_oob(__half*) { return 0x7FFFFFFFu; }
 __device__ __forceinline__ float x_from_raw(uint32_t v, float*) { return __uint_as_float(v); }
 __device__ __forceinline__ float x_from_raw(uint32_t v, __half*) { return __half2float(__ushort_as_half((unsigned short)v)); }
 
@@ -197,9 +201,7 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
         // (refinement) idx of the staged columns. Every load is issued (clamped to a valid address,
         // the value dropped later) before any is used.
         uint4 p0[4], p1[4];
-        // idx (refinement), raw x bits (main; for the refinement: idx of the column before each
-        // even element, for the ascending-order check), alpha_c bits
-        uint32_t xi[16], xw[16], aw[16];
+        uint32_t xi[16], xw[16], aw[16];  // idx (refinement), raw x bits (main), alpha_c bits
         const Rsrc r_ac = rsrc(acr, (uint32_t)sg.Kv * 4u);
         // this row tile's slab of the segment (all slices and bases): below 2 GiB (checked)
         const Rsrc r_w = rsrc(sg.packed + (int64_t)rt * nitems * kTileWords, (uint32_t)nitems * kTileWords * 4u);
@@ -226,8 +228,7 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
                 const uint32_t d = 32u * (uint32_t)(i >> 1) + (uint32_t)(i & 1);
                 aw[i] = ld32(r_ac, 4u * col0 + 4u * d);
                 xi[i] = ld32(r_idx, 4u * col0 + 4u * d);
-                if (si) xw[i] = (i & 1) == 0 && col0 + d > 0 ? ld32(r_idx, 4u * (col0 + d - 1u)) : 0u;
-                else xw[i] = ldx_raw(r_xd, xrow + col0 + d, (XT*)nullptr);
+                xw[i] = ldx_raw(r_xd, xrow + col0 + d, (XT*)nullptr);
             }
         };
         for (int ks = lo; ks < hi; ++ks) {
@@ -236,21 +237,14 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
             {
                 float xv[16];
                 if (si) {  // the gather through idx (the loads wait here, where they are used anyway)
-                    // VCM: each column's index must lie in [0, K) and exceed the one before it
-                    // (ascending, distinct); a column that breaks this reads nothing, contributes
-                    // nothing and sets bit 1 of the workspace's word 0
-                    const int colb = ks * kSliceCols + 2 * cg;
-                    bool bad_any = false;
+                    // VCM: an index outside [0, K) reads beyond the buffer (0: its column adds
+                    // nothing); a padding column past s has idx 0 (read out of idx's range) and
+                    // alpha_c 0. The indices are checked and reported once per launch, at the end.
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int col = colb + 32 * (i >> 1) + (i & 1);
-                        const uint32_t prev = (i & 1) ? xi[i - 1] : xw[i];
-                        const bool bad = col < sg.Kv && (xi[i] >= (uint64_t)ldx || (col > 0 && (int)prev >= (int)xi[i]));
-                        bad_any = bad_any || bad;
-                        const uint32_t off = bad || col >= sg.Kv ? xrow : xrow + xi[i];  // valid; dropped
-                        xv[i] = bad ? 0.f : x_from_raw(ldx_raw(r_xg, off, (XT*)nullptr), (XT*)nullptr);
+                        const uint32_t off = xi[i] < (uint64_t)ldx ? xrow + xi[i] : x_oob((XT*)nullptr);
+                        xv[i] = x_from_raw(ldx_raw(r_xg, off, (XT*)nullptr), (XT*)nullptr);
                     }
-                    if (bad_any && P.err != nullptr) atomicOr(P.err, kWsErrIndex);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) xv[i] = x_from_raw(xw[i], (XT*)nullptr);
@@ -350,6 +344,18 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
             buf ^= 1;
         }
         arb ^= 1;
+    }
+
+    // VCM index check, once per GEMV (its first row tile and column chunk), after the matrix work:
+    // an index outside [0, K) or not above the one before it sets bit 1 of workspace word 0
+    if (rt == 0 && blockIdx.y == 0 && S1.nb > 0 && P.err != nullptr) {
+        const Rsrc r_i = rsrc(S1.idx, (uint32_t)S1.Kv * 4u);
+        bool bad = false;
+        for (int q = tid; q < S1.Kv; q += kMmThreads) {
+            const uint32_t v = ld32(r_i, 4u * (uint32_t)q), pv = ld32(r_i, q > 0 ? 4u * (uint32_t)(q - 1) : 0u);
+            bad = bad || v >= (uint64_t)ldx || (q > 0 && (int)pv >= (int)v);
+        }
+        if (bad) atomicOr(P.err, kWsErrIndex);
     }
 
     // y[b][row] (+)= the running sums (kPack: lane r16 < 8 adds the lo sums of lane r16 + 8)

@@ -300,8 +300,8 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
     }
 
     // ---- index checks (the weights stay in flight): an index outside [0, K) or not above the one
-    // before it is reported and its column reads the zero pad with alpha_c_s = 0 (it adds
-    // nothing); so do the padding columns
+    // before it is reported; a column outside [0, K) reads the zero pad with alpha_c_s = 0 (it
+    // adds nothing; one out of order still adds x[idx]), and so do the padding columns
     uint32_t ia[4] = {xpad, xpad, xpad, xpad};  // LDS addresses of the table's 4 staged activations
     if (rb) {
         bool bad_idx = false;
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kR4Threads, 1) void k_rows4(const R4Params P) {
             const bool live = q < (uint32_t)S1.Kv;
             const bool bad = live && (xi >= ldx || (q > 0u && (int)prev >= (int)xi));
             bad_idx = bad_idx || bad;
-            const bool use = live && !bad;
+            const bool use = live && xi < ldx;
             ia[t] = use ? P.xs_off + 4u * plan::r4_xpos(xi, P.xsh) : xpad;
             acs[t] = use ? acs[t] : 0u;
             prev = xi;
