@@ -131,11 +131,20 @@ def main():
     def main_only(c):
         ubw.lut_gemv(c["packed"], c["ar"], c["ac"], c["x"], n, k, y=c["y"], workspace=ws)
 
+    def step_g4(c):
+        """The same step at group width 4 (whole rows per workgroup, 16-entry tables of the full
+        row in LDS, one plain store per output; no workspace needed)."""
+        ubw.lut_gemv_refined(c["packed"], c["ar"], c["ac"], c["idx"], c["packed_s"], c["ar_s"], c["ac_s"], c["x"],
+                             n, k, g=4, y=c["y"])
+
     wbytes = packed0.numel() * 4
     outw = torch.empty(-(-wbytes // 8192), dtype=torch.int32, device=dev)
 
     def read_only(c):
         ubw.bench_stream_read(c["packed"], wbytes, outw)
+
+    def tiny(c):  # one 16-byte read by one workgroup: the floor of any launch
+        ubw.bench_stream_read(c["packed"], 16, outw)
 
     # warmup: W untimed steps (and touch every copy once)
     for i in range(max(args.warmup, ncopy)):
@@ -181,8 +190,12 @@ def main():
     ms_per_step = timed(step, args.steps) * 1e-3
     # B. main bases only (ubw_lut_gemv, one launch per call), same protocol
     main_us = timed(main_only, args.steps)
-    # C. size-matched streaming read of the same weight bytes (ceiling of one read that size)
+    # C. size-matched streaming read of the same weight bytes (ceiling of one read that size), and
+    # the launch floor (a one-workgroup kernel that reads 16 bytes)
     read_us = timed(read_only, args.steps)
+    floor_us = timed(tiny, args.steps)
+    # C'. the step at group width 4
+    g4_us = timed(step_g4, args.steps)
     # D. the same three, one launch at a time: each launch alone on the GPU between two events
     # (median), i.e. dispatch, the kernel and its end, with nothing of a neighbour overlapping
     iso = min(args.steps, 100)
@@ -277,6 +290,17 @@ def main():
             "GBps": round(wbytes / (read_us * 1e-6) / 1e9, 2),
             "us_isolated": round(iso_read, 3),
             "GBps_isolated": round(wbytes / (iso_read * 1e-6) / 1e9, 2),
+        },
+        "launch_floor": {
+            "what": "a one-workgroup kernel reading 16 bytes, same protocol: the per-launch cost of any kernel",
+            "us_per_launch": round(floor_us, 3),
+        },
+        "g4_step": {
+            "what": "the same step at group width 4 (ubw_lut_gemv_refined, g=4: whole rows per workgroup, "
+                    "no workspace)",
+            "us_per_launch": round(g4_us, 3),
+            "GBps": round(step_bytes / (g4_us * 1e-6) / 1e9, 2),
+            "pct_of_peak": round(100 * step_bytes / (g4_us * 1e-6) / 1e9 / PEAK_GBS, 2),
         },
         "isolated": {
             "what": "median of single launches, each alone on the GPU between two events (dispatch, kernel "

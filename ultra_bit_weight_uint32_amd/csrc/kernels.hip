@@ -133,6 +133,21 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
     return __half2float(__ushort_as_half((unsigned short)h));
 }
 
+// Two slots' lookups (8 table reads) added into s[0..3]: all 8 addresses, then all 8 reads, then
+// the adds, written in that order. Where the kernel's scalar registers run over their budget
+// the compiler's scheduler keeps a region in source order; in this order 8 reads are in flight
+// at once even then (read-add pairs one at a time would each wait out the LDS latency).
+__device__ __forceinline__ void lookup_pair(lds_cchar* tb, uint32_t wa, uint32_t wb, uint32_t la, uint32_t lb,
+                                            float s[4]) {
+    const uint32_t ad[8] = {perm_addr<0>(wa, la), perm_addr<1>(wa, la), perm_addr<2>(wa, la), perm_addr<3>(wa, la),
+                            perm_addr<0>(wb, lb), perm_addr<1>(wb, lb), perm_addr<2>(wb, lb), perm_addr<3>(wb, lb)};
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = *(const lds_f32*)(tb + ad[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e & 3] += t[e];
+}
+
 // Sums over the 32 groups of one row's slice for one base: step t = 4 i + jj reads the table
 // of group t ^ l at the pattern in byte jj of slot i. lo gets steps 0..15 (groups of the
 // 128-column half (l >> 4) of the slice), hi steps 16..31 (the other half).
@@ -145,12 +160,7 @@ __device__ __forceinline__ void lookup_halves(lds_cchar* tb, const uint4& w0, co
     for (int half = 0; half < 2; ++half) {
         s[half][0] = s[half][1] = s[half][2] = s[half][3] = 0.f;
 #pragma unroll
-        for (int i = 4 * half; i < 4 * half + 4; ++i) {
-            s[half][0] += *(const lds_f32*)(tb + perm_addr<0>(W[i], lc[i]));
-            s[half][1] += *(const lds_f32*)(tb + perm_addr<1>(W[i], lc[i]));
-            s[half][2] += *(const lds_f32*)(tb + perm_addr<2>(W[i], lc[i]));
-            s[half][3] += *(const lds_f32*)(tb + perm_addr<3>(W[i], lc[i]));
-        }
+        for (int i = 4 * half; i < 4 * half + 4; i += 2) lookup_pair(tb, W[i], W[i + 1], lc[i], lc[i + 1], s[half]);
     }
     lo = (s[0][0] + s[0][1]) + (s[0][2] + s[0][3]);
     hi = (s[1][0] + s[1][1]) + (s[1][2] + s[1][3]);
@@ -159,15 +169,10 @@ __device__ __forceinline__ void lookup_halves(lds_cchar* tb, const uint4& w0, co
 // The whole slice: one sum over the 32 groups.
 __device__ __forceinline__ float lookup_row(lds_cchar* tb, const uint4& w0, const uint4& w1, const uint32_t lc[8]) {
     const uint32_t W[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        s0 += *(const lds_f32*)(tb + perm_addr<0>(W[i], lc[i]));
-        s1 += *(const lds_f32*)(tb + perm_addr<1>(W[i], lc[i]));
-        s2 += *(const lds_f32*)(tb + perm_addr<2>(W[i], lc[i]));
-        s3 += *(const lds_f32*)(tb + perm_addr<3>(W[i], lc[i]));
-    }
-    return (s0 + s1) + (s2 + s3);
+    for (int i = 0; i < 8; i += 2) lookup_pair(tb, W[i], W[i + 1], lc[i], lc[i + 1], s);
+    return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -475,6 +480,14 @@ struct Unit {
     uint32_t xc;       // XL: idx of the staged column (read at staging, so nothing waits for it here)
     uint32_t xp;       // XL: idx of the column before it (for the ascending-order check)
 };
+
+// Register slots of the unit pipeline: a unit's loads are issued this many units ahead of its
+// lookups. Three at one or two activation rows, where a unit's work is shorter than a memory
+// round trip. Two at four rows of two row tiles: one unit's four passes outlast the round trip,
+// and the third slot's 23 registers put the instance at its 128-VGPR limit (measured cold, batch
+// 4, 3 bases: 8192 x 8192 27.6 -> 26.3 us, 28672 x 8192 68.4 -> 67.6 us).
+template <int RPL, int BMAX>
+constexpr int kSlots = (RPL == 2 && BMAX == 4) ? 2 : 3;
 
 // A unit within its segment's part of the list: row group, unit within the row group, and the
 // slice and base of the unit's first item (item 2 q), kept incrementally so that walking the
@@ -823,32 +836,37 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             fm = __builtin_amdgcn_readfirstlane(s_fm);  // uniform: the branches below are scalar
         }
         if (fm & 1u) return;  // a wait gave up: add nothing (workspace word 0 says so)
-        uint32_t sink = 0;
+        // The row sums (the two halves of each row added across the wave) go out in one of three
+        // ways, each a loop of its own: a value returned by an exchange must not reach the other
+        // two paths, or every flush would wait for all loads in flight (the units requested ahead).
+        auto put = [&](auto out) {
 #pragma unroll
-        for (int j = 0; j < RPL; ++j) {
-            const int rt = gr * RPL + j;
-            const int row = rt * kTileRows + rho;
-            const bool rv = rt < P.NT && row < a.N;
+            for (int j = 0; j < RPL; ++j) {
+                const int rt = gr * RPL + j;
+                const int row = rt * kTileRows + rho;
+                const bool rv = rt < P.NT && row < a.N;
 #pragma unroll
-            for (int b = 0; b < BMAX; ++b) {
-                if (b >= a.batch) continue;
-                const uint32_t pv = __float_as_uint(acc[j][b]);
-                const auto sw = __builtin_amdgcn_permlane32_swap(pv, pv, false, false);
-                const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                if (h == 0 && rv) {
-                    float* dst = a.y + (int64_t)b * a.N + row;
-                    if (fm & 2u)
-                        sink |= __float_as_uint(
-                            __hip_atomic_exchange(dst, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    else if (P.mode == kModeStore) *dst = total;
-                    else atomicAdd(dst, total);
+                for (int b = 0; b < BMAX; ++b) {
+                    if (b >= a.batch) continue;
+                    const uint32_t pv = __float_as_uint(acc[j][b]);
+                    const auto sw = __builtin_amdgcn_permlane32_swap(pv, pv, false, false);
+                    const float total = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                    if (h == 0 && rv) out(a.y + (int64_t)b * a.N + row, total);
                 }
             }
-        }
-        if (fm & 2u) {  // every row of the row group written: raise the flag once all have returned
-            asm volatile("" ::"v"(sink));
+        };
+        if (fm & 2u) {  // every row of the row group written with exchanges, then the flag raised
+            uint32_t sink = 0;
+            put([&](float* dst, float v) {
+                sink |= __float_as_uint(__hip_atomic_exchange(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            });
+            asm volatile("" ::"v"(sink));  // all of them have returned
             __syncthreads();
             if (tid == 0) raise_flag(gr);
+        } else if (P.mode == kModeStore) {
+            put([](float* dst, float v) { *dst = v; });
+        } else {
+            put([](float* dst, float v) { atomicAdd(dst, v); });
         }
     };
 
@@ -961,6 +979,7 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             const uint32_t left = (uint32_t)(US - cu.q);
             return hi - x < left ? hi - x : left;
         };
+        constexpr int NS = kSlots<RPL, BMAX>;
         Unit<XT, RPL, BMAX, XL> s0, s1, s2;
         // The candidate zeroer of the row group this run starts in is a run that starts among the
         // row group's first Q + 1 units of this segment (none when arrivers without units go
@@ -975,8 +994,10 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         if (!cand) enter(pcur.rg, run_units(lo, pcur));
         load_unit<SI, XL, GS>(s1, P, lcur, lo + 1 < hi, lcn, tid);
         advance(lcur, US, nb);
-        load_unit<SI, XL, GS>(s2, P, lcur, lo + 2 < hi, lcn, tid);
-        advance(lcur, US, nb);
+        if constexpr (NS == 3) {
+            load_unit<SI, XL, GS>(s2, P, lcur, lo + 2 < hi, lcn, tid);
+            advance(lcur, US, nb);
+        }
         if (cand) zero_if_first(pcur.rg);
         auto step = [&](const Unit<XT, RPL, BMAX, XL>& U, uint32_t x) {
             const bool last = x + 1 == hi || pcur.q + 1 == US;
@@ -984,16 +1005,27 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             advance(pcur, US, nb);
             if (last && x + 1 < hi) enter(pcur.rg, run_units(x + 1, pcur));
         };
-        for (uint32_t x = lo; x < hi; x += 3) {
-            step(s0, x);
-            load_unit<SI, XL, GS>(s0, P, lcur, x + 3 < hi, lcn, tid);
-            advance(lcur, US, nb);
-            if (x + 1 < hi) step(s1, x + 1);
-            load_unit<SI, XL, GS>(s1, P, lcur, x + 4 < hi, lcn, tid);
-            advance(lcur, US, nb);
-            if (x + 2 < hi) step(s2, x + 2);
-            load_unit<SI, XL, GS>(s2, P, lcur, x + 5 < hi, lcn, tid);
-            advance(lcur, US, nb);
+        if constexpr (NS == 3) {
+            for (uint32_t x = lo; x < hi; x += 3) {
+                step(s0, x);
+                load_unit<SI, XL, GS>(s0, P, lcur, x + 3 < hi, lcn, tid);
+                advance(lcur, US, nb);
+                if (x + 1 < hi) step(s1, x + 1);
+                load_unit<SI, XL, GS>(s1, P, lcur, x + 4 < hi, lcn, tid);
+                advance(lcur, US, nb);
+                if (x + 2 < hi) step(s2, x + 2);
+                load_unit<SI, XL, GS>(s2, P, lcur, x + 5 < hi, lcn, tid);
+                advance(lcur, US, nb);
+            }
+        } else {
+            for (uint32_t x = lo; x < hi; x += 2) {
+                step(s0, x);
+                load_unit<SI, XL, GS>(s0, P, lcur, x + 2 < hi, lcn, tid);
+                advance(lcur, US, nb);
+                if (x + 1 < hi) step(s1, x + 1);
+                load_unit<SI, XL, GS>(s1, P, lcur, x + 3 < hi, lcn, tid);
+                advance(lcur, US, nb);
+            }
         }
     };
     run(std::integral_constant<int, 0>{});
