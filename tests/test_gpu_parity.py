@@ -1085,11 +1085,14 @@ def test_matrix_core_vs_tables_16_rows(n, k, nb):
 
 
 @pytest.mark.parametrize("n,k,batch", [(9 * 256 + 37, 1500, 1), (23 * 256, 777, 1), (10 * 256, 2048, 3),
-                                       (17 * 256 - 5, 600, 4)])
+                                       (17 * 256 - 5, 600, 4), (8 * 256, 1500, 1), (16 * 256 - 100, 900, 2),
+                                       (24 * 256, 700, 4)])
 def test_xcd_local_row_groups_integer_exact(n, k, batch):
-    """y = result with 8 or more row groups runs with each row group on one XCD (its zeroing done
-    by the workgroup holding its first unit): every split over 8 .. 100000 workgroups, ragged row
-    groups per XCD, the refinement alone and main + refinement, NaN garbage overwritten, exact."""
+    """y = result with 8 or more row groups: each row group on one XCD, zeroed by a workgroup
+    without units at a lower ID (8, 16 and 24 row groups with up to 64 workgroups), or the
+    first-arriver protocol (row groups that do not divide over the 8 XCDs, or 100000 workgroups,
+    more than the device holds): every split, the refinement alone and main + refinement, NaN
+    garbage overwritten, exact."""
     rng = np.random.default_rng(n + k + batch)
     g = make_integer_gemv(rng, n, k, 2, s=max(1, k // 20), ns=2, batch=batch)
     packed, ps = pack(g.bits, k), pack(g.bits_s, g.s)

@@ -419,15 +419,16 @@ __global__ void k_extract4(const uint32_t* __restrict__ packed, int nb, int N, i
 //    each XCD's share in ID order. Row group rg is worked on only by workgroups on XCD rg mod 8,
 //    and zeroed by workgroup rg, which has no units, runs on that XCD and has a lower ID than
 //    every workgroup that adds into it: whenever one of those waits, workgroup rg has been
-//    allocated, and it zeroes the rows with atomic exchanges, waits for them and raises the
-//    flag without waiting for anything else. No zeroing waits for an atomic's answer first.
+//    allocated, and it zeroes the rows with device-scope atomic stores, waits until they are
+//    acknowledged and raises the flag without waiting for anything else. No zeroing waits for
+//    an atomic's answer first.
 //  * First-arriver mode (otherwise, e.g. grouped launches): the value the add returns says
 //    whether the workgroup arrived first, and the first arriver initializes the rows. A
 //    candidate (an arriver without units, or a run that starts among the row group's first
 //    units) makes its add before its loads and looks at the answer right away: if first, wave 0
-//    zeroes the rows, waits for the exchanges and raises the flag. Any other workgroup looks at
+//    zeroes the rows, waits for the stores and raises the flag. Any other workgroup looks at
 //    the answer only at its flush and, if it did arrive first, writes its own partial sums there
-//    with exchanges (every row of the row group) and then raises the flag. The first arriver is
+//    with atomic stores (every row of the row group) and then raises the flag. The first arriver is
 //    running (it made the add) and raises the flag without waiting for any other workgroup;
 //    every waiter arrived after it.
 // Either way nothing depends on how many workgroups the device holds at once, so launches on
@@ -696,14 +697,17 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
     auto read_flag = [&](int grg) -> uint32_t {
         return __hip_atomic_load(rg_word(grg) + kWsFlagOffset, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
+    // Wait until every memory operation this wave issued has completed (for stores: been
+    // acknowledged); vmcnt(0), the other counters left alone.
+    auto wait_stores = []() { __builtin_amdgcn_s_waitcnt(0x0F70); };
     auto raise_flag = [&](int grg) {
         __hip_atomic_fetch_add(rg_word(grg) + kWsFlagOffset, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     // Wave 0 of a row group's zeroing workgroup: y = 0 on every row of row group grg (all
-    // activation rows) with atomic exchanges, wait until all have returned (each has then been
-    // performed), raise the flag.
+    // activation rows) with device-scope atomic stores, wait until all have been acknowledged
+    // (each has then been performed where the adds are), raise the flag. (Exchanges, which must
+    // read each cold line first, took ~6.5 us under a full device's loads.)
     auto zero_rows = [&](int grg) {
-        uint32_t sink = 0;
 #pragma unroll
         for (int j = 0; j < RPL; ++j) {
             const int rt = grg * RPL + j;
@@ -714,11 +718,10 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
 #pragma unroll
                 for (int b = 0; b < BMAX; ++b)
                     if (rv && b < a.batch)
-                        sink |= __float_as_uint(__hip_atomic_exchange(a.y + (int64_t)b * a.N + row, 0.f,
-                                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                        __hip_atomic_store(a.y + (int64_t)b * a.N + row, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        asm volatile("" ::"v"(sink));
+        wait_stores();
         if (L == 0) raise_flag(grg);
     };
 
@@ -837,8 +840,9 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         }
         if (fm & 1u) return;  // a wait gave up: add nothing (workspace word 0 says so)
         // The row sums (the two halves of each row added across the wave) go out in one of three
-        // ways, each a loop of its own: a value returned by an exchange must not reach the other
-        // two paths, or every flush would wait for all loads in flight (the units requested ahead).
+        // ways, each a loop of its own, so that no path carries another's waits (a value returned
+        // by an atomic that could reach the other paths made every flush wait for all loads in
+        // flight, the units requested ahead).
         auto put = [&](auto out) {
 #pragma unroll
             for (int j = 0; j < RPL; ++j) {
@@ -855,12 +859,9 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
                 }
             }
         };
-        if (fm & 2u) {  // every row of the row group written with exchanges, then the flag raised
-            uint32_t sink = 0;
-            put([&](float* dst, float v) {
-                sink |= __float_as_uint(__hip_atomic_exchange(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            });
-            asm volatile("" ::"v"(sink));  // all of them have returned
+        if (fm & 2u) {  // every row of the row group written with atomic stores, then the flag raised
+            put([](float* dst, float v) { __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); });
+            wait_stores();  // all of them acknowledged
             __syncthreads();
             if (tid == 0) raise_flag(gr);
         } else if (P.mode == kModeStore) {
@@ -1201,11 +1202,17 @@ using plan::default_workgroups;
 // single-launch protocol cannot be used (no workspace, or too many arrivals per row group for
 // the counter's field).
 // The single-launch protocol runs in XCD-local mode (static zeroing by NRG workgroups without
-// units at the lowest IDs; see step_body) when allowed and every one of the eight XCDs gets
-// workgroups and row groups (Gu >= 8, NRG >= 8). Otherwise it runs in first-arriver mode,
+// units at the lowest IDs; see step_body) when allowed, every one of the eight XCDs gets
+// workgroups and the same number of row groups (Gu >= 8, NRG a multiple of 8), and the zeroing
+// workgroups fit on the device beside the others (Gu + NRG <= cap). Otherwise it runs in
+// first-arriver mode. (Measured cold with salient refinement, y = result: with workgroups beyond
+// the device's capacity the last ones start only when zeroers end, 70B gate 31.4 us vs 30.4 us
+// first-arriver; with 43 row groups, six on three XCDs and five on the others, 11008 x 4096 at
+// 4 rows 20.0 us vs 16.5 us; 4096 x 4096, all resident and balanced: 6.9 us vs 7.05 us.)
+// In first-arriver mode,
 // where with equal ranges (R = 0) and room on the device
 // (Gu + NRG <= cap) NRG arrivers without units go first (lowest IDs), one per row group: they
-// usually arrive first and zero, so no workgroup with units waits for the exchanges' round trip
+// usually arrive first and zero, so no workgroup with units waits for the zeroing's round trip
 // (measured on 4096 x 4096, 256 units, with such workgroups as zeroing owners: 5.84 -> 5.36 us).
 // With R > 0 such workgroups would crowd the CUs of the longer ranges (4096 x 4096 with 5%
 // salient columns, 272 units: 6.12 us without, 6.29 us with).
@@ -1227,7 +1234,8 @@ static hipError_t finish_params(StepParams& P, int64_t Gu, int64_t cap, bool all
         if (e != hipSuccess) return e;
         P.mode = kModeAtomic;
     }
-    if (P.mode == kModeFirst && allow_xcd && Gu >= kXcds && P.NRG >= kXcds) {
+    if (P.mode == kModeFirst && allow_xcd && Gu >= kXcds && P.NRG >= kXcds && P.NRG % kXcds == 0 &&
+        Gu + P.NRG <= cap) {
         P.xmode = 1;
         P.Zn = (int)ceil_div(P.NRG, kXcds) * kXcds;  // keeps unit workgroup g - Zn on the XCD of g
     } else if (P.mode == kModeFirst && R == 0 && Gu + P.NRG <= cap) {
