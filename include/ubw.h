@@ -62,9 +62,10 @@ typedef enum {
 enum { UBW_F32 = 0, UBW_F16 = 1 };                       /* activation dtypes */
 enum { UBW_SRC_CANON_BITS = 0, UBW_SRC_INT8_SIGNS = 1 };  /* ubw_pack_bases sources */
 
-/* Largest batch one GEMV call accepts. Batches of 7 rows or more (5 or more when
- * batch * nb * N * K >= 2^30) run in one launch on the
- * matrix cores when the call has per-row scales and at most six bases (main + refinement): the
+/* Largest batch one GEMV call accepts. At group width 8 a batch runs in one launch on the
+ * matrix cores when that is predicted to be faster than the tables (a cost model of both paths in
+ * the weight bytes and the rows: from 5 to 9 rows on, depending on the matrix size) and the call
+ * has per-row scales and at most six bases (main + refinement): the
  * sign bits are expanded to fp16 +-1 and v = alpha_c * x is split into fp16 high and low parts
  * (round toward zero each), so that per element |v - hi - lo| < 2^-20 |v| + 2^-38 m, m the
  * largest |v| of that activation row within the 256-column slice, against the tables' fp32 v

@@ -92,6 +92,30 @@ static void check_wg_range(std::mt19937_64& rng) {
     }
 }
 
+// Path choice: the tables up to 4 rows (one launch) at any size, the matrix cores from 9 rows on,
+// the crossover between them falling as the matrix grows (never back to the tables with more
+// weights or more rows), and the measured crossovers of the fitted shapes.
+static void check_path_choice(std::mt19937_64& rng) {
+    for (int it = 0; it < 20000; ++it) {
+        const int64_t wb = (int64_t)rnd(rng, 1, (uint64_t)1 << (it % 2 ? 24 : 34));
+        for (int b = 1; b <= 16; ++b) {
+            const bool m = prefer_mfma(wb, b);
+            if (b <= 4) CHECK(!m, "matrix cores at %d rows, %lld bytes", b, (long long)wb);
+            if (b >= 9) CHECK(m, "tables at %d rows, %lld bytes", b, (long long)wb);
+            if (m && b < 16) CHECK(prefer_mfma(wb, b + 1), "back to the tables at %d rows", b + 1);
+            if (m) CHECK(prefer_mfma(wb * 2, b), "back to the tables at %lld bytes", (long long)wb * 2);
+        }
+    }
+    struct Case {
+        int64_t bytes;
+        int tables_up_to;  // the largest batch that stays on the tables
+    } cases[] = {{91750400, 4}, {91226112, 4}, {26214400, 5}, {11976704, 6}, {12058624, 6}, {4456448, 7},
+                 {3276800, 7}};
+    for (const Case& c : cases)
+        for (int b = 1; b <= 16; ++b)
+            CHECK(prefer_mfma(c.bytes, b) == (b > c.tables_up_to), "%lld bytes at %d rows", (long long)c.bytes, b);
+}
+
 static void check_default_workgroups(std::mt19937_64& rng) {
     for (int it = 0; it < 20000; ++it) {
         const int64_t cap = 2 * (int64_t)rnd(rng, 1, 1024);
@@ -192,6 +216,7 @@ int main() {
     std::mt19937_64 rng(20260805);
     check_fast_div(rng);
     check_wg_range(rng);
+    check_path_choice(rng);
     check_default_workgroups(rng);
     check_rows4(rng);
     check_validation(rng);

@@ -985,7 +985,8 @@ def test_fp32_activations_in_variants(batch):
 
 
 # ------------------------------------------------------------------------------------------
-# batches of 7+ rows on the matrix cores (default path) vs the tables (explicit geometry)
+# batches the path model sends to the matrix cores (default path) vs the tables (explicit geometry):
+# from 9 rows at any size, from 7 rows above ~6.4 MB of weights, from 8 rows above ~3 MB
 
 @pytest.mark.parametrize("n,k,nb,s,ns,batch,xdt,xscale", [
     (300, 200, 2, 0, 0, 9, np.float16, 1.0),         # one slice: one chunk, plain stores
@@ -993,8 +994,8 @@ def test_fp32_activations_in_variants(batch):
     (777, 1501, 3, 100, 3, 9, np.float32, 1e-5),     # tiny activations: staging scale > 1
     (4100, 700, 1, 37, 1, 12, np.float16, 1.0),      # many row tiles, ragged last tile
     (256, 4096, 2, 205, 2, 16, np.float16, 1.0),     # one row tile, many chunks
-    (513, 2049, 2, 60, 2, 7, np.float16, 1.0),       # fewest rows on the matrix cores
-    (1030, 777, 3, 45, 1, 8, np.float32, 1.0),       # 8 rows, ragged slices and tiles
+    (4100, 6000, 3, 300, 2, 7, np.float16, 1.0),     # 7 rows (9.2 MB of weights), ragged last tile
+    (3100, 4500, 2, 45, 1, 8, np.float32, 1.0),      # 8 rows (3.5 MB), ragged slices and tiles
 ])
 def test_matrix_core_batches_match_oracle(n, k, nb, s, ns, batch, xdt, xscale):
     rng = np.random.default_rng(n + k + batch)

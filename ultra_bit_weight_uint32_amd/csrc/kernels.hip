@@ -1419,8 +1419,10 @@ static hipError_t launch_step_rows(const StepArgs& a, hipStream_t s) {
 }
 
 static bool use_mfma(const StepArgs& a) {
-    if (a.tables_only || a.batch < kMfmaMinBatchLarge || !mfma_step_supported(a)) return false;
-    return a.batch >= kMfmaMinBatch || (int64_t)a.batch * a.seg[0].nb * a.N * a.seg[0].Kv >= kMfmaLargeWork;
+    if (a.tables_only || !mfma_step_supported(a)) return false;
+    int64_t bits = 0;
+    for (int i = 0; i < a.nseg; ++i) bits += (int64_t)a.seg[i].nb * a.N * a.seg[i].Kv;
+    return plan::prefer_mfma(bits / 8, a.batch);
 }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t s) {

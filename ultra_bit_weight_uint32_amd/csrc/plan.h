@@ -80,6 +80,34 @@ inline int64_t default_workgroups(int64_t U, int64_t cap, int batch) {
     return cap;
 }
 
+// ---- which path a GEMV of b activation rows takes: the one predicted to be faster. Each path's
+// time is linear in the weight bytes W (MB, main + refinement bases) and in the rows, with
+// coefficients fitted (least squares on relative error) to cold timings of both paths on seven
+// shapes (4096 x 4096 to 28672 x 8192 and 8192 x 28672, 2-3 bases, 5% salient columns in 2
+// bases, fp16 x, y = result) at 1-16 rows. Tables: one launch of r <= 4 rows, a batch as
+// consecutive launches of 4. Matrix cores: one launch of any b <= 16. Within 10% of the
+// measurements except the 1024-row shape (up to 17%); the faster path chosen in 76 of 77 cases
+// (the miss: 1024 x 8192 at 8 rows, 0.24 us).
+struct PathCost {
+    double c0, c1, w0, w1;  // c0 + c1 (r - 1) + W (w0 + w1 (r - 1)) us
+};
+constexpr PathCost kTablesCost{6.228, 1.178, 0.27510, 0.10751};
+constexpr PathCost kMfmaCost{17.788, 0.415, 0.67806, 0.01765};
+inline double path_us(const PathCost& c, double W, int r) {
+    return c.c0 + c.c1 * (r - 1) + W * (c.w0 + c.w1 * (r - 1));
+}
+inline double tables_us(double W, int b) {
+    double t = 0.0;
+    for (; b > 0; b -= 4) t += path_us(kTablesCost, W, b < 4 ? b : 4);
+    return t;
+}
+inline double mfma_us(double W, int b) { return path_us(kMfmaCost, W, b); }
+// weight_bytes: packed bytes of every base of the GEMV (main and refinement)
+inline bool prefer_mfma(int64_t weight_bytes, int b) {
+    const double W = (double)weight_bytes * 1e-6;
+    return mfma_us(W, b) < tables_us(W, b);
+}
+
 // ---- group width 4: 32 chunks per row (32 / nb per base), C columns each.
 struct R4Chunk {
     bool ok;
