@@ -383,6 +383,28 @@ def test_progress_beyond_device_capacity():
         assert ubw.workspace_check(ws) == (ubw.UBW_OK, 0), wgs
 
 
+def test_workspace_error_word_decoding():
+    """The workspace error word as ubw_workspace_check reports it, bits written from the host (no
+    wait is made to run out): bit 0 -> UBW_EWAIT (a wait gave up; it wins over bit 1), bit 1 ->
+    UBW_ERANGE, clear=True zeroes the word; a valid GEMV into that workspace leaves a set bit as
+    it is (the word is sticky until cleared) and still writes the right y."""
+    rng = np.random.default_rng(91)
+    g = make_integer_gemv(rng, 777, 900, 2, s=45, ns=1, batch=1)
+    ws = ubw.workspace(777, DEV)
+    for word, status in ((1, ubw.UBW_EWAIT), (2, ubw.UBW_ERANGE), (3, ubw.UBW_EWAIT)):
+        ws[0] = word
+        assert ubw.workspace_check(ws) == (status, word)
+        assert ubw.workspace_check(ws, clear=True) == (status, word)
+        assert ubw.workspace_check(ws) == (ubw.UBW_OK, 0)
+    ws[0] = 2
+    y = ubw.lut_gemv_refined(pack(g.bits, g.k), dev(g.alpha_r), dev(g.alpha_c), dev(g.idx), pack(g.bits_s, g.s),
+                             dev(g.alpha_r_s), dev(g.alpha_c_s), dev(g.x), g.n, g.k,
+                             y=torch.full((1, 777), float("nan"), device=DEV), workspace=ws)
+    assert np.array_equal(host(y).astype(np.float64), oracle_gemv(g))
+    assert ubw.workspace_check(ws, clear=True) == (ubw.UBW_ERANGE, 2)
+    assert ubw.workspace_check(ws) == (ubw.UBW_OK, 0)
+
+
 def test_concurrent_streams_separate_workspaces():
     """Two streams, each with its own workspace, issue full-device y = result launches at the same
     time: the 4096 x 4096 step (2 bases + 205 salient columns) and a 70B gate (28672 x 8192,
