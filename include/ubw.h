@@ -23,14 +23,17 @@
  *     layout of ubw_packed_words() uint32 words. Tiles of 256 rows x 256 columns per base;
  *     padding rows and columns are zero. Only this library reads it.
  *   - Group width g: the number of columns one pattern index covers (tables of 2^g entries).
- *     ubw_lut_gemv and ubw_vcm_gather_refine take g = 8. ubw_build_lut and
- *     ubw_extract_patterns take g = 4 or 8.
+ *     Every call takes g = 4 or 8 (ubw_lut_gemv_multi and ubw_lut_gemv_gs: 8 only). At g = 8
+ *     the GEMV splits K over workgroups; at g = 4 a workgroup owns whole rows (the 16-entry
+ *     tables of a full row fit in its LDS), for the shapes listed at ubw_lut_gemv.
  *   - Scalars: alpha_r [nb][N] and alpha_c [nb][K] fp32, row-major; y [batch][N] fp32.
  *   - Activations x [batch][K], fp16 (UBW_F16) or fp32 (UBW_F32), row-major.
  *   - Pointers are device pointers unless a comment says otherwise. The caller allocates
- *     and owns every buffer; the library allocates nothing. Its only process-wide state is a
+ *     and owns every buffer; the library allocates nothing. Its process-wide state is a
  *     per-device cache of how many workgroups of each kernel a device holds at once (filled
- *     on first use, thread-safe).
+ *     on first use, thread-safe) and the static device array that
+ *     ubw_lut_gemv_refined_noalloc uses as its workspace (one per device, loaded with the
+ *     library).
  *   - stream is a hipStream_t (NULL = the default stream). Every call only enqueues work on
  *     it and returns; results are ready when the stream is synchronized.
  *   - Return value: UBW_OK (0) or a negative ubw_status. Arguments are validated on the host
