@@ -403,8 +403,8 @@ __global__ void k_extract4(const uint32_t* __restrict__ packed, int nb, int N, i
 // Per unit and activation row b: stage v = alpha_c * x for both items, build each item's 32
 // tables (half h writes LDS columns 32 h .. 32 h + 31), barrier, look up every owned row,
 // accumulate alpha_r * sum, barrier. The two halves of a row (different items) are added with a
-// cross-lane swap when flushing. The data of the next three units are in flight while a unit
-// is processed (three register slots, reloaded in place).
+// cross-lane swap when flushing. The next unit's data are in flight while a unit is processed
+// (two register slots, reloaded in place).
 //
 // y = result in one launch (kModeFirst, with a workspace). Per row group, 256 bytes of
 // workspace: word 0 counts arrivals, (generation << 12) | units announced in this launch, and
@@ -481,14 +481,6 @@ struct Unit {
     uint32_t xc;       // XL: idx of the staged column (read at staging, so nothing waits for it here)
     uint32_t xp;       // XL: idx of the column before it (for the ascending-order check)
 };
-
-// Register slots of the unit pipeline: a unit's loads are issued this many units ahead of its
-// lookups. Three at one or two activation rows, where a unit's work is shorter than a memory
-// round trip. Two at four rows of two row tiles: one unit's four passes outlast the round trip,
-// and the third slot's 23 registers put the instance at its 128-VGPR limit (measured cold, batch
-// 4, 3 bases: 8192 x 8192 27.6 -> 26.3 us, 28672 x 8192 68.4 -> 67.6 us).
-template <int RPL, int BMAX>
-constexpr int kSlots = (RPL == 2 && BMAX == 4) ? 2 : 3;
 
 // A unit within its segment's part of the list: row group, unit within the row group, and the
 // slice and base of the unit's first item (item 2 q), kept incrementally so that walking the
@@ -959,8 +951,8 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         }
     };
 
-    // The run of segment SI's units in [x0, x1). Three register slots, each reloaded in place
-    // three units ahead (no copies between slots, which would wait on loads still in flight);
+    // The run of segment SI's units in [x0, x1). Two register slots, each reloaded in place two
+    // units ahead (no copies between slots, which would wait on loads still in flight);
     // loads past the run are issued with valid = false and read nothing, so every path issues
     // the same loads. The run's first arrival is made before its loads, so that a first arriver
     // learns it (and zeroes) without waiting for them.
@@ -980,8 +972,14 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             const uint32_t left = (uint32_t)(US - cu.q);
             return hi - x < left ? hi - x : left;
         };
-        constexpr int NS = kSlots<RPL, BMAX>;
-        Unit<XT, RPL, BMAX, XL> s0, s1, s2;
+        // Two register slots: a unit's loads are issued while the unit before it is processed.
+        // (A third slot, loads two units ahead, lost everywhere it was measured, cold: the 4096 x
+        // 4096 step 6.95 -> 6.28 us and main only 6.06 -> 5.53 us with two, 11008 x 4096 with
+        // refinement 8.9 -> 8.1 us, the 70B gate 30.6 -> 28.8 us, 8192 x 8192 13.8 -> 12.4 us.
+        // At launch every workgroup requests its slots' units at once; per-workgroup timestamps
+        // on the 70B gate had the later-dispatched half of the workgroups waiting behind that
+        // burst, and the third slot's registers cost the instances their scheduling room.)
+        Unit<XT, RPL, BMAX, XL> s0, s1;
         // The candidate zeroer of the row group this run starts in is a run that starts among the
         // row group's first Q + 1 units of this segment (none when arrivers without units go
         // first): it announces its arrival before its loads and looks at the answer as soon as
@@ -995,10 +993,6 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         if (!cand) enter(pcur.rg, run_units(lo, pcur));
         load_unit<SI, XL, GS>(s1, P, lcur, lo + 1 < hi, lcn, tid);
         advance(lcur, US, nb);
-        if constexpr (NS == 3) {
-            load_unit<SI, XL, GS>(s2, P, lcur, lo + 2 < hi, lcn, tid);
-            advance(lcur, US, nb);
-        }
         if (cand) zero_if_first(pcur.rg);
         auto step = [&](const Unit<XT, RPL, BMAX, XL>& U, uint32_t x) {
             const bool last = x + 1 == hi || pcur.q + 1 == US;
@@ -1006,27 +1000,13 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             advance(pcur, US, nb);
             if (last && x + 1 < hi) enter(pcur.rg, run_units(x + 1, pcur));
         };
-        if constexpr (NS == 3) {
-            for (uint32_t x = lo; x < hi; x += 3) {
-                step(s0, x);
-                load_unit<SI, XL, GS>(s0, P, lcur, x + 3 < hi, lcn, tid);
-                advance(lcur, US, nb);
-                if (x + 1 < hi) step(s1, x + 1);
-                load_unit<SI, XL, GS>(s1, P, lcur, x + 4 < hi, lcn, tid);
-                advance(lcur, US, nb);
-                if (x + 2 < hi) step(s2, x + 2);
-                load_unit<SI, XL, GS>(s2, P, lcur, x + 5 < hi, lcn, tid);
-                advance(lcur, US, nb);
-            }
-        } else {
-            for (uint32_t x = lo; x < hi; x += 2) {
-                step(s0, x);
-                load_unit<SI, XL, GS>(s0, P, lcur, x + 2 < hi, lcn, tid);
-                advance(lcur, US, nb);
-                if (x + 1 < hi) step(s1, x + 1);
-                load_unit<SI, XL, GS>(s1, P, lcur, x + 3 < hi, lcn, tid);
-                advance(lcur, US, nb);
-            }
+        for (uint32_t x = lo; x < hi; x += 2) {
+            step(s0, x);
+            load_unit<SI, XL, GS>(s0, P, lcur, x + 2 < hi, lcn, tid);
+            advance(lcur, US, nb);
+            if (x + 1 < hi) step(s1, x + 1);
+            load_unit<SI, XL, GS>(s1, P, lcur, x + 3 < hi, lcn, tid);
+            advance(lcur, US, nb);
         }
     };
     run(std::integral_constant<int, 0>{});
