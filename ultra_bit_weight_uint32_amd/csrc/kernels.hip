@@ -7,21 +7,23 @@
 // indices with bit operations -> fetch precomputed partial sums -> apply alpha_r.
 //
 // gfx950 mapping (the page's kernel targets another GPU; only its dataflow is kept):
-//   - a workgroup of 256 threads owns 256-row tiles x 256-column slices; each lane owns one row
-//     of a tile and walks the slice's 32 groups of 8 columns, for two bases at a time;
-//   - a group table has 256 fp32 entries, all in one LDS bank: entry p of group x of base
-//     k (k = 0, 1 within the pair) lives at byte 256 p + 128 k + 4 x, so the two bases' tables
-//     of a slice fill one 64 KiB block and every table sits in bank x;
-//   - the lane with l = lane mod 32 reads group (l + t) mod 32 at step t, so each half-wave
-//     touches 32 distinct banks per lookup (the LDS serves a wave64 access as two 32-lane
-//     halves over 32 banks);
+//   - a workgroup of 512 threads works through a contiguous range of units (stream-K); a unit is
+//     one or more 256-row tiles x two (256-column slice, base) items, one per half of each wave,
+//     each lane owning one row of the tile;
+//   - a group table has 256 fp32 entries, all in one LDS bank: entry p of group x of item h
+//     lives at byte 256 p + 128 h + 4 x, so a unit's 64 tables fill one 64 KiB block and every
+//     table sits in bank x;
+//   - the lane with l = lane mod 32 reads group t ^ l at step t, and the packer stores each row's
+//     words and bytes in the matching XOR order, so each half-wave touches 32 distinct banks per
+//     lookup and the pattern byte sits where the lookup reads it;
 //   - the lookup address is one v_perm_b32 that puts the weight byte (the pattern) in byte 1
-//     and the lane's column offset for that step in byte 0; a v_alignbyte_b32 per 4 lookups
-//     supplies the lane's rotated byte order;
-//   - slices of one row are combined with fp32 atomics; when the caller asks for y = result the
-//     first workgroup to arrive at a row group zeroes those rows and the others wait for its
-//     flag before adding (atomics only, no fences), so one launch does the whole step;
-//   - no MFMA: the work is a memory-bound table-lookup reduction.
+//     and the lane's column offset for that step in byte 0;
+//   - slices of one row are combined with fp32 atomics; when the caller asks for y = result, the
+//     rows of each row group are initialized once per launch (by a zeroing workgroup with a lower
+//     ID on the same XCD, or by the first workgroup to arrive) and the others wait for its flag
+//     before adding (atomics only, no fences), so one launch does the whole step;
+//   - no MFMA in this file: the work is a memory-bound table-lookup reduction (larger batches
+//     go to the matrix-core kernel in mfma.hip).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 

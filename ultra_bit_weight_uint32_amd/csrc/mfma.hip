@@ -1,6 +1,7 @@
 // The GEMV step for several activation rows at once on the matrix cores.
 //
-// "FluxBin" technical summary, "1. Algorithm innovation" and "2. Kernel design": each base is
+// FluxBin (gist.science/ko/paper/2608.15602), technical summary, "1. Algorithm innovation" and
+// "2. Kernel innovation": each base is
 // (alpha_r alpha_c^T) (.) B with B in {-1,+1}, so y_b = sum_k alpha_r^(k) (.) (B^(k) v_b^(k)) with
 // v_b^(k) = alpha_c^(k) (.) x_b. The page's table lookup replaces the multiply-adds of one
 // activation row; with several rows the tables must be built and searched once per row, while
