@@ -540,6 +540,22 @@ def test_large_matrix_five_and_six_rows():
             assert max_rel_err(gpu_gemv(gb), oracle_gemv(gb)) <= TOL, (name, b)
 
 
+@pytest.mark.parametrize("name,n,k,nb,s,batches", [
+    ("7B up", 11008, 4096, 2, 205, (6, 7)),        # tables at 6 rows, matrix cores at 7
+    ("4096 sq", 4096, 4096, 2, 205, (7, 8)),       # tables at 7, matrix cores at 8
+    ("70B k", 1024, 8192, 3, 410, (7, 8)),         # tables at 7, matrix cores at 8
+])
+def test_path_model_crossovers(name, n, k, nb, s, batches):
+    """Each side of the path model's crossover for three shapes (the batch before it runs on the
+    tables, the batch at it on the matrix cores): every output against the oracle, with salient
+    refinement, y = result through the workspace."""
+    rng = np.random.default_rng(n + k + nb)
+    g = make_gemv(rng, name, n, k, nb, s=s, ns=2, batch=max(batches))
+    for b in batches:
+        gb = g.with_batch(b)
+        assert max_rel_err(gpu_gemv(gb), oracle_gemv(gb)) <= TOL, (name, b)
+
+
 def test_decoder_layer_70b_full():
     """Every output of all seven 70B-shaped GEMVs (q/k/v/o, gate/up/down; 3 bases + 5% salient
     columns in 2 bases) at batch 1 (tables) and 16 (matrix cores) against the oracle."""
