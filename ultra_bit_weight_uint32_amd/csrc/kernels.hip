@@ -480,8 +480,10 @@ struct Unit {
     float ac;          // staging: alpha_c of the staged item's base at the staged column
     XT xv[BMAX];       // staging: activations of the staged column (0 for rows >= batch)
     uint4 xb;          // XL: this thread's 16 bytes of the activation block
-    uint32_t xc;       // XL: idx of the staged column (read at staging, so nothing waits for it here)
-    uint32_t xp;       // XL: idx of the column before it (for the ascending-order check)
+    uint32_t xc;       // idx of the staged column (XL: read at staging; otherwise at the gather, one
+                       // unit later, so nothing waits for it at the load)
+    uint32_t xp;       // idx of the column before it (for the ascending-order check)
+    uint32_t xf;       // without XL: bit 0 the staged column is valid, bit 1 it is not column 0
 };
 
 // A unit within its segment's part of the list: row group, unit within the row group, and the
@@ -553,8 +555,8 @@ __device__ __forceinline__ void buf_x(Rsrc r, uint32_t off, __half& v) {
 // compiler's waits stay exact: a unit waits for its own data only, never for the units requested
 // after it. Order: alpha_c and x first (for idx segments: idx, alpha_c and, with XL, the whole
 // activation block), so the tables can be built while the weights are still arriving; then the
-// weights and alpha_r; for idx segments without XL the gather of x last, so that only it waits
-// for idx. A unit past the run (!valid) issues the
+// weights and alpha_r; for idx segments without XL the gather of x follows later (gather_unit),
+// once idx is in. A unit past the run (!valid) issues the
 // same loads through empty descriptors: they read nothing. (Branching around them instead
 // makes the compiler merge two register assignments with copies that wait for everything.)
 // Per-lane constants of the loads, computed once: a unit's offsets are then a scalar (uniform)
@@ -585,22 +587,17 @@ __device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const Step
     const bool its_ok = 2 * cu.q + (int)lcn.sd < nitems;
     const uint32_t colBase = (uint32_t)sks * kSliceCols;
     const bool cvalid = its_ok && colBase + lcn.colL < (uint32_t)sg.Kv;
-    // idx of the staged column and of the one before it (for the checks); with XL they are loaded
-    // straight into the unit and checked at staging (a copy of a value still in flight would wait
-    // for it), otherwise checked below, where the gather waits for them anyway
+    // idx of the staged column and of the one before it (for the checks), loaded straight into
+    // the unit (a copy of a value still in flight would wait for it) and checked where they are
+    // used: at staging with XL, otherwise at the gather (gather_unit)
     const uint32_t col = colBase + lcn.colL;
-    uint32_t raw = 0, rawp = 0;
     if constexpr (SI == 1) {
         const Rsrc r_idx = make_rsrc(sg.idx, valid ? (uint32_t)sg.Kv * 4u : 0u);
         const int ioff = (int)(cvalid ? col * 4u : kOob);
         const int poff = (int)(cvalid && col > 0 ? col * 4u - 4u : kOob);
-        if constexpr (XL) {
-            U.xc = __builtin_amdgcn_raw_buffer_load_b32(r_idx, ioff, 0, 0);
-            U.xp = __builtin_amdgcn_raw_buffer_load_b32(r_idx, poff, 0, 0);
-        } else {
-            raw = __builtin_amdgcn_raw_buffer_load_b32(r_idx, ioff, 0, 0);
-            rawp = __builtin_amdgcn_raw_buffer_load_b32(r_idx, poff, 0, 0);
-        }
+        U.xc = __builtin_amdgcn_raw_buffer_load_b32(r_idx, ioff, 0, 0);
+        U.xp = __builtin_amdgcn_raw_buffer_load_b32(r_idx, poff, 0, 0);
+        if constexpr (!XL) U.xf = (valid && cvalid ? 1u : 0u) | (col > 0 ? 2u : 0u);
     }
     const uint32_t acBase = ((uint32_t)sk * (uint32_t)sg.Kv + colBase) * 4u;
     U.ac = buf_f32(make_rsrc(sg.alpha_c, valid ? (uint32_t)sg.nb * (uint32_t)sg.Kv * 4u : 0u),
@@ -633,16 +630,28 @@ __device__ __forceinline__ void load_unit(Unit<XT, RPL, BMAX, XL>& U, const Step
         const uint32_t row = (uint32_t)rt * kTileRows + lcn.rho;
         U.ar[j] = buf_f32(r_ar, lval && row < (uint32_t)a.N ? arBase + row * 4u : kOob);
     }
-    if constexpr (SI == 1 && !XL) {
-        // VCM: the index must lie in [0, K) and exceed the one before it (ascending, distinct);
-        // either fault sets bit 1 of workspace word 0, and a column outside [0, K) reads nothing
-        // (x = 0, so it contributes nothing; one out of order still adds x[idx])
-        const bool bad = valid && cvalid && (raw >= ldx || (col > 0 && (int)rawp >= (int)raw));
-        if (bad && a.ws != nullptr) atomicOr(a.ws, kWsErrIndex);
-        const bool use = cvalid && raw < ldx;
+}
+
+// The refinement's activations without XL: x at the staged column's index, loaded once idx has
+// arrived. It is issued while the unit before is processed (after that unit's staging), so no
+// load waits for idx: a gather issued with the unit's own loads waited for idx at once, one
+// memory round trip per refinement unit. VCM: the index must lie in [0, K) and exceed the one
+// before it (ascending, distinct); either fault sets bit 1 of workspace word 0, and a column
+// outside [0, K) reads nothing (x = 0, so it contributes nothing; one out of order still adds
+// x[idx]).
+template <typename XT, int RPL, int BMAX, bool XL>
+__device__ __forceinline__ void gather_unit(Unit<XT, RPL, BMAX, XL>& U, const StepParams& P) {
+    static_assert(!XL, "with XL the gather reads the activation block in LDS at staging");
+    const StepArgs& a = P.a;
+    const uint32_t ldx = (uint32_t)a.ldx;
+    const uint32_t xs = sizeof(XT);
+    const bool cvalid = (U.xf & 1u) != 0;
+    const bool bad = cvalid && (U.xc >= ldx || ((U.xf & 2u) != 0 && (int)U.xp >= (int)U.xc));
+    if (bad && a.ws != nullptr) atomicOr(a.ws, kWsErrIndex);
+    const bool use = cvalid && U.xc < ldx;
+    const Rsrc r_x = make_rsrc(a.x, (uint32_t)a.batch * ldx * xs);
 #pragma unroll
-        for (int b = 0; b < BMAX; ++b) buf_x(r_x, use ? ((uint32_t)b * ldx + raw) * xs : kOob, U.xv[b]);
-    }
+    for (int b = 0; b < BMAX; ++b) buf_x(r_x, use ? ((uint32_t)b * ldx + U.xc) * xs : kOob, U.xv[b]);
 }
 
 // The body of a step: workgroup g of the P.G that work on the GEMV described by P.
@@ -906,7 +915,8 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
 
     // One unit: stage, then one table build + lookup pass per activation row; flush if it is
     // the last unit of its row group in this run.
-    auto process = [&](const Unit<XT, RPL, BMAX, XL>& U, int nitems, Cursor cu, bool last, auto si_c) {
+    auto process = [&](const Unit<XT, RPL, BMAX, XL>& U, int nitems, Cursor cu, bool last, auto si_c,
+                       auto&& after_stage) {
         constexpr int SI = decltype(si_c)::value;
         const bool mine = 2 * cu.q + h < nitems;  // this half has an item in this unit
         // scaled activations of both items: v = alpha_c * x (LUT-BSF folds alpha_c here)
@@ -936,6 +946,7 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             for (int b = 0; b < BMAX; ++b)
                 if (b < a.batch) sv[b * 512 + tid] = U.ac * to_f32(U.xv[b]);
         }
+        after_stage();
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < BMAX; ++b) {
@@ -996,17 +1007,24 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
         load_unit<SI, XL, GS>(s1, P, lcur, lo + 1 < hi, lcn, tid);
         advance(lcur, US, nb);
         if (cand) zero_if_first(pcur.rg);
-        auto step = [&](const Unit<XT, RPL, BMAX, XL>& U, uint32_t x) {
+        // The refinement without XL gathers a unit's activations once its idx is in: the first
+        // unit's here, every later one's after the staging of the unit before it.
+        constexpr bool deferred = SI == 1 && !XL;
+        auto gather = [&](Unit<XT, RPL, BMAX, XL>& V) {
+            if constexpr (deferred) gather_unit(V, P);
+        };
+        gather(s0);
+        auto step = [&](const Unit<XT, RPL, BMAX, XL>& U, uint32_t x, Unit<XT, RPL, BMAX, XL>& next) {
             const bool last = x + 1 == hi || pcur.q + 1 == US;
-            process(U, nitems, pcur, last, si_c);
+            process(U, nitems, pcur, last, si_c, [&]() { gather(next); });
             advance(pcur, US, nb);
             if (last && x + 1 < hi) enter(pcur.rg, run_units(x + 1, pcur));
         };
         for (uint32_t x = lo; x < hi; x += 2) {
-            step(s0, x);
+            step(s0, x, s1);
             load_unit<SI, XL, GS>(s0, P, lcur, x + 2 < hi, lcn, tid);
             advance(lcur, US, nb);
-            if (x + 1 < hi) step(s1, x + 1);
+            if (x + 1 < hi) step(s1, x + 1, s0);
             load_unit<SI, XL, GS>(s1, P, lcur, x + 3 < hi, lcn, tid);
             advance(lcur, US, nb);
         }
