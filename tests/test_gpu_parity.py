@@ -315,14 +315,17 @@ def drop_positions(g, positions):
     return h
 
 
-@pytest.mark.parametrize("batch", [1, 3, 9])
-def test_vcm_index_checks(batch):
+@pytest.mark.parametrize("batch,k", [(1, 900), (3, 900), (9, 900), (1, 904), (2, 904)])
+def test_vcm_index_checks(batch, k):
     """Salient indices are checked on the device: an index outside [0, K) or not above the one
     before it is reported in workspace word 0 (UBW_ERANGE); a column outside [0, K) contributes
     nothing, one out of order still adds its term (the oracle's sum takes any order); a valid
-    list reports nothing. Batch 9 runs on the matrix cores, 1 and 3 on the tables."""
-    rng = np.random.default_rng(23 + batch)
-    n, k, s = 260, 900, 90
+    list reports nothing. Batch 9 runs on the matrix cores, 1 to 3 on the tables: with K = 900
+    the activation block (1800 or 5400 bytes, not a multiple of 16) is gathered from memory
+    through idx one unit after idx is loaded; with K = 904 (1808 or 3616 bytes) the whole block
+    is staged in LDS and gathered there."""
+    rng = np.random.default_rng(23 + batch + k)
+    n, s = 260, 90
     g = make_integer_gemv(rng, n, k, 1, s=s, ns=2, batch=batch)
     ok_ws = ubw.workspace(n, DEV)
     want = oracle_gemv(g)
