@@ -23,9 +23,11 @@
 // with its own count (its workgroups beyond it exit at once).
 // Workgroup (row tile rt, chunk kc): 256 threads, 4 waves, wave w owns tile rows 64 w .. +63 as
 // four 16-row blocks. For each base and each 256-column slice of the chunk:
-//   * the packed words of the wave's rows are loaded (the tile layout: row rho's 8 words as two
-//     16-byte halves, slot s holding canonical word s ^ ((rho & 31) >> 2) with bytes permuted by
-//     rho & 3); each lane takes the canonical byte g = lane / 16 of every word of its row,
+//   * the packed words of the wave's rows are loaded once (the tile layout: row rho's 8 words as
+//     two 16-byte halves, slot s holding canonical word s ^ ((rho & 31) >> 2) with bytes permuted
+//     by rho & 3): lane (g = lane / 16, r16) loads slots 2 g and 2 g + 1 of its row, and the four
+//     lanes of a row trade bytes with two cross-lane swaps until each holds the canonical byte g
+//     of every word of its row,
 //   * v = alpha_c * x for the slice's 256 columns and up to 16 activation rows goes to LDS as
 //     fp16 hi and lo (each thread a row's 8 column pairs 32 i + 2 cg, so that the 16 threads
 //     of a row read consecutive columns),
@@ -109,9 +111,9 @@ __device__ __forceinline__ Rsrc rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 __device__ __forceinline__ uint32_t ld32(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0); }
-__device__ __forceinline__ uint4 ld128(Rsrc r, uint32_t off) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ uint2 ld64(Rsrc r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return make_uint2(v[0], v[1]);
 }
 __device__ __forceinline__ uint32_t ldx_raw(Rsrc r, uint32_t i, float*) { return ld32(r, 4u * i); }
 __device__ __forceinline__ uint32_t ldx_raw(Rsrc r, uint32_t i, __half*) {
@@ -162,10 +164,31 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
     }
 
     // Per 16-row block m of this wave: the lane's row is rho = 64 w + 16 m + r16, whose slots are
-    // permuted by a = ((rho & 31) >> 2) = 4 (m & 1) + (r16 >> 2) and bytes by c = r16 & 3.
-    const int bp = g ^ (r16 & 3);                    // physical byte holding canonical byte g
-    const int alo = r16 >> 2;                        // low two bits of a (the same for every m)
-    const uint32_t unperm = 0x03020100u ^ (0x01010101u * (uint32_t)alo);
+    // permuted by a = ((rho & 31) >> 2) = 4 (m & 1) + (r16 >> 2) and bytes by c = r16 & 3: slot q
+    // holds word q ^ a, and canonical byte g of each word sits at byte g ^ c. Lane (g, r16) loads
+    // slots 2 g and 2 g + 1 of its row and needs byte g ^ c of all eight; the four lanes of a row
+    // (16 apart) trade those bytes in two cross-lane swaps. Byte selectors, fixed per lane:
+    const uint32_t cc = (uint32_t)(r16 & 3);
+    const uint32_t alo = (uint32_t)(r16 >> 2);  // low two bits of a (the same for every m)
+    auto pair_sel = [](uint32_t b0, uint32_t b1) { return b0 | ((4u + b0) << 8) | (b1 << 16) | ((4u + b1) << 24); };
+    // the 2 bytes (one per loaded slot) each lane group needs: groups 0, 1 and groups 2, 3
+    const uint32_t sel_lo = pair_sel(cc, cc ^ 1u), sel_hi = pair_sel(cc ^ 2u, cc ^ 3u);
+    // after the swaps a lane holds byte g ^ c of slots {0, 1, 4, 5} in one dword and {2, 3, 6, 7}
+    // in the other; position of slot s in that 8-byte pair: nibble s of 0x76325410. The dword of
+    // words 4 h .. 4 h + 3 (h = 0, 1) takes at byte j word 4 h + j, i.e. slot (4 h + j) ^ a.
+    uint32_t selc[2][2];
+#pragma unroll
+    for (int pm = 0; pm < 2; ++pm)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            uint32_t sel = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t slot = ((uint32_t)j ^ alo) + 4u * (uint32_t)(hh ^ pm);
+                sel |= ((0x76325410u >> (4u * slot)) & 0xFu) << (8 * j);
+            }
+            selc[pm][hh] = sel;
+        }
 
     // running sums of y for the lane's 16 (row, activation row) pairs: D[4 g + j][r16] of block m
     float acc[4][4];
@@ -202,7 +225,7 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
         // Loads of one slice: the wave's packed rows, alpha_c and (main segment) x or
         // (refinement) idx of the staged columns. Every load is issued (clamped to a valid address,
         // the value dropped later) before any is used.
-        uint4 p0[4], p1[4];
+        uint2 pq[4];  // per 16-row block: slots 2 g and 2 g + 1 of the lane's row
         uint32_t xi[16], xw[16], aw[16];  // idx (refinement), raw x bits (main), alpha_c bits
         const Rsrc r_ac = rsrc(acr, (uint32_t)sg.Kv * 4u);
         // this row tile's slab of the segment (all slices and bases): below 2 GiB (checked)
@@ -218,8 +241,8 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const uint32_t rho = (uint32_t)(64 * w + 16 * m + r16);
-                p0[m] = ld128(r_w, ib + 16u * rho);
-                p1[m] = ld128(r_w, ib + 16u * (kTileRows + rho));
+                // slots 0..3 of a row are its first 16-byte half, slots 4..7 the second
+                pq[m] = ld64(r_w, ib + 16u * ((g >> 1) ? kTileRows + rho : rho) + 8u * (uint32_t)(g & 1));
             }
             // per-lane base offsets and a constant per element (the load's immediate offset);
             // columns past Kv read 0 from alpha_c and idx (out of the descriptors' range) and
@@ -302,16 +325,20 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
             uint32_t cb[4][2];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const uint32_t W[8] = {p0[m].x, p0[m].y, p0[m].z, p0[m].w, p1[m].x, p1[m].y, p1[m].z, p1[m].w};
-                uint32_t E[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) E[q] = __builtin_amdgcn_ubfe(W[q], 8 * bp, 8);
-                // slot q holds word q ^ a: word t is in slot t ^ a; a's bit 2 is (m & 1)
-                const int sw = (m & 1) ? 4 : 0;
-                const uint32_t d0 = E[0 ^ sw] | (E[1 ^ sw] << 8) | (E[2 ^ sw] << 16) | (E[3 ^ sw] << 24);
-                const uint32_t d1 = E[4 ^ sw] | (E[5 ^ sw] << 8) | (E[6 ^ sw] << 16) | (E[7 ^ sw] << 24);
-                cb[m][0] = __builtin_amdgcn_perm(0u, d0, unperm);  // byte j = byte j ^ alo
-                cb[m][1] = __builtin_amdgcn_perm(0u, d1, unperm);
+                // per loaded slot, the byte of each lane group: groups 0, 1 in Plo, 2, 3 in Phi
+                const uint32_t Plo = __builtin_amdgcn_perm(pq[m].y, pq[m].x, sel_lo);
+                const uint32_t Phi = __builtin_amdgcn_perm(pq[m].y, pq[m].x, sel_hi);
+                // lanes l and l ^ 32 (groups g, g ^ 2): the upper half's Plo and the lower half's
+                // Phi change places; then each lane holds the bytes of groups g & 2 (low 16 bits)
+                // and (g & 2) + 1 from source groups g & 1 (first) and (g & 1) + 2 (second)
+                const auto s1 = __builtin_amdgcn_permlane32_swap(Plo, Phi, false, false);
+                const uint32_t A = __builtin_amdgcn_perm(s1[1], s1[0], 0x05040100u);  // for group g & 2
+                const uint32_t B = __builtin_amdgcn_perm(s1[1], s1[0], 0x07060302u);  // for group (g & 2) + 1
+                // lanes l and l ^ 16 (groups g, g ^ 1): the odd group's A and the even group's B
+                // change places; then the first dword holds slots {0, 1, 4, 5}, the second {2, 3, 6, 7}
+                const auto s2 = __builtin_amdgcn_permlane16_swap(A, B, false, false);
+                cb[m][0] = __builtin_amdgcn_perm(s2[1], s2[0], selc[m & 1][0]);
+                cb[m][1] = __builtin_amdgcn_perm(s2[1], s2[0], selc[m & 1][1]);
             }
             __syncthreads();
             float4_t c[4];
