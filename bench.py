@@ -653,13 +653,22 @@ def saliency_sweep(torch, ubw, dev):
 
 
 def host_cpu_model():
-    """The host CPU's model name (/proc/cpuinfo), or the platform's processor string."""
+    """The host CPU's model name with its family and model numbers (/proc/cpuinfo: a virtualized
+    host may report only the brand), or the platform's processor string."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.lower().startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (t.strip() for t in line.split(":", 1))
+                if k in ("model name", "cpu family", "model") and k not in fields:
+                    fields[k] = v
+            if not line.strip() and fields:
+                break
     except OSError:
         pass
+    if "model name" in fields:
+        extra = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model") if k in fields)
+        return fields["model name"] + (f" ({extra})" if extra else "")
     import platform
     return platform.processor() or "unknown"
 
@@ -683,6 +692,7 @@ def cpu_baseline(g, step_bytes, seconds):
         "unit": "GB/s",
         "cores": cores,
         "cpu_model": host_cpu_model(),
+        "host_logical_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"{reps} full calls of the same step (4096x4096, 2 bases + 205 salient columns, batch 1), "
                   f"{dt * 1e3:.1f} ms per call",
