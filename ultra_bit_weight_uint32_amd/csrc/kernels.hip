@@ -1020,14 +1020,15 @@ __device__ __forceinline__ void step_body(const StepParams& P, int g) {
             advance(pcur, US, nb);
             if (last && x + 1 < hi) enter(pcur.rg, run_units(x + 1, pcur));
         };
-        // Wave priority from the units this workgroup has left, in the two-row-tile batch-1
-        // instances (the large matrices, two workgroups per CU with several units each): of two
-        // workgroups sharing a CU the one behind gets issue priority, so that both stay busy to
-        // the end (with equal priorities the older one's waves issue first and the younger
-        // finishes alone: 70B gate + up grouped 48.2 -> 44.6 us). The other instances keep the
-        // default priority (on the one-row-tile step it cost 0.1 us).
+        // Wave priority from the units this workgroup has left, in the instances with two or
+        // more row tiles per unit (the large matrices, two workgroups per CU with several units
+        // each): of two workgroups sharing a CU the one behind gets issue priority, so that both
+        // stay busy to the end (with equal priorities the older one's waves issue first and the
+        // younger finishes alone: 70B gate + up grouped 48.2 -> 44.6 us, the 70B gate at 4 rows
+        // 64.0 -> 60.0 us). The one-row-tile instances keep the default priority (on the 4096 x
+        // 4096 step it cost 0.1 us).
         auto set_prio = [&](uint32_t x) {
-            if constexpr (RPL >= 2 && BMAX == 1) {
+            if constexpr (RPL >= 2) {
                 const uint32_t rem = x1 - x;
                 if (rem >= 6) __builtin_amdgcn_s_setprio(3);
                 else if (rem >= 4) __builtin_amdgcn_s_setprio(2);
