@@ -204,6 +204,17 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
     const int b = tid >> 4, cg = tid & 15;
     const bool brow = b < batch;
     int buf = 0, arb = 0;
+    // Grouped launches: wave priority from the (base, slice) steps this workgroup has left, so
+    // that of the workgroups sharing a CU the ones behind issue first.
+    const bool balance = G.count > 1;
+    int left = 0;
+#pragma unroll
+    for (int slot = 0; slot < kMmSlots; ++slot) {
+        if (slot >= nbt) break;
+        const int lo = slot >= nb0 ? (s0 > S0.KT ? s0 - S0.KT : 0) : s0;
+        const int hi = slot >= nb0 ? s1 - S0.KT : (s1 < S0.KT ? s1 : S0.KT);
+        left += hi > lo ? hi - lo : 0;
+    }
 #pragma unroll
     for (int slot = 0; slot < kMmSlots; ++slot) {
         if (slot >= nbt) break;
@@ -257,6 +268,13 @@ __global__ __launch_bounds__(kMmThreads, 4) void k_pm1_mfma(const MmGroup G) {
             }
         };
         for (int ks = lo; ks < hi; ++ks) {
+            if (balance) {
+                if (left >= 9) __builtin_amdgcn_s_setprio(3);
+                else if (left >= 6) __builtin_amdgcn_s_setprio(2);
+                else if (left >= 3) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+                --left;
+            }
             issue(ks);
             // stage v = alpha_c * x of this slice, each activation row scaled by 2^-e
             {
