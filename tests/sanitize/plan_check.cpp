@@ -109,8 +109,8 @@ static void check_path_choice(std::mt19937_64& rng) {
     struct Case {
         int64_t bytes;
         int tables_up_to;  // the largest batch that stays on the tables
-    } cases[] = {{91750400, 4}, {91226112, 4}, {26214400, 5}, {11976704, 6}, {12058624, 6}, {4456448, 7},
-                 {3276800, 7}};
+    } cases[] = {{91019264, 4}, {91017216, 4}, {26005504, 5}, {11836352, 7}, {11835392, 7}, {4404224, 8},
+                 {3250688, 8}};
     for (const Case& c : cases)
         for (int b = 1; b <= 16; ++b)
             CHECK(prefer_mfma(c.bytes, b) == (b > c.tables_up_to), "%lld bytes at %d rows", (long long)c.bytes, b);

@@ -544,9 +544,9 @@ def test_large_matrix_five_and_six_rows():
 
 
 @pytest.mark.parametrize("name,n,k,nb,s,batches", [
-    ("7B up", 11008, 4096, 2, 205, (6, 7)),        # tables at 6 rows, matrix cores at 7
-    ("4096 sq", 4096, 4096, 2, 205, (7, 8)),       # tables at 7, matrix cores at 8
-    ("70B k", 1024, 8192, 3, 410, (7, 8)),         # tables at 7, matrix cores at 8
+    ("7B up", 11008, 4096, 2, 205, (7, 8)),        # tables at 7 rows, matrix cores at 8
+    ("4096 sq", 4096, 4096, 2, 205, (8, 9)),       # tables at 8, matrix cores at 9
+    ("70B k", 1024, 8192, 3, 410, (8, 9)),         # tables at 8, matrix cores at 9
 ])
 def test_path_model_crossovers(name, n, k, nb, s, batches):
     """Each side of the path model's crossover for three shapes (the batch before it runs on the

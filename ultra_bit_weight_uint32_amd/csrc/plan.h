@@ -85,14 +85,14 @@ inline int64_t default_workgroups(int64_t U, int64_t cap, int batch) {
 // coefficients fitted (least squares on relative error) to cold timings of both paths on seven
 // shapes (4096 x 4096 to 28672 x 8192 and 8192 x 28672, 2-3 bases, 5% salient columns in 2
 // bases, fp16 x, y = result) at 1-16 rows. Tables: one launch of r <= 4 rows, a batch as
-// consecutive launches of 4. Matrix cores: one launch of any b <= 16. Within 10% of the
-// measurements except the 1024-row shape (up to 17%); the faster path chosen in 76 of 77 cases
-// (the miss: 1024 x 8192 at 8 rows, 0.24 us).
+// consecutive launches of 4. Matrix cores: one launch of any b <= 16. Within 25% of every
+// measurement; the faster path chosen in 76 of 77 cases (the miss: 8192 x 8192 at 6 rows,
+// 0.86 us).
 struct PathCost {
     double c0, c1, w0, w1;  // c0 + c1 (r - 1) + W (w0 + w1 (r - 1)) us
 };
-constexpr PathCost kTablesCost{6.228, 1.178, 0.27510, 0.10751};
-constexpr PathCost kMfmaCost{17.788, 0.415, 0.67806, 0.01765};
+constexpr PathCost kTablesCost{5.10722, 0.92463, 0.21975, 0.12134};
+constexpr PathCost kMfmaCost{17.20606, 0.34310, 0.60430, 0.02099};
 inline double path_us(const PathCost& c, double W, int r) {
     return c.c0 + c.c1 * (r - 1) + W * (c.w0 + c.w1 * (r - 1));
 }
